@@ -1,0 +1,282 @@
+"""Seeded synthetic inputs for packed, variable-length, interval-masked attention.
+
+This module is shared by the oracle and the GPU path and therefore holds none
+of the method's arithmetic: it draws document lengths, writes down the
+per-key-column row intervals that *describe* each workload's mask (the input
+encoding), and draws q/k/v.  It never fills defaults, reduces extrema,
+classifies tiles or computes attention.
+
+Sources for the shapes and structures (cited by page title and section):
+  * PaddleNLP FlashMask article (m.nxbn.cn/news/70198):
+      §2.2 the 16x16 causal worked example (LTS/LTE table);
+      §5.1 shared-question masks (several answers share one prompt);
+      §5.2 mixed masks (global + sliding window, prefix-LM);
+      §6.7 ZeroPadding: stored row indices are global (a running offset is
+           added per packed sample), so every index below is a global row.
+  * Varlen-Packing technical document (www.gsyq.cn/news/432802), §2: the
+      worked batch of lengths [128, 128, 4096] with 2 heads and Br=128.
+  * Unsloth packing blog (unsloth.ai, "3x faster training + packing"),
+      padding-free packing section: the short/long length mix.
+
+Recipe (stated once, used everywhere):
+  * lengths come from numpy.random.default_rng(seed) (PCG64), integer draws
+    inclusive of both bounds; "draw until filled" clips the last document to
+    the tokens that remain;
+  * q, k, v come from numpy.random.default_rng(seed + 1), drawn in that order
+    as float32 N(0, 1) of shape [N, H, D]; bf16 configs round them to bf16
+    with round-to-nearest-even (torch's float32 -> bfloat16 cast);
+  * the default seed of config k is 1000 + k.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+
+__all__ = ["Workload", "make_config", "make_lengths", "PAGE_LTS", "PAGE_LTE",
+           "causal_document_vectors", "shared_question_vectors",
+           "prefix_window_vectors", "random_case", "CONFIG_IDS"]
+
+# The 16-column causal example of the FlashMask article, §2.2 (its table is
+# flattened to a digit string in the extracted text; these are the 16 values
+# per row of that table, column 0 first).
+PAGE_LTS = [13, 5, 5, 5, 6, 6, 9, 9, 9, 12, 12, 12, 16, 16, 16, 16]
+PAGE_LTE = [15, 14, 14, 15, 12, 12, 11, 11, 16, 16, 16, 16, 16, 16, 16, 16]
+
+CONFIG_IDS = (1, 2, 3, 4, 5)
+
+BF16 = "bf16"
+F32 = "f32"
+
+
+@dataclasses.dataclass
+class Workload:
+    """One packed attention problem.
+
+    cu_seqlens: int32 [B+1]; startend: int32 [n_vec, N] global row indices.
+    q/k/v are float32 numpy arrays [N, H, D] holding exactly the values the
+    GPU sees (already rounded to bf16 when dtype == "bf16").
+    """
+    name: str
+    N: int
+    H: int
+    D: int
+    dtype: str
+    causal: bool
+    n_vec: int
+    cu_seqlens: np.ndarray
+    startend: np.ndarray
+    scale: np.float32
+    q: Optional[np.ndarray] = None
+    k: Optional[np.ndarray] = None
+    v: Optional[np.ndarray] = None
+    meta: dict = dataclasses.field(default_factory=dict)
+
+    @property
+    def B(self) -> int:
+        return int(len(self.cu_seqlens) - 1)
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return np.diff(self.cu_seqlens.astype(np.int64))
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 -> float32, round-to-nearest-even (torch's cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def draw_qkv(seed: int, N: int, H: int, D: int, dtype: str):
+    rng = np.random.default_rng(seed + 1)
+    out = []
+    for _ in range(3):
+        a = rng.standard_normal((N, H, D), dtype=np.float32)
+        if dtype == BF16:
+            a = _round_bf16(a)
+        out.append(a)
+    return out
+
+
+def _fill_until(rng, N: int, draw_one) -> List[int]:
+    lens: List[int] = []
+    total = 0
+    while total < N:
+        L = int(draw_one(rng))
+        L = min(L, N - total)
+        lens.append(L)
+        total += L
+    return lens
+
+
+def make_lengths(k: int, seed: int, N: Optional[int] = None) -> List[int]:
+    """Document lengths of config k (configs 3 and 5 take an optional N)."""
+    rng = np.random.default_rng(seed)
+    if k == 1:
+        return [16]
+    if k == 2:
+        return [128, 128, 4096]
+    if k == 3:
+        N = 16384 if N is None else N
+
+        def one(r):
+            if r.random() < 0.8:
+                return r.integers(64, 512, endpoint=True)
+            return r.integers(2048, 8192, endpoint=True)
+        return _fill_until(rng, N, one)
+    if k == 5:
+        N = 131072 if N is None else N
+        return _fill_until(rng, N, lambda r: r.integers(4096, 32768, endpoint=True))
+    raise ValueError("config %d has group structure; use make_config" % k)
+
+
+def causal_document_vectors(cu: np.ndarray, n_vec: int, N: int) -> np.ndarray:
+    """Causal document mask: each key column is masked for rows at or after
+    the end of its own document (LTS = document end); LTE is either the
+    default (n_vec = 1) or written out as N (n_vec = 2)."""
+    cu = np.asarray(cu, dtype=np.int64)
+    lts = np.empty(N, np.int64)
+    for b in range(len(cu) - 1):
+        lts[cu[b]:cu[b + 1]] = cu[b + 1]
+    rows = [lts]
+    if n_vec == 2:
+        rows.append(np.full(N, N, np.int64))
+    return np.stack(rows).astype(np.int32)
+
+
+def shared_question_vectors(groups, N: int) -> np.ndarray:
+    """Shared-question (DPO/RM) mask of the FlashMask article §5.1/§6.7.
+
+    groups: list of (group_start, [segment ends...]) with the prompt first.
+    Prompt keys are visible to every row of the group (LTS = group end);
+    an answer's keys are hidden from rows after that answer (LTS = answer
+    end), so sibling answers never see each other.  LTE = N.
+    """
+    lts = np.empty(N, np.int64)
+    for g_start, ends in groups:
+        g_end = ends[-1]
+        prev = g_start
+        for si, e in enumerate(ends):
+            lts[prev:e] = g_end if si == 0 else e
+            prev = e
+    lte = np.full(N, N, np.int64)
+    return np.stack([lts, lte]).astype(np.int32)
+
+
+def prefix_window_vectors(cu: np.ndarray, prefix: List[int], W: int, N: int) -> np.ndarray:
+    """Prefix-LM + sliding-window mask (FlashMask article §5.2), non-causal,
+    all four vectors.  For a document [s, e) with bidirectional prefix p:
+      prefix key j:  UT = [0, s)              LT = [min(max(s+p, j+W), e), N)
+      suffix key j:  UT = [0, j)              LT = [min(j+W, e), N)
+    so prefix rows see the whole prefix, and a suffix row i sees key j
+    (prefix or suffix, j <= i) only while i - j < W."""
+    lts = np.empty(N, np.int64); lte = np.full(N, N, np.int64)
+    uts = np.zeros(N, np.int64); ute = np.empty(N, np.int64)
+    cu = np.asarray(cu, dtype=np.int64)
+    for b in range(len(cu) - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        p = int(prefix[b])
+        j = np.arange(s, e, dtype=np.int64)
+        pre = j < s + p
+        lts[s:e] = np.where(pre, np.minimum(np.maximum(s + p, j + W), e),
+                            np.minimum(j + W, e))
+        ute[s:e] = np.where(pre, s, j)
+    return np.stack([lts, lte, uts, ute]).astype(np.int32)
+
+
+def make_config(k: int, seed: Optional[int] = None, with_qkv: bool = True,
+                N: Optional[int] = None, H: Optional[int] = None) -> Workload:
+    """Workload of config k (1..5).  N and H may be reduced for tests; the
+    structure (length mix, mask form) stays that of the config."""
+    seed = 1000 + k if seed is None else seed
+    if k == 1:
+        N_, H_, D_ = 16, 1, 32
+        cu = np.array([0, 16], np.int32)
+        sv = np.array([PAGE_LTS, PAGE_LTE], np.int32)
+        w = Workload("cfg1_page_16x16", N_, H_, D_, F32, True, 2, cu, sv,
+                     np.float32(1.0 / np.sqrt(np.float32(D_))))
+    elif k == 2:
+        lens = [128, 128, 4096]
+        N_ = sum(lens); H_ = 2 if H is None else H; D_ = 128
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        w = Workload("cfg2_varlen_128_128_4096", N_, H_, D_, BF16, True, 2, cu,
+                     causal_document_vectors(cu, 2, N_), np.float32(1.0 / np.sqrt(np.float32(D_))))
+    elif k == 3:
+        N_ = 16384 if N is None else N; H_ = 32 if H is None else H; D_ = 128
+        lens = make_lengths(3, seed, N_)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        w = Workload("cfg3_sft_packing_%d" % N_, N_, H_, D_, BF16, True, 1, cu,
+                     causal_document_vectors(cu, 1, N_), np.float32(1.0 / np.sqrt(np.float32(D_))))
+    elif k == 4:
+        N_ = 32768 if N is None else N; H_ = 32 if H is None else H; D_ = 128
+        rng = np.random.default_rng(seed)
+        groups = []
+        bounds = [0]
+        total = 0
+        while total < N_:
+            segs = [int(rng.integers(512, 2048, endpoint=True))]
+            segs += [int(rng.integers(256, 1024, endpoint=True)) for _ in range(4)]
+            ends = []
+            pos = total
+            for L in segs:
+                if pos >= N_:
+                    break
+                pos = min(pos + L, N_)
+                ends.append(pos)
+            groups.append((total, ends))
+            total = ends[-1]
+            bounds.append(total)
+        cu = np.array(bounds, np.int32)
+        w = Workload("cfg4_shared_question_%d" % N_, N_, H_, D_, BF16, True, 2, cu,
+                     shared_question_vectors(groups, N_), np.float32(1.0 / np.sqrt(np.float32(D_))))
+        w.meta["groups"] = groups
+    elif k == 5:
+        N_ = 131072 if N is None else N; H_ = 8 if H is None else H; D_ = 128
+        W = 4096
+        rng = np.random.default_rng(seed)
+        lens = _fill_until(rng, N_, lambda r: r.integers(4096, 32768, endpoint=True))
+        # prefix fractions: drawn after all lengths, from the same generator
+        prefix = [int(np.floor(rng.uniform(0.1, 0.5) * L)) for L in lens]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        w = Workload("cfg5_prefix_window_%d" % N_, N_, H_, D_, BF16, False, 4, cu,
+                     prefix_window_vectors(cu, prefix, W, N_), np.float32(1.0 / np.sqrt(np.float32(D_))))
+        w.meta.update(prefix=prefix, window=W)
+    else:
+        raise ValueError("unknown config %r" % k)
+    w.meta["seed"] = seed
+    w.meta["config"] = k
+    if with_qkv:
+        w.q, w.k, w.v = draw_qkv(seed, w.N, w.H, w.D, w.dtype)
+    return w
+
+
+def random_case(seed: int, N_max: int = 64, H: int = 1, D: int = 16,
+                causal: Optional[bool] = None, n_vec: Optional[int] = None,
+                dtype: str = F32, with_qkv: bool = True, allow_empty: bool = True) -> Workload:
+    """Tiny adversarial case: random sequence lengths (zero-length ones
+    included), random interval endpoints in [0, N] including empty and
+    reversed intervals.  Used for brute-force checks."""
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(1, N_max, endpoint=True))
+    n_cuts = int(rng.integers(0, 5, endpoint=True))
+    cuts = sorted(int(x) for x in rng.integers(0, N, size=n_cuts, endpoint=True))
+    cu = np.array([0] + cuts + [N], np.int32)
+    if not allow_empty:
+        cu = np.unique(cu).astype(np.int32)
+    if causal is None:
+        causal = bool(rng.integers(0, 1, endpoint=True))
+    if n_vec is None:
+        n_vec = int(rng.choice([1, 2]) if causal else rng.choice([2, 4]))
+    sv = rng.integers(0, N, size=(n_vec, N), endpoint=True).astype(np.int32)
+    # bias some columns towards tidy intervals around their own index
+    j = np.arange(N)
+    tidy = rng.random(N) < 0.5
+    sv[0] = np.where(tidy, np.minimum(j + rng.integers(0, 8, N), N), sv[0])
+    w = Workload("random_%d" % seed, N, H, D, dtype, causal, n_vec, cu, sv,
+                 np.float32(rng.uniform(0.05, 0.5)))
+    w.meta["seed"] = seed
+    if with_qkv:
+        w.q, w.k, w.v = draw_qkv(seed, N, H, D, dtype)
+    return w
