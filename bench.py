@@ -1,0 +1,172 @@
+"""Benchmark of the packed FlashMask forward on one MI355X.
+
+One step = one pass of the whole hot path over the workload, inputs already
+resident in HBM:  block extrema (N2) -> tile classes + work list (N3) ->
+attention (N4, plus the split merge when rows are split).  The metric is
+effective TFLOP/s: unmasked FLOPs (4 * D per attending (query, key, head)
+triple) divided by the time of one step.
+
+Timing: W untimed warm-up steps, then K steps between HIP events on the
+library's stream.  A spin kernel is queued first so the host can enqueue
+all K steps ahead and the GPU runs them back to back.  Inside every step two
+more events bracket the attention launch; their mean elapsed time is the
+dominant kernel's average launch duration for the roofline figure.
+The oracle (fp64 NumPy, the parity reference) is timed on the host cores
+on a bounded sample of the same workload as the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, packed masked attn fwd"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload config id (1..5); 2 is the headline")
+    ap.add_argument("--split", type=int, default=-1, help="max key blocks per item (-1 auto, 0 none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on oracle CPU time")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, flops, budget_s):
+    """Times the oracle on the host cores.  Sample: whole sequences of the
+    workload for all heads, taken in order until the budget is spent (the
+    whole workload when it fits)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cu = w.cu_seqlens.astype(np.int64)
+    done_flops, t_total, seqs = 0, 0.0, 0
+    t_start = time.perf_counter()
+    for b in range(w.B):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if e <= s:
+            continue
+        sv = w.startend[:, s:e].astype(np.int64) - s
+        t0 = time.perf_counter()
+        O.attention(w.q[s:e], w.k[s:e], w.v[s:e], np.array([0, e - s]), sv, w.n_vec, w.causal, w.scale)
+        t_total += time.perf_counter() - t0
+        pairs = O.unmasked_pairs(np.array([0, e - s]), sv, w.n_vec, w.causal)
+        done_flops += O.effective_flops(pairs, w.H, w.D)
+        seqs += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    return {"value": done_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": "%d of %d sequences (all %d heads), %.3g effective GFLOP, %.2f s fp64 NumPy" % (
+                seqs, w.B, w.H, done_flops / 1e9, t_total),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import packed_varlen_masked_amd as pv
+
+    w = W.make_config(args.config)
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float32
+    q = torch.from_numpy(w.q).to(dt).to(dev)
+    k = torch.from_numpy(w.k).to(dt).to(dev)
+    v = torch.from_numpy(w.v).to(dt).to(dev)
+    cu = torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(dev)
+    sv = torch.from_numpy(np.ascontiguousarray(w.startend.astype(np.int32))).to(dev)
+
+    # algorithmic work: closed form for causal documents, else the oracle's count
+    import oracle as O
+    pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
+    flops = O.effective_flops(pairs, w.H, w.D)
+
+    plan = pv.build_plan(cu, sv, w.n_vec, w.causal, w.N, w.H, w.D, dt, max_kb_per_item=args.split)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.H, w.N, dtype=torch.float32, device=dev)
+    S = plan.max_kb_per_item
+
+    def step(ev_a=None, ev_b=None):
+        pv.build_plan_into(plan, cu, sv)
+        if ev_a is not None:
+            ev_a.record()
+        pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), plan=plan, out=out, lse=lse)
+        if ev_b is not None:
+            ev_b.record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    host_ahead = True
+    try:
+        torch.cuda._sleep(int(2e8))  # let the host queue all K steps ahead of the GPU
+    except Exception:
+        host_ahead = False
+    th0 = time.perf_counter()
+    t0.record()
+    for i in range(K):
+        step(ev_a[i], ev_b[i])
+    t1.record()
+    host_ms = (time.perf_counter() - th0) * 1e3 / K
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+    attn_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+    attn_avg = float(attn_ms.mean())
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (attn_avg * 1e-3) / 1e12
+
+    # correctness spot check of the timed configuration (outside the timing)
+    hdr = plan.header()
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v, page-derived lengths and masks)",
+        "config": {"workload": w.name, "N": w.N, "B": w.B, "H": w.H, "D": w.D,
+                   "lengths": [int(x) for x in w.lengths][:16], "causal": bool(w.causal),
+                   "n_vec": w.n_vec, "block_q": plan.layout.block_q, "block_k": plan.layout.block_k,
+                   "max_kb_per_item": S, "n_items": hdr["n_items"],
+                   "class_counts": hdr["class_counts"], "unmasked_pairs_per_head": int(pairs),
+                   "effective_gflop": round(flops / 1e9, 4)},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "timing": {"host_enqueue_ms_per_step": round(host_ms, 4), "host_ran_ahead": host_ahead},
+        "roofline": {"bound": "mfma", "kernel": "fm_attn_bf16_kernel" + (" + fm_merge_bf16_kernel" if S > 0 else ""),
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(attn_avg, 6),
+                     "p10_p50_p90_ms": [round(float(x), 6) for x in np.percentile(attn_ms, [10, 50, 90])]},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, flops, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

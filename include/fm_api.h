@@ -1,0 +1,256 @@
+/*
+ * fm_api.h — C ABI of libflashmask_mi355.so: FlashMask-style forward
+ * attention over packed, variable-length sequences on MI355X (gfx950).
+ *
+ * What is computed (sources cited by page title and section):
+ *   [FM] PaddleNLP FlashMask article (m.nxbn.cn/news/70198)
+ *   [VP] Varlen-Packing technical document (www.gsyq.cn/news/432802)
+ *
+ *   Sequences are concatenated without padding into one token axis of N
+ *   rows; sequence b owns rows [cu_seqlens[b], cu_seqlens[b+1]) ([VP]
+ *   background, §2).  Each key column j carries a column-wise sparse mask:
+ *   query rows in [LTS_j, LTE_j) and [UTS_j, UTE_j) do not attend to it
+ *   ([FM] §2.1, §2.2).  Endpoints are GLOBAL row indices into the packed
+ *   axis ([FM] §6.7: a running offset is added per packed sample).  A
+ *   causal call also hides keys after the query.  Pairs in different
+ *   sequences never attend.  The forward returns `out` and `softmax_lse`,
+ *   the outputs the backward op consumes ([FM] §3.4).
+ *
+ *   The kernels follow the two phases of [FM] §3: a preprocessing pass
+ *   reduces the vectors to per-key-block min/max ("extrema", §3.1), and the
+ *   attention loop classifies every Br x Bc tile as fully masked (skipped),
+ *   partially masked (masked element by element) or unmasked (no mask work)
+ *   (§3.2).  Work is a compact list of (sequence, head, q tile) items
+ *   instead of the fixed seq_count x n_head x ceil(max_len/Br) grid of
+ *   [VP] §2.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device memory on the current device; the
+ *     caller owns every buffer.  The library never allocates or frees
+ *     device memory, never synchronises the stream (except fm_read_status,
+ *     a test helper) and keeps no pointer after return.  All work is
+ *     enqueued on `stream` (NULL = the legacy default stream).
+ *   - Return value: FM_OK or an FM_E_* code; fm_last_error() then gives a
+ *     thread-local message.  Arguments are checked on the host before any
+ *     launch; nothing is enqueued when a call fails.
+ *   - Errors in DEVICE data (cu_seqlens not starting at 0, decreasing, or
+ *     not ending at N) cannot be seen on the host without a sync.  The
+ *     preprocessing kernel detects them, writes a non-zero status word,
+ *     and every later stage then produces no work items; `out` and
+ *     `softmax_lse` are left unwritten.  fm_read_status() reports it.
+ *   - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef FM_API_H
+#define FM_API_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define FM_OK            0
+#define FM_E_INVAL       1  /* bad shape, pointer, or argument combination */
+#define FM_E_UNSUPPORTED 2  /* dtype / head_dim / size not built in        */
+#define FM_E_WORKSPACE   3  /* workspace or output capacity too small       */
+#define FM_E_HIP         4  /* a HIP runtime call or launch failed          */
+
+/* ---- dtypes of q, k, v, out ------------------------------------------- */
+#define FM_BF16 0           /* bf16 storage, fp32 accumulation (MFMA)       */
+#define FM_F32  1           /* fp32 storage and arithmetic (reference path) */
+
+/* ---- flags of fm_attn_fwd --------------------------------------------- */
+/* Visit every tile that is fully masked by the interval vectors (but not
+ * those fully masked by the causal rule) and mask it element by element
+ * instead of skipping it.  Used to show that skipping changes no bit of
+ * the result ([FM] §3.3).  Requires max_kb_per_item == 0.                 */
+#define FM_FLAG_NO_SKIP    0x1u
+/* The workspace already holds the plan built by fm_build_plan (or by
+ * fm_preprocess_mask + fm_build_worklist at the workspace layout) for the
+ * same cu_seqlens, startend, n_vec, causal, N, B, H, tiles and split: the
+ * preprocessing and worklist launches are skipped.  This is the per-layer
+ * call when every layer shares one mask.                                   */
+#define FM_FLAG_PLAN_READY 0x2u
+
+/* ---- limits ----------------------------------------------------------- */
+#define FM_MAX_SEQS        16383  /* B: sequences per call                 */
+#define FM_MAX_COST        16383  /* key blocks one q tile may visit        */
+
+/* Status word bits written by the preprocessing kernel. */
+#define FM_STATUS_CU0      0x1    /* cu_seqlens[0] != 0                     */
+#define FM_STATUS_ORDER    0x2    /* cu_seqlens decreases somewhere         */
+#define FM_STATUS_CUN      0x4    /* cu_seqlens[B] != N                     */
+#define FM_STATUS_CAP      0x8    /* more key blocks than extrema_cap       */
+
+/* Returns the message of the last failing call on this thread ("" if none). */
+const char* fm_last_error(void);
+
+/* Library version, e.g. 100 for 0.1.0. */
+int fm_version(void);
+
+/*
+ * Default tile sizes (Br query rows x Bc key columns) of fm_attn_fwd for a
+ * (dtype, head_dim).  bf16 is built for head_dim 128 with Br = 128,
+ * Bc = 64; fp32 is built for head_dim 32, 64 and 128 and accepts any
+ * 1 <= Br <= 64, 1 <= Bc <= 64 (default 64 x 32).
+ * Returns FM_E_UNSUPPORTED for other combinations.
+ */
+int fm_get_tile_config(int dtype, int head_dim, int* block_q, int* block_k);
+
+/*
+ * Split size S (max key blocks per work item) chosen when fm_attn_fwd
+ * receives max_kb_per_item < 0.  Host-only arithmetic on the sizes: long
+ * rows are cut only when H * (N / Br + B) items would leave the GPU idle.
+ * Returns S >= 0, or -1 on bad arguments.
+ */
+int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim);
+
+/*
+ * Workspace layout.  All offsets are bytes from the workspace base and are
+ * 256-byte aligned.  `*_cap` are host-side upper bounds computed from
+ * (N, B, H, Br, Bc, S) only.
+ *   hdr:        int32 status, n_kblocks, n_items, sched_counter, n_slots
+ *               at byte 0..19; int64 class_counts[3] at byte 64.
+ *   kb_off:     int32 [B+1]         first key block of each sequence
+ *   extrema:    int32 [kb_cap][8]   per key block: min/max of LTS, LTE,
+ *                                   UTS, UTE (in that order)
+ *   items:      int32 [item_cap][8] work items (see fm_build_worklist)
+ *   tile_class: uint8 [map_cap]     per-tile classes (only if requested)
+ *   scratch:    worklist scratch (fm_worklist_scratch_size bytes)
+ *   partial:    fp32 split partials [slot_cap * H] x (Br*D + 2*Br) (S > 0)
+ */
+typedef struct fm_ws_layout {
+    size_t  bytes;
+    size_t  off_hdr, off_kb_off, off_extrema, off_items, off_tile_class;
+    size_t  off_scratch, off_partial;
+    size_t  scratch_bytes, partial_bytes;
+    int64_t kb_cap, item_cap, map_cap, slot_cap;
+    int32_t block_q, block_k, max_kb_per_item, head_dim;
+} fm_ws_layout;
+
+/*
+ * Fills *out for a problem; head_dim is needed only to size the split
+ * partials (pass the attention head_dim; any value >= 1 when S == 0).
+ * want_class_map != 0 reserves the per-tile class map.
+ */
+int fm_workspace_layout(int64_t N, int B, int H, int head_dim, int block_q, int block_k,
+                        int max_kb_per_item, int want_class_map, fm_ws_layout* out);
+
+/* Bytes of fm_workspace_layout(...).bytes for fm_attn_fwd's defaults:
+ * tiles from fm_get_tile_config, split from max_kb_per_item (< 0 = auto),
+ * no class map.  Returns 0 on bad arguments.                               */
+size_t fm_workspace_size(int64_t N, int B, int H, int head_dim, int dtype, int max_kb_per_item);
+
+/* Scratch bytes fm_build_worklist needs for these sizes (0 on bad args). */
+size_t fm_worklist_scratch_size(int64_t N, int B, int H, int block_q, int block_k,
+                                int max_kb_per_item);
+
+/*
+ * Preprocessing ([FM] §3.1).  Default-fills the stored vectors ([FM]
+ * §2.2: LTS, UTS default to 0; LTE, UTE to the query length, here N) and
+ * reduces them, per sequence and per key block of block_k columns starting
+ * at the sequence's first column (the last block may be ragged), to
+ *   extrema[g*8 + 0..7] = min LTS, max LTS, min LTE, max LTE,
+ *                          min UTS, max UTS, min UTE, max UTE
+ * for global key block g = kb_off[b] + kb.  In causal mode the UT slots
+ * are 0.
+ *
+ * startend:  int32 [n_vec][N] device, structure-of-arrays.  Accepted
+ *            (n_vec, causal): causal 1 = {LTS}, causal 2 = {LTS, LTE},
+ *            non-causal 2 = {LTS, UTE}, non-causal 4 = {LTS, LTE, UTS, UTE};
+ *            anything else -> FM_E_INVAL.  Any int32 value is accepted;
+ *            start >= end is an empty interval.
+ * cu_seqlens: int32 [B+1] device, 0 = cu[0] <= ... <= cu[B] = N
+ *            (checked on the device, see the status word).
+ * block_k:   >= 1.  kb_off: int32 [B+1] device (out).
+ * extrema:   int32 [extrema_cap][8] device (out); extrema_cap must be at
+ *            least ceil(N / block_k) + B (FM_E_WORKSPACE otherwise).
+ * n_kblocks, status: int32 device scalars (out).
+ */
+int fm_preprocess_mask(const int32_t* startend, int n_vec, int causal,
+                       const int32_t* cu_seqlens, int B, int64_t N, int block_k,
+                       int32_t* kb_off, int32_t* extrema, int64_t extrema_cap,
+                       int32_t* n_kblocks, int32_t* status, hipStream_t stream);
+
+/*
+ * Tile classification and work list ([FM] §3.2; [VP] §2 for the
+ * (sequence, head, q tile) triple).  Inputs kb_off, extrema and status
+ * come from fm_preprocess_mask with the same block_k.
+ *
+ * Tile (b, qt, kb): rows [r0, r1), columns [c0, c1), both clipped to the
+ * sequence.  FULL when causal and c0 >= r1, or r0 >= LTS_max and
+ * r1 <= LTE_min, or (non-causal) r0 >= UTS_max and r1 <= UTE_min; else
+ * PARTIAL when a causal tile reaches above the diagonal (c1 > r0 + 1), or
+ * r0 < LTE_max and r1 > LTS_min, or (non-causal) r0 < UTE_max and
+ * r1 > UTS_min; else UNMASKED.  r1 is the exclusive row end.
+ *
+ * For every q tile, K = its non-FULL key blocks and cost = |K|.  With
+ * S = max_kb_per_item: S == 0 or cost <= S gives one item over
+ * [K_first, K_last + 1) ([0, 0) when K is empty); otherwise K is cut into
+ * ceil(cost / S) consecutive chunks whose sizes differ by at most one,
+ * larger chunks first.  One item per head.
+ * Item record (int32 x 8): seq, head, q_tile, kb_begin, kb_end, split_idx,
+ * n_splits, cost.  Order: ascending (-cost, seq, q_tile, split_idx, head),
+ * i.e. longest first, deterministic.
+ *
+ * items: int32 [items_cap][8] device (out); n_items: int32 device (out).
+ * class_counts: int64 [3] device (out): FULL, PARTIAL, UNMASKED tiles,
+ *   counted once per (sequence, q tile, key block) for all heads.
+ * tile_class: uint8 device (out, nullable): per sequence row-major
+ *   [Tr_b][Tc_b], sequences concatenated; 0 FULL, 1 PARTIAL, 2 UNMASKED.
+ * scratch: device, fm_worklist_scratch_size(...) bytes.
+ */
+int fm_build_worklist(const int32_t* cu_seqlens, int B, int64_t N, int H,
+                      int block_q, int block_k, const int32_t* kb_off,
+                      const int32_t* extrema, const int32_t* status, int causal,
+                      int max_kb_per_item, int32_t* items, int64_t items_cap,
+                      int32_t* n_items, int64_t* class_counts, uint8_t* tile_class,
+                      int64_t tile_class_cap, void* scratch, size_t scratch_bytes,
+                      hipStream_t stream);
+
+/*
+ * Both of the above into a workspace laid out by fm_workspace_layout(N,
+ * B, H, head_dim, block_q, block_k, max_kb_per_item, want_class_map).
+ * block_q / block_k = 0 take fm_get_tile_config(dtype, head_dim);
+ * max_kb_per_item < 0 takes fm_auto_split.
+ */
+int fm_build_plan(const int32_t* cu_seqlens, int B, int64_t N, int H, int head_dim, int dtype,
+                  const int32_t* startend, int n_vec, int causal, int block_q, int block_k,
+                  int max_kb_per_item, int want_class_map, void* workspace, size_t ws_bytes,
+                  hipStream_t stream);
+
+/*
+ * The forward ([FM] §3: FlashAttention-2 extended with the mask).
+ *   out[i, h, :]     = sum_{j in A_i} softmax_j(scale * <q_i, k_j>) v_j
+ *   softmax_lse[h, i] = ln sum_{j in A_i} exp(scale * <q_i, k_j>)
+ * where A_i is the set of keys row i attends to (same sequence, not
+ * masked).  A row with A_i empty gets out = 0 and lse = -inf.
+ *
+ * q, k, v, out: contiguous [N, H, D] of dtype (self-attention: one
+ *   cu_seqlens for queries and keys; one mask for all heads).
+ * softmax_lse: fp32 [H, N].  scale: finite, > 0.
+ * block_q / block_k: 0 = defaults of fm_get_tile_config.
+ * max_kb_per_item: < 0 auto (fm_auto_split), 0 = never split, else S.
+ *   bf16 only; fp32 requires 0 or < 0 (treated as 0).
+ * workspace: device, >= fm_workspace_layout(...).bytes for these sizes
+ *   (class map not needed).  flags: FM_FLAG_*.
+ * Results are deterministic: the same inputs give the same bits.
+ */
+int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype,
+                int64_t N, int H, int D, const int32_t* cu_seqlens, int B,
+                const int32_t* startend, int n_vec, int causal, float scale,
+                void* out, float* softmax_lse, int block_q, int block_k,
+                int max_kb_per_item, void* workspace, size_t ws_bytes,
+                unsigned flags, hipStream_t stream);
+
+/* Test helper: synchronises `stream` and copies the workspace's status
+ * word to *status (0 = the device data was valid). */
+int fm_read_status(const void* workspace, hipStream_t stream, int32_t* status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FM_API_H */

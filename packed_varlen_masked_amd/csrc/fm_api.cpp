@@ -1,0 +1,398 @@
+// Host side of the C ABI declared in include/fm_api.h: argument checks,
+// workspace layout, and the launch sequence (extrema -> tiles/sort ->
+// attention [-> merge]) on the caller's stream.  No device allocation, no
+// stream synchronisation (except the fm_read_status test helper).
+#include "fm_api.h"
+#include "fm_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() { g_err.clear(); return FM_OK; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kMaxBytes = (int64_t)1 << 46;  // 64 TiB: any layout above is rejected
+
+// Number of compute units of the current device (cached per device).
+int device_cus(int* n_cu) {
+    static std::mutex mu;
+    static std::vector<int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(FM_E_HIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+    if (cache[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            return fail(FM_E_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
+        cache[dev] = v;
+    }
+    *n_cu = cache[dev];
+    return FM_OK;
+}
+
+bool mask_form_ok(int n_vec, int causal) {
+    if (causal) return n_vec == 1 || n_vec == 2;
+    return n_vec == 2 || n_vec == 4;
+}
+
+// Upper bounds from host-known sizes only.
+struct Caps { int64_t kb, qt, slot, item, map; int cost; };
+
+bool compute_caps(int64_t N, int B, int H, int Br, int Bc, int S, Caps* c) {
+    const double n = (double)N;
+    c->kb = cdiv(N, Bc) + B;
+    c->qt = cdiv(N, Br) + B;
+    if (S == 0) {
+        c->slot = c->qt;
+    } else {
+        // sum_b Tr_b * ceil(Tc_b / S) with Tr <= L/Br + 1, ceil(Tc/S) <= L/(Bc S) + 1/S + 1
+        const double v = n * n / ((double)Br * Bc * S) + n * (1.0 + 1.0 / S) / Br + n / ((double)Bc * S) +
+                         (double)B * (1.0 + 1.0 / S);
+        if (v > 4e12) return false;
+        c->slot = (int64_t)ceil(v) + 1;
+    }
+    const double m = n * n / ((double)Br * Bc) + n / Br + n / Bc + B;
+    if (m > 4e12) return false;
+    c->map = (int64_t)ceil(m) + 1;
+    c->item = c->slot * H;
+    c->cost = S > 0 ? S : (int)cdiv(N, Bc);
+    return c->item < INT32_MAX;
+}
+
+fm::ScratchLayout scratch_layout(int B, const Caps& c) {
+    fm::ScratchLayout s;
+    size_t off = 0;
+    s.off_slots = off; off = align256(off + (size_t)c.slot * fm::SLOT_WORDS * sizeof(int32_t));
+    s.off_pos = off; off = align256(off + (size_t)c.slot * sizeof(int32_t));
+    s.off_seq_counts = off; off = align256(off + (size_t)B * 3 * sizeof(long long));
+    s.off_sl_off = off; off = align256(off + (size_t)(B + 1) * sizeof(int32_t));
+    s.bytes = off;
+    s.slot_cap = c.slot;
+    return s;
+}
+
+int check_sizes(int64_t N, int B, int H) {
+    if (B < 1 || B > FM_MAX_SEQS) return fail(FM_E_INVAL, "B=%d outside [1, %d]", B, FM_MAX_SEQS);
+    if (N < 0 || N >= INT32_MAX) return fail(FM_E_INVAL, "N=%lld outside [0, 2^31-1)", (long long)N);
+    if (H < 1) return fail(FM_E_INVAL, "H=%d must be >= 1", H);
+    return FM_OK;
+}
+
+int tile_config(int dtype, int D, int* bq, int* bk) {
+    if (dtype == FM_BF16) {
+        if (D != 128) return fail(FM_E_UNSUPPORTED, "bf16 path is built for head_dim 128 (got %d)", D);
+        *bq = 128; *bk = 64;
+        return FM_OK;
+    }
+    if (dtype == FM_F32) {
+        if (D != 32 && D != 64 && D != 128)
+            return fail(FM_E_UNSUPPORTED, "fp32 path is built for head_dim 32, 64, 128 (got %d)", D);
+        *bq = 64; *bk = 32;
+        return FM_OK;
+    }
+    return fail(FM_E_UNSUPPORTED, "unknown dtype %d", dtype);
+}
+
+int auto_split(int64_t N, int B, int H, int dtype) {
+    if (dtype != FM_BF16) return 0;
+    const int64_t est_items = (int64_t)H * (cdiv(N, 128) + B);
+    return est_items >= 1024 ? 0 : 4;
+}
+
+int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_map,
+                fm_ws_layout* out) {
+    int rc = check_sizes(N, B, H);
+    if (rc) return rc;
+    if (Br < 1 || Bc < 1) return fail(FM_E_INVAL, "block sizes must be >= 1 (got %d, %d)", Br, Bc);
+    if (S < 0) return fail(FM_E_INVAL, "max_kb_per_item must be >= 0 here (got %d)", S);
+    if (D < 1) return fail(FM_E_INVAL, "head_dim must be >= 1");
+    Caps c;
+    if (!compute_caps(N, B, H, Br, Bc, S, &c)) return fail(FM_E_INVAL, "problem too large for one plan");
+    if (c.cost > FM_MAX_COST)
+        return fail(FM_E_UNSUPPORTED, "a q tile may visit %d key blocks (> %d); raise block_k or split",
+                    c.cost, FM_MAX_COST);
+    const fm::ScratchLayout sl = scratch_layout(B, c);
+    fm_ws_layout L;
+    memset(&L, 0, sizeof(L));
+    size_t off = 0;
+    L.off_hdr = off; off = align256(off + 256);
+    L.off_kb_off = off; off = align256(off + (size_t)(B + 1) * 4);
+    L.off_extrema = off; off = align256(off + (size_t)c.kb * 32);
+    L.off_items = off; off = align256(off + (size_t)c.item * 32);
+    L.off_tile_class = want_map ? off : 0; if (want_map) off = align256(off + (size_t)c.map);
+    L.off_scratch = off; L.scratch_bytes = sl.bytes; off = align256(off + sl.bytes);
+    L.partial_bytes = S > 0 ? (size_t)c.slot * H * ((size_t)Br * D + 2 * (size_t)Br) * 4 : 0;
+    L.off_partial = S > 0 ? off : 0; off = align256(off + L.partial_bytes);
+    if ((int64_t)off > kMaxBytes) return fail(FM_E_INVAL, "workspace would exceed 64 TiB");
+    L.bytes = off;
+    L.kb_cap = c.kb; L.item_cap = c.item; L.map_cap = want_map ? c.map : 0; L.slot_cap = c.slot;
+    L.block_q = Br; L.block_k = Bc; L.max_kb_per_item = S; L.head_dim = D;
+    *out = L;
+    return FM_OK;
+}
+
+int hip_check(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return FM_OK;
+}
+
+int preprocess_impl(const int32_t* sv, int n_vec, int causal, const int32_t* cu, int B, int64_t N,
+                    int Bc, int32_t* kb_off, int32_t* ext, int64_t ext_cap, int32_t* nkb,
+                    int32_t* status, hipStream_t s) {
+    int rc = check_sizes(N, B, 1);
+    if (rc) return rc;
+    if (!mask_form_ok(n_vec, causal))
+        return fail(FM_E_INVAL, "unsupported (n_vec=%d, causal=%d): causal takes 1 or 2 vectors, non-causal 2 or 4",
+                    n_vec, causal);
+    if (Bc < 1) return fail(FM_E_INVAL, "block_k must be >= 1");
+    if (!cu || !kb_off || !ext || !nkb || !status || (N > 0 && !sv))
+        return fail(FM_E_INVAL, "null pointer argument");
+    if (ext_cap < cdiv(N, Bc) + B)
+        return fail(FM_E_WORKSPACE, "extrema_cap %lld < ceil(N/block_k)+B = %lld", (long long)ext_cap,
+                    (long long)(cdiv(N, Bc) + B));
+    int n_cu = 0;
+    if ((rc = device_cus(&n_cu))) return rc;
+    return hip_check(fm::launch_extrema(sv, n_vec, causal ? 1 : 0, cu, B, N, Bc, kb_off, ext, ext_cap,
+                                        nkb, status, n_cu, s), "extrema launch");
+}
+
+int worklist_impl(const int32_t* cu, int B, int64_t N, int H, int Br, int Bc, const int32_t* kb_off,
+                  const int32_t* ext, const int32_t* status, int32_t* status_rw, int causal, int S,
+                  int32_t* items, int64_t items_cap, int32_t* n_items, int64_t* counts,
+                  uint8_t* map, int64_t map_cap, void* scratch, size_t scratch_bytes,
+                  int32_t* sched, int32_t* n_slots, hipStream_t s) {
+    int rc = check_sizes(N, B, H);
+    if (rc) return rc;
+    if (Br < 1 || Bc < 1) return fail(FM_E_INVAL, "block sizes must be >= 1");
+    if (S < 0) return fail(FM_E_INVAL, "max_kb_per_item must be >= 0");
+    if (!cu || !kb_off || !ext || !status || !items || !n_items || !counts || !scratch)
+        return fail(FM_E_INVAL, "null pointer argument");
+    Caps c;
+    if (!compute_caps(N, B, H, Br, Bc, S, &c)) return fail(FM_E_INVAL, "problem too large for one plan");
+    if (c.cost > FM_MAX_COST) return fail(FM_E_UNSUPPORTED, "cost bound %d > %d", c.cost, FM_MAX_COST);
+    const fm::ScratchLayout sl = scratch_layout(B, c);
+    if (scratch_bytes < sl.bytes)
+        return fail(FM_E_WORKSPACE, "scratch %zu < %zu bytes", scratch_bytes, sl.bytes);
+    if (items_cap < c.item)
+        return fail(FM_E_WORKSPACE, "items_cap %lld < bound %lld", (long long)items_cap, (long long)c.item);
+    if (map && map_cap < c.map)
+        return fail(FM_E_WORKSPACE, "tile_class_cap %lld < bound %lld", (long long)map_cap, (long long)c.map);
+    fm::PlanPtrs p;
+    p.cu = cu; p.B = B; p.N = N; p.H = H; p.Br = Br; p.Bc = Bc; p.S = S; p.causal = causal ? 1 : 0;
+    p.kb_off = kb_off; p.extrema = ext; p.status = status; p.status_rw = status_rw;
+    p.items = items; p.items_cap = items_cap; p.n_items = n_items; p.class_counts = counts;
+    p.sched_counter = sched; p.n_slots = n_slots; p.tile_class = map; p.tile_class_cap = map ? map_cap : 0;
+    p.scratch = (char*)scratch; p.sl = sl; p.cost_cap = c.cost;
+    return hip_check(fm::launch_worklist(p, s), "worklist launch");
+}
+
+struct Ws {
+    char* base;
+    fm_ws_layout L;
+    int32_t* hdr() const { return (int32_t*)(base + L.off_hdr); }
+    int64_t* counts() const { return (int64_t*)(base + L.off_hdr + fm::HDR_COUNTS_BYTE); }
+};
+
+int build_plan_impl(const Ws& w, const int32_t* cu, int B, int64_t N, int H, const int32_t* sv,
+                    int n_vec, int causal, hipStream_t s) {
+    const fm_ws_layout& L = w.L;
+    int32_t* hdr = w.hdr();
+    int rc = preprocess_impl(sv, n_vec, causal, cu, B, N, L.block_k, (int32_t*)(w.base + L.off_kb_off),
+                             (int32_t*)(w.base + L.off_extrema), L.kb_cap, hdr + fm::HDR_NKB,
+                             hdr + fm::HDR_STATUS, s);
+    if (rc) return rc;
+    return worklist_impl(cu, B, N, H, L.block_q, L.block_k, (const int32_t*)(w.base + L.off_kb_off),
+                         (const int32_t*)(w.base + L.off_extrema), hdr + fm::HDR_STATUS,
+                         hdr + fm::HDR_STATUS, causal, L.max_kb_per_item,
+                         (int32_t*)(w.base + L.off_items), L.item_cap, hdr + fm::HDR_NITEMS, w.counts(),
+                         L.off_tile_class ? (uint8_t*)(w.base + L.off_tile_class) : nullptr, L.map_cap,
+                         w.base + L.off_scratch, L.scratch_bytes, hdr + fm::HDR_SCHED,
+                         hdr + fm::HDR_NSLOTS, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fm_last_error(void) { return g_err.c_str(); }
+
+int fm_version(void) { return 100; }
+
+int fm_get_tile_config(int dtype, int head_dim, int* block_q, int* block_k) {
+    if (!block_q || !block_k) return fail(FM_E_INVAL, "null pointer argument");
+    int rc = tile_config(dtype, head_dim, block_q, block_k);
+    return rc ? rc : ok();
+}
+
+int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim) {
+    int bq, bk;
+    if (check_sizes(N, B, H) || tile_config(dtype, head_dim, &bq, &bk)) return -1;
+    return auto_split(N, B, H, dtype);
+}
+
+int fm_workspace_layout(int64_t N, int B, int H, int head_dim, int block_q, int block_k,
+                        int max_kb_per_item, int want_class_map, fm_ws_layout* out) {
+    if (!out) return fail(FM_E_INVAL, "null pointer argument");
+    int rc = layout_impl(N, B, H, head_dim, block_q, block_k, max_kb_per_item, want_class_map, out);
+    return rc ? rc : ok();
+}
+
+size_t fm_workspace_size(int64_t N, int B, int H, int head_dim, int dtype, int max_kb_per_item) {
+    int bq, bk;
+    if (check_sizes(N, B, H) || tile_config(dtype, head_dim, &bq, &bk)) return 0;
+    int S = max_kb_per_item < 0 ? auto_split(N, B, H, dtype) : max_kb_per_item;
+    if (dtype == FM_F32) S = 0;
+    fm_ws_layout L;
+    if (layout_impl(N, B, H, head_dim, bq, bk, S, 0, &L)) return 0;
+    return L.bytes;
+}
+
+size_t fm_worklist_scratch_size(int64_t N, int B, int H, int block_q, int block_k, int max_kb_per_item) {
+    if (check_sizes(N, B, H) || block_q < 1 || block_k < 1 || max_kb_per_item < 0) return 0;
+    Caps c;
+    if (!compute_caps(N, B, H, block_q, block_k, max_kb_per_item, &c)) return 0;
+    return scratch_layout(B, c).bytes;
+}
+
+int fm_preprocess_mask(const int32_t* startend, int n_vec, int causal, const int32_t* cu_seqlens, int B,
+                       int64_t N, int block_k, int32_t* kb_off, int32_t* extrema, int64_t extrema_cap,
+                       int32_t* n_kblocks, int32_t* status, hipStream_t stream) {
+    int rc = preprocess_impl(startend, n_vec, causal, cu_seqlens, B, N, block_k, kb_off, extrema,
+                             extrema_cap, n_kblocks, status, stream);
+    return rc ? rc : ok();
+}
+
+int fm_build_worklist(const int32_t* cu_seqlens, int B, int64_t N, int H, int block_q, int block_k,
+                      const int32_t* kb_off, const int32_t* extrema, const int32_t* status, int causal,
+                      int max_kb_per_item, int32_t* items, int64_t items_cap, int32_t* n_items,
+                      int64_t* class_counts, uint8_t* tile_class, int64_t tile_class_cap, void* scratch,
+                      size_t scratch_bytes, hipStream_t stream) {
+    int rc = worklist_impl(cu_seqlens, B, N, H, block_q, block_k, kb_off, extrema, status,
+                           const_cast<int32_t*>(status), causal, max_kb_per_item, items, items_cap,
+                           n_items, class_counts, tile_class, tile_class_cap, scratch, scratch_bytes,
+                           nullptr, nullptr, stream);
+    return rc ? rc : ok();
+}
+
+int fm_build_plan(const int32_t* cu_seqlens, int B, int64_t N, int H, int head_dim, int dtype,
+                  const int32_t* startend, int n_vec, int causal, int block_q, int block_k,
+                  int max_kb_per_item, int want_class_map, void* workspace, size_t ws_bytes,
+                  hipStream_t stream) {
+    int bq = block_q, bk = block_k, rc;
+    if (bq == 0 || bk == 0) {
+        int dq, dk;
+        if ((rc = tile_config(dtype, head_dim, &dq, &dk))) return rc;
+        if (bq == 0) bq = dq;
+        if (bk == 0) bk = dk;
+    }
+    int S = max_kb_per_item < 0 ? auto_split(N, B, H, dtype) : max_kb_per_item;
+    if (dtype == FM_F32) S = 0;
+    Ws w;
+    if ((rc = layout_impl(N, B, H, head_dim, bq, bk, S, want_class_map, &w.L))) return rc;
+    if (!workspace) return fail(FM_E_INVAL, "null workspace");
+    if (ws_bytes < w.L.bytes) return fail(FM_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.L.bytes);
+    w.base = (char*)workspace;
+    rc = build_plan_impl(w, cu_seqlens, B, N, H, startend, n_vec, causal, stream);
+    return rc ? rc : ok();
+}
+
+int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t N, int H, int D,
+                const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
+                float scale, void* out, float* softmax_lse, int block_q, int block_k,
+                int max_kb_per_item, void* workspace, size_t ws_bytes, unsigned flags,
+                hipStream_t stream) {
+    int rc = check_sizes(N, B, H);
+    if (rc) return rc;
+    int dq, dk;
+    if ((rc = tile_config(dtype, D, &dq, &dk))) return rc;
+    const int bq = block_q ? block_q : dq, bk = block_k ? block_k : dk;
+    if (dtype == FM_BF16 && (bq != 128 || bk != 64))
+        return fail(FM_E_UNSUPPORTED, "bf16 path is built for block_q=128, block_k=64 (got %d, %d)", bq, bk);
+    if (dtype == FM_F32 && (bq < 1 || bq > 64 || bk < 1 || bk > 64))
+        return fail(FM_E_UNSUPPORTED, "fp32 path takes 1 <= block_q, block_k <= 64 (got %d, %d)", bq, bk);
+    if (!mask_form_ok(n_vec, causal))
+        return fail(FM_E_INVAL, "unsupported (n_vec=%d, causal=%d)", n_vec, causal);
+    if (!(scale > 0.f) || !isfinite(scale)) return fail(FM_E_INVAL, "scale must be finite and > 0");
+    if (flags & ~(FM_FLAG_NO_SKIP | FM_FLAG_PLAN_READY)) return fail(FM_E_INVAL, "unknown flags 0x%x", flags);
+    int S = max_kb_per_item < 0 ? auto_split(N, B, H, dtype) : max_kb_per_item;
+    if (dtype == FM_F32) {
+        if (max_kb_per_item > 0) return fail(FM_E_UNSUPPORTED, "fp32 path does not split items");
+        S = 0;
+    }
+    if ((flags & FM_FLAG_NO_SKIP) && S != 0)
+        return fail(FM_E_INVAL, "FM_FLAG_NO_SKIP requires max_kb_per_item == 0");
+    if (!cu_seqlens || !workspace) return fail(FM_E_INVAL, "null pointer argument");
+    if (N > 0 && (!q || !k || !v || !out || !softmax_lse || !startend))
+        return fail(FM_E_INVAL, "null pointer argument");
+    Ws w;
+    if ((rc = layout_impl(N, B, H, D, bq, bk, S, 0, &w.L))) return rc;
+    if (ws_bytes < w.L.bytes) return fail(FM_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.L.bytes);
+    w.base = (char*)workspace;
+    if (!(flags & FM_FLAG_PLAN_READY)) {
+        if ((rc = build_plan_impl(w, cu_seqlens, B, N, H, startend, n_vec, causal, stream))) return rc;
+    }
+    if (N == 0) return ok();
+    int n_cu = 0;
+    if ((rc = device_cus(&n_cu))) return rc;
+    fm::AttnArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = softmax_lse;
+    a.N = N; a.H = H; a.D = D; a.B = B;
+    a.cu = cu_seqlens; a.sv = startend; a.n_vec = n_vec; a.causal = causal ? 1 : 0;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.Br = bq; a.Bc = bk; a.S = S;
+    a.kb_off = (const int32_t*)(w.base + w.L.off_kb_off);
+    a.extrema = (const int32_t*)(w.base + w.L.off_extrema);
+    a.items = (const int32_t*)(w.base + w.L.off_items);
+    a.n_items = w.hdr() + fm::HDR_NITEMS;
+    a.items_cap = w.L.item_cap;
+    a.sched_counter = w.hdr() + fm::HDR_SCHED;
+    const fm::ScratchLayout sl = [&] {
+        Caps c;
+        compute_caps(N, B, H, bq, bk, S, &c);
+        return scratch_layout(B, c);
+    }();
+    a.sl_off = (const int32_t*)(w.base + w.L.off_scratch + sl.off_sl_off);
+    a.partial = S > 0 ? (float*)(w.base + w.L.off_partial) : nullptr;
+    a.flags = flags;
+    const hipError_t e = dtype == FM_BF16 ? fm::launch_attn_bf16(a, n_cu, stream)
+                                          : fm::launch_attn_f32(a, n_cu, stream);
+    if ((rc = hip_check(e, "attention launch"))) return rc;
+    return ok();
+}
+
+int fm_read_status(const void* workspace, hipStream_t stream, int32_t* status) {
+    if (!workspace || !status) return fail(FM_E_INVAL, "null pointer argument");
+    int rc;
+    if ((rc = hip_check(hipMemcpyAsync(status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, stream),
+                        "hipMemcpyAsync")))
+        return rc;
+    if ((rc = hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize"))) return rc;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal interface between the host API (fm_api.cpp) and the HIP
+// translation units.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace fm {
+
+// Header words of the workspace (int32 index) and class counts (byte offset).
+enum : int { HDR_STATUS = 0, HDR_NKB = 1, HDR_NITEMS = 2, HDR_SCHED = 3, HDR_NSLOTS = 4 };
+constexpr int HDR_COUNTS_BYTE = 64;
+constexpr int ITEM_WORDS = 8;   // seq, head, q_tile, kb_begin, kb_end, split_idx, n_splits, cost
+constexpr int SLOT_WORDS = 8;   // seq, q_tile, split_idx, n_splits, kb_begin, kb_end, cost, valid
+
+// Worklist scratch carved from one buffer (all offsets 256-aligned).
+struct ScratchLayout {
+    size_t off_slots, off_pos, off_seq_counts, off_sl_off, bytes;
+    int64_t slot_cap;
+};
+
+struct PlanPtrs {
+    const int32_t* cu;
+    int B;
+    int64_t N;
+    int H, Br, Bc, S;
+    int causal;
+    const int32_t* kb_off;
+    const int32_t* extrema;
+    const int32_t* status;     // read
+    int32_t* status_rw;        // written when capacities overflow (may equal status)
+    int32_t* items;
+    int64_t items_cap;
+    int32_t* n_items;
+    int64_t* class_counts;
+    int32_t* sched_counter;    // nullable: zeroed when given
+    int32_t* n_slots;          // nullable
+    uint8_t* tile_class;       // nullable
+    int64_t tile_class_cap;
+    char* scratch;
+    ScratchLayout sl;
+    int cost_cap;              // largest cost a q tile can have (histogram size - 1)
+};
+
+hipError_t launch_extrema(const int32_t* sv, int n_vec, int causal, const int32_t* cu, int B,
+                          int64_t N, int Bc, int32_t* kb_off, int32_t* extrema,
+                          int64_t extrema_cap, int32_t* n_kblocks, int32_t* status,
+                          int n_cu, hipStream_t s);
+
+hipError_t launch_worklist(const PlanPtrs& p, hipStream_t s);
+
+// Attention launch arguments shared by the bf16 and fp32 paths.
+struct AttnArgs {
+    const void* q; const void* k; const void* v; void* out; float* lse;
+    int64_t N; int H, D, B;
+    const int32_t* cu; const int32_t* sv; int n_vec; int causal;
+    float scale_log2;          // scale * log2(e)
+    int Br, Bc, S;
+    const int32_t* kb_off; const int32_t* extrema;
+    const int32_t* items; const int32_t* n_items; int64_t items_cap;
+    int32_t* sched_counter;
+    const int32_t* sl_off;     // per-sequence first slot (split partial index)
+    float* partial;            // split partials (S > 0)
+    unsigned flags;
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int n_cu, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int n_cu, hipStream_t s);
+
+}  // namespace fm

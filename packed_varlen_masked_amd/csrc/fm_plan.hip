@@ -1,0 +1,364 @@
+// Plan kernels: block extrema (preprocessing) and the tile classes / work
+// list.  Sources: PaddleNLP FlashMask article (m.nxbn.cn/news/70198) §3.1
+// (per-key-block min/max of LTS/LTE/UTS/UTE), §3.2 (three tile classes);
+// Varlen-Packing technical document (www.gsyq.cn/news/432802) §2 (work named
+// by (sequence, head, q tile)) and §1.2 (a fixed grid waits for its slowest
+// block, hence compact items ordered longest first).
+#include <algorithm>
+
+#include "fm_common.hpp"
+#include "fm_internal.h"
+
+namespace fm {
+
+// ------------------------------------------------------------------------
+// Per-workgroup scan of the key-block counts of all sequences into LDS.
+// Every workgroup of the extrema kernel repeats it (B is small next to N),
+// which removes a launch and a grid-wide dependency.  Also validates cu.
+// Returns the status bits (0 = valid) and leaves s_off[0..B] filled.
+__device__ int scan_kblocks(const int32_t* __restrict__ cu, int B, int64_t N, int Bc,
+                            int64_t cap, int32_t* s_off, long long* tmp) {
+    __shared__ int s_bad;
+    if (threadIdx.x == 0) s_bad = (cu[0] != 0 ? FM_STATUS_CU0 : 0) | (cu[B] != (int)N ? FM_STATUS_CUN : 0);
+    __syncthreads();
+    long long carry = 0;
+    for (int base = 0; base < B; base += blockDim.x) {
+        const int b = base + threadIdx.x;
+        long long tc = 0;
+        if (b < B) {
+            const int L = cu[b + 1] - cu[b];
+            if (L < 0) atomicOr(&s_bad, FM_STATUS_ORDER);
+            tc = L > 0 ? ceil_div(L, Bc) : 0;
+        }
+        long long tot;
+        const long long ex = block_exclusive_scan(tc, tmp, &tot);
+        if (b < B) s_off[b] = (int32_t)min(carry + ex, (long long)INT_MAX);
+        carry += tot;
+    }
+    if (threadIdx.x == 0) {
+        s_off[B] = (int32_t)min(carry, (long long)INT_MAX);
+        if (carry > cap) atomicOr(&s_bad, FM_STATUS_CAP);
+    }
+    __syncthreads();
+    return s_bad;
+}
+
+// N2: one wave per key block, grid-stride over the global key blocks.
+// Lanes read consecutive columns (coalesced 256 B per vector per wave) and
+// reduce min/max across the wave.
+__global__ __launch_bounds__(256) void fm_extrema_kernel(
+    const int32_t* __restrict__ sv, int n_vec, int causal, const int32_t* __restrict__ cu,
+    int B, int64_t N, int Bc, int32_t* __restrict__ kb_off, int32_t* __restrict__ ext,
+    int64_t ext_cap, int32_t* __restrict__ n_kblocks, int32_t* __restrict__ status) {
+    extern __shared__ int32_t s_off[];  // [B+1]
+    __shared__ long long tmp[17];
+    const int bad = scan_kblocks(cu, B, N, Bc, ext_cap, s_off, tmp);
+    if (blockIdx.x == 0) {
+        for (int b = threadIdx.x; b <= B; b += blockDim.x) kb_off[b] = bad ? 0 : s_off[b];
+        if (threadIdx.x == 0) { *status = bad; *n_kblocks = bad ? 0 : s_off[B]; }
+    }
+    if (bad) return;
+    const int total = s_off[B];
+    const int lane = threadIdx.x & 63;
+    const int waves = blockDim.x >> 6;
+    for (int g = blockIdx.x * waves + (threadIdx.x >> 6); g < total; g += gridDim.x * waves) {
+        // sequence owning global key block g: last b with s_off[b] <= g
+        int lo = 0, hi = B;  // s_off[lo] <= g < s_off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_off[mid] <= g) lo = mid; else hi = mid;
+        }
+        const int b = lo;
+        const int64_t c0 = (int64_t)cu[b] + (int64_t)(g - s_off[b]) * Bc;
+        const int64_t c1 = min(c0 + Bc, (int64_t)cu[b + 1]);
+        int mn[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+        int mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+        for (int64_t col = c0 + lane; col < c1; col += 64) {
+            const Vec4 f = fill_column(sv, n_vec, causal, N, col);
+            mn[0] = min(mn[0], f.lts); mx[0] = max(mx[0], f.lts);
+            mn[1] = min(mn[1], f.lte); mx[1] = max(mx[1], f.lte);
+            mn[2] = min(mn[2], f.uts); mx[2] = max(mx[2], f.uts);
+            mn[3] = min(mn[3], f.ute); mx[3] = max(mx[3], f.ute);
+        }
+        int outv = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int a = wave_min(mn[t]), z = wave_max(mx[t]);
+            if (lane == 2 * t) outv = a;
+            if (lane == 2 * t + 1) outv = z;
+        }
+        if (lane < 8) ext[(int64_t)g * 8 + lane] = outv;
+    }
+}
+
+// ------------------------------------------------------------------------
+// Sizes of sequence b that the worklist stage needs.
+struct SeqDims { int s, e, L, Tr, Tc, MS; };
+
+__device__ inline SeqDims seq_dims(const int32_t* __restrict__ cu, int b, int Br, int Bc, int S) {
+    SeqDims d;
+    d.s = cu[b]; d.e = cu[b + 1]; d.L = max(d.e - d.s, 0);
+    d.Tr = d.L ? ceil_div(d.L, Br) : 0;
+    d.Tc = d.L ? ceil_div(d.L, Bc) : 0;
+    d.MS = (S > 0 && d.Tc > 0) ? ceil_div(d.Tc, S) : 1;
+    return d;
+}
+
+// N3a: one workgroup per sequence.  Each wave takes q tiles of its sequence,
+// classifies the tile row (one key block per lane), writes the class map,
+// counts classes, and writes the split slots of the q tile.
+__global__ __launch_bounds__(256) void fm_tiles_kernel(
+    const int32_t* __restrict__ cu, int B, int Br, int Bc, int S, int causal,
+    const int32_t* __restrict__ kb_off, const int32_t* __restrict__ ext,
+    const int32_t* __restrict__ status, int32_t* __restrict__ slots,
+    long long* __restrict__ seq_counts, int32_t* __restrict__ sl_off,
+    uint8_t* __restrict__ tile_class, int64_t tile_class_cap, int64_t slot_cap) {
+    if (*status != 0) return;
+    const int b = blockIdx.x;
+    __shared__ long long tmp[17];
+    __shared__ long long s_cnt[3];
+    // offsets of this sequence: slots (sum of Tr*MS) and class map (Tr*Tc)
+    long long slot_base = 0, map_base = 0;
+    for (int base = 0; base < b; base += blockDim.x) {
+        const int bb = base + threadIdx.x;
+        long long ns = 0, nm = 0;
+        if (bb < b) {
+            const SeqDims d = seq_dims(cu, bb, Br, Bc, S);
+            ns = (long long)d.Tr * d.MS;
+            nm = (long long)d.Tr * d.Tc;
+        }
+        long long t1, t2;
+        block_exclusive_scan(ns, tmp, &t1);
+        block_exclusive_scan(nm, tmp, &t2);
+        slot_base += t1; map_base += t2;
+    }
+    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) sl_off[b] = (int32_t)slot_base;
+    __syncthreads();
+    const SeqDims d = seq_dims(cu, b, Br, Bc, S);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int32_t* __restrict__ xb = ext + (int64_t)kb_off[b] * 8;
+    long long my_cnt[3] = {0, 0, 0};
+    for (int qt = wid; qt < d.Tr; qt += nw) {
+        const int r0 = d.s + qt * Br, r1 = min(r0 + Br, d.e);
+        int cost = 0, first = INT_MAX, last = -1;
+        const int64_t map_row = map_base + (int64_t)qt * d.Tc;
+        for (int kb0 = 0; kb0 < d.Tc; kb0 += 64) {
+            const int kb = kb0 + lane;
+            bool nonfull = false;
+            if (kb < d.Tc) {
+                int x[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) x[t] = xb[(int64_t)kb * 8 + t];
+                const int c0 = d.s + kb * Bc, c1 = min(c0 + Bc, d.e);
+                const TileInfo ti = classify_tile(r0, r1, c0, c1, x, causal);
+                my_cnt[0] += ti.cls == CLS_FULL;
+                my_cnt[1] += ti.cls == CLS_PARTIAL;
+                my_cnt[2] += ti.cls == CLS_UNMASKED;
+                nonfull = ti.cls != CLS_FULL;
+                if (tile_class && map_row + kb < tile_class_cap) tile_class[map_row + kb] = (uint8_t)ti.cls;
+                if (nonfull) { first = min(first, kb); last = max(last, kb); }
+            }
+            cost += __popcll(__ballot(nonfull));
+        }
+        first = wave_min(first);
+        last = wave_max(last);
+        const int n = (S == 0 || cost <= S) ? 1 : ceil_div(cost, S);
+        const int q = cost / n, r = cost % n;
+        const int64_t sb = slot_base + (int64_t)qt * d.MS;
+        if (sb + d.MS > slot_cap) continue;  // host bound violated: leave no slot
+        // record fields other than the kb range, and empty slots past n
+        for (int s = lane; s < d.MS; s += 64) {
+            int32_t* rec = slots + (sb + s) * SLOT_WORDS;
+            const int size = q + (s < r ? 1 : 0);
+            rec[0] = b; rec[1] = qt; rec[2] = s; rec[3] = n;
+            rec[6] = size; rec[7] = s < n ? 1 : 0;
+            if (n == 1 && s == 0) {
+                rec[4] = cost ? first : 0;
+                rec[5] = cost ? last + 1 : 0;
+            } else if (s >= n) {
+                rec[4] = 0; rec[5] = 0;
+            }
+        }
+        if (n > 1) {
+            // second pass: kb range of each chunk from the rank of each
+            // non-FULL block among the row's non-FULL blocks
+            int rank0 = 0;
+            const int big = r * (q + 1);
+            for (int kb0 = 0; kb0 < d.Tc; kb0 += 64) {
+                const int kb = kb0 + lane;
+                bool nonfull = false;
+                if (kb < d.Tc) {
+                    int x[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) x[t] = xb[(int64_t)kb * 8 + t];
+                    const int c0 = d.s + kb * Bc, c1 = min(c0 + Bc, d.e);
+                    nonfull = classify_tile(r0, r1, c0, c1, x, causal).cls != CLS_FULL;
+                }
+                const uint64_t bal = __ballot(nonfull);
+                if (nonfull) {
+                    const int k = rank0 + __popcll(bal & lanemask_lt());
+                    int s, off, size;
+                    if (k < big) { s = k / (q + 1); off = k % (q + 1); size = q + 1; }
+                    else { s = r + (k - big) / q; off = (k - big) % q; size = q; }
+                    int32_t* rec = slots + (sb + s) * SLOT_WORDS;
+                    if (off == 0) rec[4] = kb;
+                    if (off == size - 1) rec[5] = kb + 1;
+                }
+                rank0 += __popcll(bal);
+            }
+        }
+    }
+    // class counts of this sequence
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const long long t = wave_sum64(my_cnt[c]);
+        if (lane == 0) atomicAdd((unsigned long long*)&s_cnt[c], (unsigned long long)t);
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) seq_counts[(int64_t)b * 3 + threadIdx.x] = s_cnt[threadIdx.x];
+}
+
+// N3b: one workgroup.  Stable counting sort of the valid slots by
+// descending cost (longest first), then one item per (slot, head).
+__global__ __launch_bounds__(1024) void fm_sort_kernel(
+    const int32_t* __restrict__ cu, int B, int H, int Br, int Bc, int S, int cost_cap,
+    const int32_t* __restrict__ status, int32_t* __restrict__ status_rw,
+    const int32_t* __restrict__ slots, int32_t* __restrict__ pos,
+    const long long* __restrict__ seq_counts, int32_t* __restrict__ items, int64_t items_cap,
+    int32_t* __restrict__ n_items, long long* __restrict__ class_counts,
+    int32_t* __restrict__ sched_counter, int32_t* __restrict__ n_slots_out, int64_t slot_cap) {
+    extern __shared__ int32_t hist[];  // [cost_cap + 1]
+    __shared__ long long tmp[17];
+    __shared__ long long s_sum[4];
+    const int tid = threadIdx.x;
+    if (*status != 0) {
+        if (tid == 0) {
+            *n_items = 0;
+            class_counts[0] = class_counts[1] = class_counts[2] = 0;
+            if (sched_counter) *sched_counter = 0;
+            if (n_slots_out) *n_slots_out = 0;
+        }
+        return;
+    }
+    // total slots and class counts over sequences
+    long long n_slots = 0;
+    if (tid < 4) s_sum[tid] = 0;
+    for (int base = 0; base < B; base += blockDim.x) {
+        const int b = base + tid;
+        long long ns = 0;
+        if (b < B) {
+            const SeqDims d = seq_dims(cu, b, Br, Bc, S);
+            ns = (long long)d.Tr * d.MS;
+            for (int c = 0; c < 3; ++c)
+                atomicAdd((unsigned long long*)&s_sum[c], (unsigned long long)seq_counts[(int64_t)b * 3 + c]);
+        }
+        long long tot;
+        block_exclusive_scan(ns, tmp, &tot);
+        n_slots += tot;
+    }
+    if (n_slots > slot_cap) n_slots = 0;  // cannot happen with a valid plan; no items then
+    for (int c = tid; c <= cost_cap; c += blockDim.x) hist[c] = 0;
+    __syncthreads();
+    for (long long sl = tid; sl < n_slots; sl += blockDim.x) {
+        const int32_t* rec = slots + sl * SLOT_WORDS;
+        if (rec[7]) atomicAdd(&hist[min(rec[6], cost_cap)], 1);
+    }
+    __syncthreads();
+    // descending exclusive scan: base[c] = number of valid slots with cost > c
+    const int per = ceil_div(cost_cap + 1, (int)blockDim.x);
+    long long local = 0;
+    for (int t = 0; t < per; ++t) {
+        const int rc = tid * per + t;  // reversed index
+        if (rc <= cost_cap) local += hist[cost_cap - rc];
+    }
+    long long total_valid;
+    long long run = block_exclusive_scan(local, tmp, &total_valid);
+    for (int t = 0; t < per; ++t) {
+        const int rc = tid * per + t;
+        if (rc <= cost_cap) {
+            const int c = cost_cap - rc;
+            const int h = hist[c];
+            hist[c] = (int32_t)run;
+            run += h;
+        }
+    }
+    __syncthreads();
+    const bool overflow = total_valid * H > items_cap;
+    if (!overflow && tid < 64) {
+        const int lane = tid;
+        for (long long chunk = 0; chunk < n_slots; chunk += 64) {
+            const long long sl = chunk + lane;
+            const bool valid = sl < n_slots && slots[sl * SLOT_WORDS + 7] != 0;
+            const int cost = valid ? min(slots[sl * SLOT_WORDS + 6], cost_cap) : 0;
+            uint64_t eq = __ballot(valid);
+            for (int bit = 0; bit < 15; ++bit) {
+                const bool bb = (cost >> bit) & 1;
+                const uint64_t m1 = __ballot(bb);
+                eq &= bb ? m1 : ~m1;
+            }
+            if (valid) {
+                const int before = __popcll(eq & lanemask_lt());
+                const int rk = hist[cost] + before;
+                pos[sl] = rk;
+                const bool leader = (eq >> lane) == 1ull;  // highest lane of its group
+                __builtin_amdgcn_wave_barrier();
+                if (leader) hist[cost] = rk + 1;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    __syncthreads();
+    if (!overflow) {
+        for (long long idx = tid; idx < n_slots * H; idx += blockDim.x) {
+            const long long sl = idx / H;
+            const int h = (int)(idx - sl * H);
+            const int32_t* rec = slots + sl * SLOT_WORDS;
+            if (!rec[7]) continue;
+            int32_t* it = items + ((int64_t)pos[sl] * H + h) * ITEM_WORDS;
+            it[0] = rec[0]; it[1] = h; it[2] = rec[1]; it[3] = rec[4];
+            it[4] = rec[5]; it[5] = rec[2]; it[6] = rec[3]; it[7] = rec[6];
+        }
+    }
+    if (tid == 0) {
+        *n_items = overflow ? 0 : (int32_t)(total_valid * H);
+        if (overflow) atomicOr(status_rw, FM_STATUS_CAP);
+        class_counts[0] = s_sum[0]; class_counts[1] = s_sum[1]; class_counts[2] = s_sum[2];
+        if (sched_counter) *sched_counter = 0;
+        if (n_slots_out) *n_slots_out = (int32_t)n_slots;
+    }
+}
+
+// ------------------------------------------------------------------------
+hipError_t launch_extrema(const int32_t* sv, int n_vec, int causal, const int32_t* cu, int B,
+                          int64_t N, int Bc, int32_t* kb_off, int32_t* extrema,
+                          int64_t extrema_cap, int32_t* n_kblocks, int32_t* status,
+                          int n_cu, hipStream_t s) {
+    const int64_t kb_bound = (N + Bc - 1) / Bc + B;
+    int64_t grid = (kb_bound + 3) / 4;
+    grid = std::max<int64_t>(1, std::min<int64_t>(grid, (int64_t)n_cu * 8));
+    const size_t lds = (size_t)(B + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL(fm_extrema_kernel, dim3((unsigned)grid), dim3(256), lds, s, sv, n_vec,
+                       causal, cu, B, N, Bc, kb_off, extrema, extrema_cap, n_kblocks, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_worklist(const PlanPtrs& p, hipStream_t s) {
+    int32_t* slots = (int32_t*)(p.scratch + p.sl.off_slots);
+    int32_t* pos = (int32_t*)(p.scratch + p.sl.off_pos);
+    long long* seq_counts = (long long*)(p.scratch + p.sl.off_seq_counts);
+    int32_t* sl_off = (int32_t*)(p.scratch + p.sl.off_sl_off);
+    hipLaunchKernelGGL(fm_tiles_kernel, dim3(p.B), dim3(256), 0, s, p.cu, p.B, p.Br, p.Bc, p.S,
+                       p.causal, p.kb_off, p.extrema, p.status, slots, seq_counts, sl_off,
+                       p.tile_class, p.tile_class_cap, p.sl.slot_cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)(p.cost_cap + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL(fm_sort_kernel, dim3(1), dim3(1024), lds, s, p.cu, p.B, p.H, p.Br, p.Bc,
+                       p.S, p.cost_cap, p.status, p.status_rw, slots, pos, seq_counts, p.items,
+                       p.items_cap, p.n_items, (long long*)p.class_counts, p.sched_counter,
+                       p.n_slots, p.sl.slot_cap);
+    return hipGetLastError();
+}
+
+}  // namespace fm
