@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--split", type=int, default=-1, help="max key blocks per item (-1 auto, 0 none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on oracle CPU time")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -115,6 +117,12 @@ def main():
         if ev_b is not None:
             ev_b.record()
 
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -93,7 +93,7 @@ int fm_version(void);
 
 /*
  * Default tile sizes (Br query rows x Bc key columns) of fm_attn_fwd for a
- * (dtype, head_dim).  bf16 is built for head_dim 128 with Br = 128,
+ * (dtype, head_dim).  bf16 is built for head_dim 128 with Br = 256,
  * Bc = 64; fp32 is built for head_dim 32, 64 and 128 and accepts any
  * 1 <= Br <= 64, 1 <= Bc <= 64 (default 64 x 32).
  * Returns FM_E_UNSUPPORTED for other combinations.
@@ -103,7 +103,8 @@ int fm_get_tile_config(int dtype, int head_dim, int* block_q, int* block_k);
 /*
  * Split size S (max key blocks per work item) chosen when fm_attn_fwd
  * receives max_kb_per_item < 0.  Host-only arithmetic on the sizes: long
- * rows are cut only when H * (N / Br + B) items would leave the GPU idle.
+ * rows are cut (into chunks of at most 6 key blocks) only when fewer than
+ * 512 items, H * (N / Br + B), would leave compute units idle.
  * Returns S >= 0, or -1 on bad arguments.
  */
 int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim);
@@ -117,15 +118,17 @@ int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim);
  *   kb_off:     int32 [B+1]         first key block of each sequence
  *   extrema:    int32 [kb_cap][8]   per key block: min/max of LTS, LTE,
  *                                   UTS, UTE (in that order)
- *   items:      int32 [item_cap][8] work items (see fm_build_worklist)
+ *   items:      int32 [item_cap][16] work items (see fm_build_worklist)
  *   tile_class: uint8 [map_cap]     per-tile classes (only if requested)
  *   scratch:    worklist scratch (fm_worklist_scratch_size bytes)
  *   partial:    fp32 split partials [slot_cap * H] x (Br*D + 2*Br) (S > 0)
+ *   merge:      int32 [slot_cap * H] split arrival counters (S > 0); zeroed
+ *               when the plan is built and left at zero by every call
  */
 typedef struct fm_ws_layout {
     size_t  bytes;
     size_t  off_hdr, off_kb_off, off_extrema, off_items, off_tile_class;
-    size_t  off_scratch, off_partial;
+    size_t  off_scratch, off_partial, off_merge;
     size_t  scratch_bytes, partial_bytes;
     int64_t kb_cap, item_cap, map_cap, slot_cap;
     int32_t block_q, block_k, max_kb_per_item, head_dim;
@@ -192,11 +195,14 @@ int fm_preprocess_mask(const int32_t* startend, int n_vec, int causal,
  * [K_first, K_last + 1) ([0, 0) when K is empty); otherwise K is cut into
  * ceil(cost / S) consecutive chunks whose sizes differ by at most one,
  * larger chunks first.  One item per head.
- * Item record (int32 x 8): seq, head, q_tile, kb_begin, kb_end, split_idx,
- * n_splits, cost.  Order: ascending (-cost, seq, q_tile, split_idx, head),
- * i.e. longest first, deterministic.
+ * Item record (int32 x 16): seq, head, q_tile, kb_begin, kb_end, split_idx,
+ * n_splits, cost, then derived words for the attention kernel: seq_start
+ * (cu_seqlens[seq]), seq_end, kb_base (kb_off[seq]), split0_slot (slot
+ * index of split 0 of this q tile; its partials sit at (slot + s) * H +
+ * head), and four zero words.  Order: ascending (-cost, seq, q_tile,
+ * split_idx, head), i.e. longest first, deterministic.
  *
- * items: int32 [items_cap][8] device (out); n_items: int32 device (out).
+ * items: int32 [items_cap][16] device (out); n_items: int32 device (out).
  * class_counts: int64 [3] device (out): FULL, PARTIAL, UNMASKED tiles,
  *   counted once per (sequence, q tile, key block) for all heads.
  * tile_class: uint8 device (out, nullable): per sequence row-major

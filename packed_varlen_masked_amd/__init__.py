@@ -27,7 +27,9 @@ FM_OK, FM_E_INVAL, FM_E_UNSUPPORTED, FM_E_WORKSPACE, FM_E_HIP = 0, 1, 2, 3, 4
 FM_BF16, FM_F32 = 0, 1
 FM_FLAG_NO_SKIP, FM_FLAG_PLAN_READY = 0x1, 0x2
 FULL, PARTIAL, UNMASKED = 0, 1, 2
-ITEM_FIELDS = ("seq", "head", "q_tile", "kb_begin", "kb_end", "split_idx", "n_splits", "cost")
+ITEM_FIELDS = ("seq", "head", "q_tile", "kb_begin", "kb_end", "split_idx", "n_splits", "cost",
+               "seq_start", "seq_end", "kb_base", "split0_slot", "zero0", "zero1", "zero2", "zero3")
+ITEM_WORDS = len(ITEM_FIELDS)
 
 _ERRNAMES = {FM_E_INVAL: "FM_E_INVAL", FM_E_UNSUPPORTED: "FM_E_UNSUPPORTED",
              FM_E_WORKSPACE: "FM_E_WORKSPACE", FM_E_HIP: "FM_E_HIP"}
@@ -44,7 +46,8 @@ class WsLayout(ctypes.Structure):
                 ("off_hdr", ctypes.c_size_t), ("off_kb_off", ctypes.c_size_t),
                 ("off_extrema", ctypes.c_size_t), ("off_items", ctypes.c_size_t),
                 ("off_tile_class", ctypes.c_size_t), ("off_scratch", ctypes.c_size_t),
-                ("off_partial", ctypes.c_size_t), ("scratch_bytes", ctypes.c_size_t),
+                ("off_partial", ctypes.c_size_t), ("off_merge", ctypes.c_size_t),
+                ("scratch_bytes", ctypes.c_size_t),
                 ("partial_bytes", ctypes.c_size_t),
                 ("kb_cap", ctypes.c_int64), ("item_cap", ctypes.c_int64),
                 ("map_cap", ctypes.c_int64), ("slot_cap", ctypes.c_int64),
@@ -171,13 +174,13 @@ def preprocess_mask(startend: torch.Tensor, n_vec: int, causal: bool, cu_seqlens
 def build_worklist(cu_seqlens: torch.Tensor, N: int, H: int, block_q: int, block_k: int,
                    kb_off: torch.Tensor, extrema: torch.Tensor, status: int, causal: bool,
                    max_kb_per_item: int = 0, want_class_map: bool = True):
-    """Returns dict(items [n_items, 8], class_counts [3], tile_class (uint8) or None)."""
+    """Returns dict(items [n_items, 16], class_counts [3], tile_class (uint8) or None)."""
     cu = _i32(cu_seqlens, "cu_seqlens")
     B = cu.numel() - 1
     dev = cu.device
     lay = workspace_layout(N, B, H, 1, block_q, block_k, max_kb_per_item, want_class_map)
     scratch = torch.empty(max(lay.scratch_bytes, 1), dtype=torch.uint8, device=dev)
-    items = torch.empty(lay.item_cap, 8, dtype=torch.int32, device=dev)
+    items = torch.empty(lay.item_cap, ITEM_WORDS, dtype=torch.int32, device=dev)
     n_items = torch.zeros(1, dtype=torch.int32, device=dev)
     counts = torch.zeros(3, dtype=torch.int64, device=dev)
     st = torch.tensor([status], dtype=torch.int32, device=dev)
@@ -223,7 +226,7 @@ class Plan:
         return self._view(self.layout.off_extrema, n_kb * 8, torch.int32, (n_kb, 8))
 
     def items(self, n_items):
-        return self._view(self.layout.off_items, n_items * 8, torch.int32, (n_items, 8))
+        return self._view(self.layout.off_items, n_items * ITEM_WORDS, torch.int32, (n_items, ITEM_WORDS))
 
     def tile_class(self, n):
         return self._view(self.layout.off_tile_class, n, torch.uint8, (n,))

@@ -32,6 +32,9 @@ def hipcc() -> str:
 def compile_flags():
     return ["-O3", "-std=c++17", "-fPIC", "--offload-arch=%s" % ARCH,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # every atomic in these kernels is issued by a single lane; the
+            # atomic optimizer would make its result needed at once
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
             "-Wno-unused-variable"]
 

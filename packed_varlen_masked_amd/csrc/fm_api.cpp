@@ -106,7 +106,7 @@ int check_sizes(int64_t N, int B, int H) {
 int tile_config(int dtype, int D, int* bq, int* bk) {
     if (dtype == FM_BF16) {
         if (D != 128) return fail(FM_E_UNSUPPORTED, "bf16 path is built for head_dim 128 (got %d)", D);
-        *bq = 128; *bk = 64;
+        *bq = 256; *bk = 64;
         return FM_OK;
     }
     if (dtype == FM_F32) {
@@ -120,8 +120,8 @@ int tile_config(int dtype, int D, int* bq, int* bk) {
 
 int auto_split(int64_t N, int B, int H, int dtype) {
     if (dtype != FM_BF16) return 0;
-    const int64_t est_items = (int64_t)H * (cdiv(N, 128) + B);
-    return est_items >= 1024 ? 0 : 4;
+    const int64_t est_items = (int64_t)H * (cdiv(N, 256) + B);
+    return est_items >= 512 ? 0 : 6;
 }
 
 int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_map,
@@ -143,11 +143,12 @@ int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_
     L.off_hdr = off; off = align256(off + 256);
     L.off_kb_off = off; off = align256(off + (size_t)(B + 1) * 4);
     L.off_extrema = off; off = align256(off + (size_t)c.kb * 32);
-    L.off_items = off; off = align256(off + (size_t)c.item * 32);
+    L.off_items = off; off = align256(off + (size_t)c.item * fm::ITEM_WORDS * 4);
     L.off_tile_class = want_map ? off : 0; if (want_map) off = align256(off + (size_t)c.map);
     L.off_scratch = off; L.scratch_bytes = sl.bytes; off = align256(off + sl.bytes);
     L.partial_bytes = S > 0 ? (size_t)c.slot * H * ((size_t)Br * D + 2 * (size_t)Br) * 4 : 0;
     L.off_partial = S > 0 ? off : 0; off = align256(off + L.partial_bytes);
+    L.off_merge = S > 0 ? off : 0; if (S > 0) off = align256(off + (size_t)c.slot * H * 4);
     if ((int64_t)off > kMaxBytes) return fail(FM_E_INVAL, "workspace would exceed 64 TiB");
     L.bytes = off;
     L.kb_cap = c.kb; L.item_cap = c.item; L.map_cap = want_map ? c.map : 0; L.slot_cap = c.slot;
@@ -185,7 +186,7 @@ int worklist_impl(const int32_t* cu, int B, int64_t N, int H, int Br, int Bc, co
                   const int32_t* ext, const int32_t* status, int32_t* status_rw, int causal, int S,
                   int32_t* items, int64_t items_cap, int32_t* n_items, int64_t* counts,
                   uint8_t* map, int64_t map_cap, void* scratch, size_t scratch_bytes,
-                  int32_t* sched, int32_t* n_slots, hipStream_t s) {
+                  int32_t* sched, int32_t* n_slots, int32_t* merge, hipStream_t s) {
     int rc = check_sizes(N, B, H);
     if (rc) return rc;
     if (Br < 1 || Bc < 1) return fail(FM_E_INVAL, "block sizes must be >= 1");
@@ -207,7 +208,7 @@ int worklist_impl(const int32_t* cu, int B, int64_t N, int H, int Br, int Bc, co
     p.kb_off = kb_off; p.extrema = ext; p.status = status; p.status_rw = status_rw;
     p.items = items; p.items_cap = items_cap; p.n_items = n_items; p.class_counts = counts;
     p.sched_counter = sched; p.n_slots = n_slots; p.tile_class = map; p.tile_class_cap = map ? map_cap : 0;
-    p.scratch = (char*)scratch; p.sl = sl; p.cost_cap = c.cost;
+    p.scratch = (char*)scratch; p.sl = sl; p.cost_cap = c.cost; p.merge_counter = S > 0 ? merge : nullptr;
     return hip_check(fm::launch_worklist(p, s), "worklist launch");
 }
 
@@ -222,17 +223,31 @@ int build_plan_impl(const Ws& w, const int32_t* cu, int B, int64_t N, int H, con
                     int n_vec, int causal, hipStream_t s) {
     const fm_ws_layout& L = w.L;
     int32_t* hdr = w.hdr();
-    int rc = preprocess_impl(sv, n_vec, causal, cu, B, N, L.block_k, (int32_t*)(w.base + L.off_kb_off),
-                             (int32_t*)(w.base + L.off_extrema), L.kb_cap, hdr + fm::HDR_NKB,
-                             hdr + fm::HDR_STATUS, s);
+    int rc = check_sizes(N, B, H);
     if (rc) return rc;
-    return worklist_impl(cu, B, N, H, L.block_q, L.block_k, (const int32_t*)(w.base + L.off_kb_off),
-                         (const int32_t*)(w.base + L.off_extrema), hdr + fm::HDR_STATUS,
-                         hdr + fm::HDR_STATUS, causal, L.max_kb_per_item,
-                         (int32_t*)(w.base + L.off_items), L.item_cap, hdr + fm::HDR_NITEMS, w.counts(),
-                         L.off_tile_class ? (uint8_t*)(w.base + L.off_tile_class) : nullptr, L.map_cap,
-                         w.base + L.off_scratch, L.scratch_bytes, hdr + fm::HDR_SCHED,
-                         hdr + fm::HDR_NSLOTS, s);
+    if (!mask_form_ok(n_vec, causal))
+        return fail(FM_E_INVAL, "unsupported (n_vec=%d, causal=%d): causal takes 1 or 2 vectors, non-causal 2 or 4",
+                    n_vec, causal);
+    if (!cu || (N > 0 && !sv)) return fail(FM_E_INVAL, "null pointer argument");
+    Caps c;
+    if (!compute_caps(N, B, H, L.block_q, L.block_k, L.max_kb_per_item, &c))
+        return fail(FM_E_INVAL, "problem too large for one plan");
+    fm::PlanPtrs p;
+    p.cu = cu; p.B = B; p.N = N; p.H = H; p.Br = L.block_q; p.Bc = L.block_k; p.S = L.max_kb_per_item;
+    p.causal = causal ? 1 : 0;
+    p.kb_off = (const int32_t*)(w.base + L.off_kb_off);
+    p.extrema = (const int32_t*)(w.base + L.off_extrema);
+    p.status = hdr + fm::HDR_STATUS; p.status_rw = hdr + fm::HDR_STATUS;
+    p.items = (int32_t*)(w.base + L.off_items); p.items_cap = L.item_cap;
+    p.n_items = hdr + fm::HDR_NITEMS; p.class_counts = w.counts();
+    p.sched_counter = hdr + fm::HDR_SCHED; p.n_slots = hdr + fm::HDR_NSLOTS;
+    p.tile_class = L.off_tile_class ? (uint8_t*)(w.base + L.off_tile_class) : nullptr;
+    p.tile_class_cap = L.off_tile_class ? L.map_cap : 0;
+    p.scratch = w.base + L.off_scratch; p.sl = scratch_layout(B, c); p.cost_cap = c.cost;
+    p.merge_counter = L.off_merge ? (int32_t*)(w.base + L.off_merge) : nullptr;
+    return hip_check(fm::launch_plan(sv, n_vec, (int32_t*)(w.base + L.off_extrema), L.kb_cap, hdr + fm::HDR_NKB,
+                                     (int32_t*)(w.base + L.off_kb_off), p, s),
+                     "plan launch");
 }
 
 }  // namespace
@@ -295,7 +310,7 @@ int fm_build_worklist(const int32_t* cu_seqlens, int B, int64_t N, int H, int bl
     int rc = worklist_impl(cu_seqlens, B, N, H, block_q, block_k, kb_off, extrema, status,
                            const_cast<int32_t*>(status), causal, max_kb_per_item, items, items_cap,
                            n_items, class_counts, tile_class, tile_class_cap, scratch, scratch_bytes,
-                           nullptr, nullptr, stream);
+                           nullptr, nullptr, nullptr, stream);
     return rc ? rc : ok();
 }
 
@@ -331,8 +346,8 @@ int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t 
     int dq, dk;
     if ((rc = tile_config(dtype, D, &dq, &dk))) return rc;
     const int bq = block_q ? block_q : dq, bk = block_k ? block_k : dk;
-    if (dtype == FM_BF16 && (bq != 128 || bk != 64))
-        return fail(FM_E_UNSUPPORTED, "bf16 path is built for block_q=128, block_k=64 (got %d, %d)", bq, bk);
+    if (dtype == FM_BF16 && (bq != 256 || bk != 64))
+        return fail(FM_E_UNSUPPORTED, "bf16 path is built for block_q=256, block_k=64 (got %d, %d)", bq, bk);
     if (dtype == FM_F32 && (bq < 1 || bq > 64 || bk < 1 || bk > 64))
         return fail(FM_E_UNSUPPORTED, "fp32 path takes 1 <= block_q, block_k <= 64 (got %d, %d)", bq, bk);
     if (!mask_form_ok(n_vec, causal))
@@ -378,6 +393,7 @@ int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t 
     }();
     a.sl_off = (const int32_t*)(w.base + w.L.off_scratch + sl.off_sl_off);
     a.partial = S > 0 ? (float*)(w.base + w.L.off_partial) : nullptr;
+    a.merge_counter = S > 0 ? (int32_t*)(w.base + w.L.off_merge) : nullptr;
     a.flags = flags;
     const hipError_t e = dtype == FM_BF16 ? fm::launch_attn_bf16(a, n_cu, stream)
                                           : fm::launch_attn_f32(a, n_cu, stream);

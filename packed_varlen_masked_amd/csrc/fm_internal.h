@@ -10,7 +10,8 @@ namespace fm {
 // Header words of the workspace (int32 index) and class counts (byte offset).
 enum : int { HDR_STATUS = 0, HDR_NKB = 1, HDR_NITEMS = 2, HDR_SCHED = 3, HDR_NSLOTS = 4 };
 constexpr int HDR_COUNTS_BYTE = 64;
-constexpr int ITEM_WORDS = 8;   // seq, head, q_tile, kb_begin, kb_end, split_idx, n_splits, cost
+constexpr int ITEM_WORDS = 16;  // seq, head, q_tile, kb_begin, kb_end, split_idx, n_splits, cost,
+                                // seq_start, seq_end, kb_base, split0_slot, 0, 0, 0, 0
 constexpr int SLOT_WORDS = 8;   // seq, q_tile, split_idx, n_splits, kb_begin, kb_end, cost, valid
 
 // Worklist scratch carved from one buffer (all offsets 256-aligned).
@@ -40,6 +41,7 @@ struct PlanPtrs {
     char* scratch;
     ScratchLayout sl;
     int cost_cap;              // largest cost a q tile can have (histogram size - 1)
+    int32_t* merge_counter;    // nullable: split arrival counters, zeroed for n_slots * H
 };
 
 hipError_t launch_extrema(const int32_t* sv, int n_vec, int causal, const int32_t* cu, int B,
@@ -48,6 +50,11 @@ hipError_t launch_extrema(const int32_t* sv, int n_vec, int causal, const int32_
                           int n_cu, hipStream_t s);
 
 hipError_t launch_worklist(const PlanPtrs& p, hipStream_t s);
+
+// Plan path: fused extrema + classification (one workgroup per sequence),
+// then the sort.  Writes kb_off, extrema, n_kblocks and the status word too.
+hipError_t launch_plan(const int32_t* sv, int n_vec, int32_t* ext, int64_t ext_cap, int32_t* n_kblocks,
+                       int32_t* kb_off_out, const PlanPtrs& p, hipStream_t s);
 
 // Attention launch arguments shared by the bf16 and fp32 paths.
 struct AttnArgs {
@@ -61,6 +68,7 @@ struct AttnArgs {
     int32_t* sched_counter;
     const int32_t* sl_off;     // per-sequence first slot (split partial index)
     float* partial;            // split partials (S > 0)
+    int32_t* merge_counter;    // split arrival counters (S > 0)
     unsigned flags;
 };
 

@@ -43,6 +43,29 @@ __device__ int scan_kblocks(const int32_t* __restrict__ cu, int B, int64_t N, in
     return s_bad;
 }
 
+// min / max of the four filled vectors over columns [c0, c1), reduced across
+// the wave; lane 2t returns the min and lane 2t+1 the max of vector t.
+__device__ inline int block_extrema(const int32_t* __restrict__ sv, int n_vec, int causal, int64_t N,
+                                    int64_t c0, int64_t c1, int lane) {
+    int mn[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+    int mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+    for (int64_t col = c0 + lane; col < c1; col += 64) {
+        const Vec4 f = fill_column(sv, n_vec, causal, N, col);
+        mn[0] = min(mn[0], f.lts); mx[0] = max(mx[0], f.lts);
+        mn[1] = min(mn[1], f.lte); mx[1] = max(mx[1], f.lte);
+        mn[2] = min(mn[2], f.uts); mx[2] = max(mx[2], f.uts);
+        mn[3] = min(mn[3], f.ute); mx[3] = max(mx[3], f.ute);
+    }
+    int outv = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int a = wave_min(mn[t]), z = wave_max(mx[t]);
+        if (lane == 2 * t) outv = a;
+        if (lane == 2 * t + 1) outv = z;
+    }
+    return outv;
+}
+
 // N2: one wave per key block, grid-stride over the global key blocks.
 // Lanes read consecutive columns (coalesced 256 B per vector per wave) and
 // reduce min/max across the wave.
@@ -71,22 +94,7 @@ __global__ __launch_bounds__(256) void fm_extrema_kernel(
         const int b = lo;
         const int64_t c0 = (int64_t)cu[b] + (int64_t)(g - s_off[b]) * Bc;
         const int64_t c1 = min(c0 + Bc, (int64_t)cu[b + 1]);
-        int mn[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-        int mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
-        for (int64_t col = c0 + lane; col < c1; col += 64) {
-            const Vec4 f = fill_column(sv, n_vec, causal, N, col);
-            mn[0] = min(mn[0], f.lts); mx[0] = max(mx[0], f.lts);
-            mn[1] = min(mn[1], f.lte); mx[1] = max(mx[1], f.lte);
-            mn[2] = min(mn[2], f.uts); mx[2] = max(mx[2], f.uts);
-            mn[3] = min(mn[3], f.ute); mx[3] = max(mx[3], f.ute);
-        }
-        int outv = 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int a = wave_min(mn[t]), z = wave_max(mx[t]);
-            if (lane == 2 * t) outv = a;
-            if (lane == 2 * t + 1) outv = z;
-        }
+        const int outv = block_extrema(sv, n_vec, causal, N, c0, c1, lane);
         if (lane < 8) ext[(int64_t)g * 8 + lane] = outv;
     }
 }
@@ -104,41 +112,15 @@ __device__ inline SeqDims seq_dims(const int32_t* __restrict__ cu, int b, int Br
     return d;
 }
 
-// N3a: one workgroup per sequence.  Each wave takes q tiles of its sequence,
-// classifies the tile row (one key block per lane), writes the class map,
-// counts classes, and writes the split slots of the q tile.
-__global__ __launch_bounds__(256) void fm_tiles_kernel(
-    const int32_t* __restrict__ cu, int B, int Br, int Bc, int S, int causal,
-    const int32_t* __restrict__ kb_off, const int32_t* __restrict__ ext,
-    const int32_t* __restrict__ status, int32_t* __restrict__ slots,
-    long long* __restrict__ seq_counts, int32_t* __restrict__ sl_off,
-    uint8_t* __restrict__ tile_class, int64_t tile_class_cap, int64_t slot_cap) {
-    if (*status != 0) return;
-    const int b = blockIdx.x;
-    __shared__ long long tmp[17];
-    __shared__ long long s_cnt[3];
-    // offsets of this sequence: slots (sum of Tr*MS) and class map (Tr*Tc)
-    long long slot_base = 0, map_base = 0;
-    for (int base = 0; base < b; base += blockDim.x) {
-        const int bb = base + threadIdx.x;
-        long long ns = 0, nm = 0;
-        if (bb < b) {
-            const SeqDims d = seq_dims(cu, bb, Br, Bc, S);
-            ns = (long long)d.Tr * d.MS;
-            nm = (long long)d.Tr * d.Tc;
-        }
-        long long t1, t2;
-        block_exclusive_scan(ns, tmp, &t1);
-        block_exclusive_scan(nm, tmp, &t2);
-        slot_base += t1; map_base += t2;
-    }
-    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
-    if (threadIdx.x == 0) sl_off[b] = (int32_t)slot_base;
-    __syncthreads();
-    const SeqDims d = seq_dims(cu, b, Br, Bc, S);
+// Tile classes of every q tile of sequence b (one wave per q tile, one key
+// block per lane; FlashMask article §3.2), the class map, per-thread class
+// counts, and the split slots of each q tile (cost = non-FULL blocks,
+// chunks of at most S blocks whose sizes differ by at most one).
+__device__ void classify_rows(const SeqDims& d, int b, int Br, int Bc, int S, int causal,
+                              const int4* __restrict__ xs, int32_t* __restrict__ slots, long long slot_base,
+                              int64_t slot_cap, long long map_base, uint8_t* __restrict__ tile_class,
+                              int64_t tile_class_cap, long long (&my_cnt)[3]) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const int32_t* __restrict__ xb = ext + (int64_t)kb_off[b] * 8;
-    long long my_cnt[3] = {0, 0, 0};
     for (int qt = wid; qt < d.Tr; qt += nw) {
         const int r0 = d.s + qt * Br, r1 = min(r0 + Br, d.e);
         int cost = 0, first = INT_MAX, last = -1;
@@ -147,9 +129,8 @@ __global__ __launch_bounds__(256) void fm_tiles_kernel(
             const int kb = kb0 + lane;
             bool nonfull = false;
             if (kb < d.Tc) {
-                int x[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) x[t] = xb[(int64_t)kb * 8 + t];
+                const int4 a = xs[2 * kb], z = xs[2 * kb + 1];
+                const int x[8] = {a.x, a.y, a.z, a.w, z.x, z.y, z.z, z.w};
                 const int c0 = d.s + kb * Bc, c1 = min(c0 + Bc, d.e);
                 const TileInfo ti = classify_tile(r0, r1, c0, c1, x, causal);
                 my_cnt[0] += ti.cls == CLS_FULL;
@@ -189,9 +170,8 @@ __global__ __launch_bounds__(256) void fm_tiles_kernel(
                 const int kb = kb0 + lane;
                 bool nonfull = false;
                 if (kb < d.Tc) {
-                    int x[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) x[t] = xb[(int64_t)kb * 8 + t];
+                    const int4 a = xs[2 * kb], z = xs[2 * kb + 1];
+                    const int x[8] = {a.x, a.y, a.z, a.w, z.x, z.y, z.z, z.w};
                     const int c0 = d.s + kb * Bc, c1 = min(c0 + Bc, d.e);
                     nonfull = classify_tile(r0, r1, c0, c1, x, causal).cls != CLS_FULL;
                 }
@@ -209,6 +189,54 @@ __global__ __launch_bounds__(256) void fm_tiles_kernel(
             }
         }
     }
+}
+
+// N3a: one workgroup per sequence.  The sequence's extrema are staged in LDS
+// once (one round of coalesced loads); each wave then classifies q tiles from
+// LDS (one key block per lane), writes the class map, counts classes, and
+// writes the split slots of its q tiles.
+constexpr int TILES_NTH = 512;
+constexpr int TILES_LDS_KB = 1024;   // key blocks staged in LDS (32 KB); longer rows read global memory
+
+__global__ __launch_bounds__(TILES_NTH) void fm_tiles_kernel(
+    const int32_t* __restrict__ cu, int B, int Br, int Bc, int S, int causal,
+    const int32_t* __restrict__ kb_off, const int32_t* __restrict__ ext,
+    const int32_t* __restrict__ status, int32_t* __restrict__ slots,
+    long long* __restrict__ seq_counts, int32_t* __restrict__ sl_off,
+    uint8_t* __restrict__ tile_class, int64_t tile_class_cap, int64_t slot_cap) {
+    if (*status != 0) return;
+    const int b = blockIdx.x;
+    __shared__ long long tmp[17];
+    __shared__ long long s_cnt[3];
+    __shared__ int4 s_ext[2 * TILES_LDS_KB];
+    // offsets of this sequence: slots (sum of Tr*MS) and class map (Tr*Tc)
+    long long slot_base = 0, map_base = 0;
+    for (int base = 0; base < b; base += blockDim.x) {
+        const int bb = base + threadIdx.x;
+        long long ns = 0, nm = 0;
+        if (bb < b) {
+            const SeqDims d = seq_dims(cu, bb, Br, Bc, S);
+            ns = (long long)d.Tr * d.MS;
+            nm = (long long)d.Tr * d.Tc;
+        }
+        long long t1, t2;
+        block_exclusive_scan(ns, tmp, &t1);
+        block_exclusive_scan(nm, tmp, &t2);
+        slot_base += t1; map_base += t2;
+    }
+    const SeqDims d = seq_dims(cu, b, Br, Bc, S);
+    const int4* __restrict__ xg = (const int4*)(ext + (int64_t)kb_off[b] * 8);
+    const bool in_lds = d.Tc <= TILES_LDS_KB;
+    if (in_lds)
+        for (int i = threadIdx.x; i < 2 * d.Tc; i += blockDim.x) s_ext[i] = xg[i];
+    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) sl_off[b] = (int32_t)slot_base;
+    __syncthreads();
+    const int4* xs = in_lds ? s_ext : xg;
+    long long my_cnt[3] = {0, 0, 0};
+    classify_rows(d, b, Br, Bc, S, causal, xs, slots, slot_base, slot_cap, map_base, tile_class,
+                  tile_class_cap, my_cnt);
+    const int lane = threadIdx.x & 63;
     // class counts of this sequence
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
@@ -219,31 +247,148 @@ __global__ __launch_bounds__(256) void fm_tiles_kernel(
     if (threadIdx.x < 3) seq_counts[(int64_t)b * 3 + threadIdx.x] = s_cnt[threadIdx.x];
 }
 
+// Fused preprocessing + classification for the plan path: one workgroup per
+// sequence.  Every workgroup reads all of cu_seqlens (validation and prefix
+// sums, B is small next to N), reduces the extrema of its own key blocks
+// (FlashMask article §3.1), keeps them in LDS, and classifies its q tiles
+// from LDS (§3.2).  Workgroup 0 writes kb_off, the key block count and the
+// status word.  Replaces the extrema and tiles launches of the plan path.
+__global__ __launch_bounds__(TILES_NTH) void fm_seqplan_kernel(
+    const int32_t* __restrict__ sv, int n_vec, int causal, const int32_t* __restrict__ cu, int B,
+    int64_t N, int Br, int Bc, int S, int64_t ext_cap, int64_t slot_cap,
+    int32_t* __restrict__ kb_off, int32_t* __restrict__ ext, int32_t* __restrict__ status,
+    int32_t* __restrict__ n_kblocks, int32_t* __restrict__ slots, long long* __restrict__ seq_counts,
+    int32_t* __restrict__ sl_off, uint8_t* __restrict__ tile_class, int64_t tile_class_cap) {
+    const int b = blockIdx.x;
+    __shared__ long long tmp[17];
+    __shared__ long long s_cnt[3];
+    __shared__ int s_bad;
+    __shared__ int4 s_ext[2 * TILES_LDS_KB];
+    if (threadIdx.x == 0) s_bad = (cu[0] != 0 ? FM_STATUS_CU0 : 0) | (cu[B] != (int)N ? FM_STATUS_CUN : 0);
+    __syncthreads();
+    long long kb_carry = 0, slot_base = 0, map_base = 0, kb_base = 0;
+    for (int base = 0; base < B; base += blockDim.x) {
+        const int bb = base + threadIdx.x;
+        long long tc = 0, ns = 0, nm = 0;
+        if (bb < B) {
+            const int L = cu[bb + 1] - cu[bb];
+            if (L < 0) atomicOr(&s_bad, FM_STATUS_ORDER);
+            const SeqDims d = seq_dims(cu, bb, Br, Bc, S);
+            tc = d.Tc;
+            if (bb < b) { ns = (long long)d.Tr * d.MS; nm = (long long)d.Tr * d.Tc; }
+        }
+        long long t0, t1, t2;
+        const long long ex = block_exclusive_scan(tc, tmp, &t0);
+        if (b == 0 && bb < B) kb_off[bb] = (int32_t)min(kb_carry + ex, (long long)INT_MAX);
+        if (bb == b) kb_base = kb_carry + ex;
+        kb_carry += t0;
+        block_exclusive_scan(ns, tmp, &t1);
+        block_exclusive_scan(nm, tmp, &t2);
+        slot_base += t1; map_base += t2;
+    }
+    if (threadIdx.x == 0 && kb_carry > ext_cap) atomicOr(&s_bad, FM_STATUS_CAP);
+    __syncthreads();
+    // kb_base was found by one thread: share it
+    if (threadIdx.x == (unsigned)(b % blockDim.x)) tmp[16] = kb_base;
+    __syncthreads();
+    kb_base = tmp[16];
+    const int bad = s_bad;
+    if (b == 0 && threadIdx.x == 0) {
+        kb_off[B] = (int32_t)min(kb_carry, (long long)INT_MAX);
+        *status = bad;
+        *n_kblocks = bad ? 0 : (int32_t)kb_carry;
+    }
+    if (bad) return;
+    const SeqDims d = seq_dims(cu, b, Br, Bc, S);
+    if (threadIdx.x == 0) sl_off[b] = (int32_t)slot_base;
+    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
+    // extrema of this sequence's key blocks: one wave per block
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const bool in_lds = d.Tc <= TILES_LDS_KB;
+    if (Bc <= 64) {
+        // one column per lane; the loads of 8 key blocks are in flight at once
+        constexpr int BATCH = 8;
+        for (int kb0 = wid; kb0 < d.Tc; kb0 += nw * BATCH) {
+            Vec4 f[BATCH];
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                const int kb = kb0 + j * nw;
+                const int64_t col = (int64_t)d.s + (int64_t)kb * Bc + lane;
+                const bool ok = kb < d.Tc && lane < Bc && col < d.e;
+                f[j] = ok ? fill_column(sv, n_vec, causal, N, col) : Vec4{INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+            }
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                const int kb = kb0 + j * nw;
+                if (kb >= d.Tc) break;
+                const int64_t col = (int64_t)d.s + (int64_t)kb * Bc + lane;
+                const bool ok = lane < Bc && col < d.e;
+                const int v4[4] = {f[j].lts, f[j].lte, f[j].uts, f[j].ute};
+                int outv = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int a = wave_min(ok ? v4[t] : INT_MAX), z = wave_max(ok ? v4[t] : INT_MIN);
+                    if (lane == 2 * t) outv = a;
+                    if (lane == 2 * t + 1) outv = z;
+                }
+                if (lane < 8) {
+                    ext[(kb_base + kb) * 8 + lane] = outv;
+                    if (in_lds) ((int*)s_ext)[kb * 8 + lane] = outv;
+                }
+            }
+        }
+    } else {
+        for (int kb = wid; kb < d.Tc; kb += nw) {
+            const int64_t c0 = (int64_t)d.s + (int64_t)kb * Bc, c1 = min(c0 + Bc, (int64_t)d.e);
+            const int v = block_extrema(sv, n_vec, causal, N, c0, c1, lane);
+            if (lane < 8) {
+                ext[(kb_base + kb) * 8 + lane] = v;
+                if (in_lds) ((int*)s_ext)[kb * 8 + lane] = v;
+            }
+        }
+    }
+    if (!in_lds) __threadfence();  // long rows are classified from global memory
+    __syncthreads();
+    const int4* xs = in_lds ? s_ext : (const int4*)(ext + kb_base * 8);
+    long long my_cnt[3] = {0, 0, 0};
+    classify_rows(d, b, Br, Bc, S, causal, xs, slots, slot_base, slot_cap, map_base, tile_class,
+                  tile_class_cap, my_cnt);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const long long t = wave_sum64(my_cnt[c]);
+        if (lane == 0) atomicAdd((unsigned long long*)&s_cnt[c], (unsigned long long)t);
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) seq_counts[(int64_t)b * 3 + threadIdx.x] = s_cnt[threadIdx.x];
+}
+
 // N3b: one workgroup.  Stable counting sort of the valid slots by
-// descending cost (longest first), then one item per (slot, head).
+// descending cost (longest first), then one item per (slot, head).  Round
+// trips are kept to two: the sizes (cu, class counts, status) are read
+// together, then the slot records, which stay in LDS for the ranking and the
+// scatter when they fit.
+constexpr int SORT_LDS_INTS = 16384;            // 64 KB: slot records (<= 2048) or slot costs
+constexpr int SORT_LDS_RECS = SORT_LDS_INTS / SLOT_WORDS;
+
 __global__ __launch_bounds__(1024) void fm_sort_kernel(
     const int32_t* __restrict__ cu, int B, int H, int Br, int Bc, int S, int cost_cap,
+    const int32_t* __restrict__ kb_off,
     const int32_t* __restrict__ status, int32_t* __restrict__ status_rw,
     const int32_t* __restrict__ slots, int32_t* __restrict__ pos,
     const long long* __restrict__ seq_counts, int32_t* __restrict__ items, int64_t items_cap,
     int32_t* __restrict__ n_items, long long* __restrict__ class_counts,
-    int32_t* __restrict__ sched_counter, int32_t* __restrict__ n_slots_out, int64_t slot_cap) {
-    extern __shared__ int32_t hist[];  // [cost_cap + 1]
+    int32_t* __restrict__ sched_counter, int32_t* __restrict__ n_slots_out, int64_t slot_cap,
+    int32_t* __restrict__ merge_counter) {
+    extern __shared__ int32_t hist[];  // [cost_cap + 1], then SORT_LDS_INTS of slot data
+    int32_t* s_slot = hist + ((cost_cap + 4) & ~3);
     __shared__ long long tmp[17];
     __shared__ long long s_sum[4];
     const int tid = threadIdx.x;
-    if (*status != 0) {
-        if (tid == 0) {
-            *n_items = 0;
-            class_counts[0] = class_counts[1] = class_counts[2] = 0;
-            if (sched_counter) *sched_counter = 0;
-            if (n_slots_out) *n_slots_out = 0;
-        }
-        return;
-    }
+    const int st = *status;   // read together with the sizes below
     // total slots and class counts over sequences
     long long n_slots = 0;
     if (tid < 4) s_sum[tid] = 0;
+    __syncthreads();
     for (int base = 0; base < B; base += blockDim.x) {
         const int b = base + tid;
         long long ns = 0;
@@ -257,12 +402,31 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
         block_exclusive_scan(ns, tmp, &tot);
         n_slots += tot;
     }
+    if (st != 0) {
+        if (tid == 0) {
+            *n_items = 0;
+            class_counts[0] = class_counts[1] = class_counts[2] = 0;
+            if (sched_counter) *sched_counter = 0;
+            if (n_slots_out) *n_slots_out = 0;
+        }
+        return;
+    }
     if (n_slots > slot_cap) n_slots = 0;  // cannot happen with a valid plan; no items then
+    const bool recs_in_lds = n_slots <= SORT_LDS_RECS;
+    const bool cost_in_lds = !recs_in_lds && n_slots <= SORT_LDS_INTS;
     for (int c = tid; c <= cost_cap; c += blockDim.x) hist[c] = 0;
+    if (recs_in_lds)
+        for (long long i = tid; i < n_slots * (SLOT_WORDS / 4); i += blockDim.x)
+            ((int4*)s_slot)[i] = ((const int4*)slots)[i];
     __syncthreads();
+    auto slot_cost = [&](long long sl) {   // -1: empty slot
+        const int32_t* rec = recs_in_lds ? s_slot + sl * SLOT_WORDS : slots + sl * SLOT_WORDS;
+        return rec[7] ? min(rec[6], cost_cap) : -1;
+    };
     for (long long sl = tid; sl < n_slots; sl += blockDim.x) {
-        const int32_t* rec = slots + sl * SLOT_WORDS;
-        if (rec[7]) atomicAdd(&hist[min(rec[6], cost_cap)], 1);
+        const int c = slot_cost(sl);
+        if (c >= 0) atomicAdd(&hist[c], 1);
+        if (cost_in_lds) s_slot[sl] = c;
     }
     __syncthreads();
     // descending exclusive scan: base[c] = number of valid slots with cost > c
@@ -284,13 +448,16 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
         }
     }
     __syncthreads();
+    // stable rank inside each cost: one wave walks the slots in order
     const bool overflow = total_valid * H > items_cap;
     if (!overflow && tid < 64) {
         const int lane = tid;
         for (long long chunk = 0; chunk < n_slots; chunk += 64) {
             const long long sl = chunk + lane;
-            const bool valid = sl < n_slots && slots[sl * SLOT_WORDS + 7] != 0;
-            const int cost = valid ? min(slots[sl * SLOT_WORDS + 6], cost_cap) : 0;
+            int c = -1;
+            if (sl < n_slots) c = cost_in_lds ? s_slot[sl] : slot_cost(sl);
+            const bool valid = c >= 0;
+            const int cost = valid ? c : 0;
             uint64_t eq = __ballot(valid);
             for (int bit = 0; bit < 15; ++bit) {
                 const bool bb = (cost >> bit) & 1;
@@ -309,15 +476,21 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
         }
     }
     __syncthreads();
+    if (merge_counter)
+        for (long long idx = tid; idx < n_slots * H; idx += blockDim.x) merge_counter[idx] = 0;
     if (!overflow) {
         for (long long idx = tid; idx < n_slots * H; idx += blockDim.x) {
             const long long sl = idx / H;
             const int h = (int)(idx - sl * H);
-            const int32_t* rec = slots + sl * SLOT_WORDS;
+            const int32_t* rec = recs_in_lds ? s_slot + sl * SLOT_WORDS : slots + sl * SLOT_WORDS;
             if (!rec[7]) continue;
             int32_t* it = items + ((int64_t)pos[sl] * H + h) * ITEM_WORDS;
-            it[0] = rec[0]; it[1] = h; it[2] = rec[1]; it[3] = rec[4];
+            const int b = rec[0];
+            it[0] = b; it[1] = h; it[2] = rec[1]; it[3] = rec[4];
             it[4] = rec[5]; it[5] = rec[2]; it[6] = rec[3]; it[7] = rec[6];
+            // derived words: sequence bounds, first extrema block, slot of split 0
+            it[8] = cu[b]; it[9] = cu[b + 1]; it[10] = kb_off[b]; it[11] = (int32_t)(sl - rec[2]);
+            it[12] = it[13] = it[14] = it[15] = 0;
         }
     }
     if (tid == 0) {
@@ -343,21 +516,40 @@ hipError_t launch_extrema(const int32_t* sv, int n_vec, int causal, const int32_
     return hipGetLastError();
 }
 
+hipError_t launch_plan(const int32_t* sv, int n_vec, int32_t* ext, int64_t ext_cap, int32_t* n_kblocks,
+                       int32_t* kb_off_out, const PlanPtrs& p, hipStream_t s) {
+    int32_t* slots = (int32_t*)(p.scratch + p.sl.off_slots);
+    int32_t* pos = (int32_t*)(p.scratch + p.sl.off_pos);
+    long long* seq_counts = (long long*)(p.scratch + p.sl.off_seq_counts);
+    int32_t* sl_off = (int32_t*)(p.scratch + p.sl.off_sl_off);
+    hipLaunchKernelGGL(fm_seqplan_kernel, dim3(p.B), dim3(TILES_NTH), 0, s, sv, n_vec, p.causal, p.cu, p.B,
+                       p.N, p.Br, p.Bc, p.S, ext_cap, p.sl.slot_cap, kb_off_out, ext, p.status_rw, n_kblocks,
+                       slots, seq_counts, sl_off, p.tile_class, p.tile_class_cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)(((p.cost_cap + 4) & ~3) + SORT_LDS_INTS) * sizeof(int32_t);
+    hipLaunchKernelGGL(fm_sort_kernel, dim3(1), dim3(1024), lds, s, p.cu, p.B, p.H, p.Br, p.Bc,
+                       p.S, p.cost_cap, p.kb_off, p.status, p.status_rw, slots, pos, seq_counts, p.items,
+                       p.items_cap, p.n_items, (long long*)p.class_counts, p.sched_counter,
+                       p.n_slots, p.sl.slot_cap, p.merge_counter);
+    return hipGetLastError();
+}
+
 hipError_t launch_worklist(const PlanPtrs& p, hipStream_t s) {
     int32_t* slots = (int32_t*)(p.scratch + p.sl.off_slots);
     int32_t* pos = (int32_t*)(p.scratch + p.sl.off_pos);
     long long* seq_counts = (long long*)(p.scratch + p.sl.off_seq_counts);
     int32_t* sl_off = (int32_t*)(p.scratch + p.sl.off_sl_off);
-    hipLaunchKernelGGL(fm_tiles_kernel, dim3(p.B), dim3(256), 0, s, p.cu, p.B, p.Br, p.Bc, p.S,
+    hipLaunchKernelGGL(fm_tiles_kernel, dim3(p.B), dim3(TILES_NTH), 0, s, p.cu, p.B, p.Br, p.Bc, p.S,
                        p.causal, p.kb_off, p.extrema, p.status, slots, seq_counts, sl_off,
                        p.tile_class, p.tile_class_cap, p.sl.slot_cap);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = (size_t)(p.cost_cap + 1) * sizeof(int32_t);
+    const size_t lds = (size_t)(((p.cost_cap + 4) & ~3) + SORT_LDS_INTS) * sizeof(int32_t);
     hipLaunchKernelGGL(fm_sort_kernel, dim3(1), dim3(1024), lds, s, p.cu, p.B, p.H, p.Br, p.Bc,
-                       p.S, p.cost_cap, p.status, p.status_rw, slots, pos, seq_counts, p.items,
+                       p.S, p.cost_cap, p.kb_off, p.status, p.status_rw, slots, pos, seq_counts, p.items,
                        p.items_cap, p.n_items, (long long*)p.class_counts, p.sched_counter,
-                       p.n_slots, p.sl.slot_cap);
+                       p.n_slots, p.sl.slot_cap, p.merge_counter);
     return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ def pv():
 
 def test_tile_config(pv):
     import torch
-    assert pv.tile_config(torch.bfloat16, 128) == (128, 64)
+    assert pv.tile_config(torch.bfloat16, 128) == (256, 64)
     assert pv.tile_config(torch.float32, 32) == (64, 32)
     with pytest.raises(pv.FMError) as e:
         pv.tile_config(torch.bfloat16, 64)
@@ -83,7 +83,7 @@ def _attn(pv, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(n_vec=4), 1), (dict(n_vec=3, causal=0), 1), (dict(n_vec=1, causal=0), 1),
-    (dict(D=64), 2), (dict(dtype=7), 2), (dict(bq=64), 2), (dict(dtype=1, D=32, bq=65), 2),
+    (dict(D=64), 2), (dict(dtype=7), 2), (dict(bq=64), 2), (dict(bq=128), 2), (dict(dtype=1, D=32, bq=65), 2),
     (dict(scale=0.0), 1), (dict(scale=float("inf")), 1), (dict(scale=-1.0), 1),
     (dict(flags=0x80), 1), (dict(flags=1, S=4), 1), (dict(dtype=1, D=32, S=3), 2),
     (dict(cu=None), 1), (dict(q=None), 1), (dict(ws=None), 1), (dict(ws_bytes=1024), 3),

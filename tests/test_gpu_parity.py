@@ -62,9 +62,20 @@ def check_plan_ints(pv, w, Br, Bc, S, H=None):
     flat = np.concatenate([c.reshape(-1) for c in ocls]) if ocls else np.zeros(0, np.int8)
     assert np.array_equal(wl["tile_class"][:flat.size].cpu().numpy().astype(np.int8), flat)
     items = wl["items"].cpu().numpy()
-    assert items.shape == oitems.shape, (items.shape, oitems.shape)
-    assert np.array_equal(items, oitems)
-    return items
+    assert items.shape == (oitems.shape[0], 16), (items.shape, oitems.shape)
+    assert np.array_equal(items[:, :8], oitems)
+    # derived words: sequence bounds, extrema base, slot of split 0
+    cu = w.cu_seqlens.astype(np.int64)
+    b = items[:, 0]
+    assert np.array_equal(items[:, 8], cu[b]) and np.array_equal(items[:, 9], cu[b + 1])
+    assert np.array_equal(items[:, 10], okb[b]) and np.all(items[:, 12:] == 0)
+    key = {}
+    for r in items.tolist():     # split s of one (seq, q tile) sits at slot split0_slot + s
+        key.setdefault((r[0], r[2]), set()).add(r[11])
+    assert all(len(v) == 1 for v in key.values())
+    slots = sorted(v.pop() for v in key.values())
+    assert len(set(slots)) == len(slots)
+    return items[:, :8]
 
 
 def run(pv, w, **kw):
@@ -140,6 +151,28 @@ def test_random_plan_ints(pv, seed):
     Br, Bc = int(rng.integers(1, 10)), int(rng.integers(1, 10))
     S = int(rng.choice([0, 1, 2, 5]))
     check_plan_ints(pv, w, Br, Bc, S, H=int(rng.integers(1, 4)))
+
+
+@pytest.mark.parametrize("k,S", [(1, 0), (2, 0), (2, 4), (3, 0), (4, 3), (5, 0)])
+def test_fused_plan_matches_oracle(pv, k, S):
+    """The plan path (one workgroup per sequence: extrema + classes, then the
+    sort) writes the same integers as the oracle into the workspace."""
+    w = W.make_config(k, with_qkv=False)
+    _, _, _, cu, sv = dev_inputs(w)
+    dt = torch.float32 if w.dtype == W.F32 else torch.bfloat16
+    Br, Bc = (4, 4) if k == 1 else (128, 64)
+    plan = pv.build_plan(cu, sv, w.n_vec, w.causal, w.N, w.H, w.D, dt, block_q=Br, block_k=Bc,
+                         max_kb_per_item=S, want_class_map=True)
+    hdr = plan.header()
+    okb, oext, ocls, ocnt, oitems = oracle_plan(w, Br, Bc, w.H, S)
+    assert hdr["status"] == 0 and hdr["n_kblocks"] == len(oext)
+    assert np.array_equal(plan.kb_off().cpu().numpy(), okb)
+    assert np.array_equal(plan.extrema(len(oext)).cpu().numpy(), oext)
+    assert hdr["class_counts"] == ocnt.tolist()
+    flat = np.concatenate([c.reshape(-1) for c in ocls])
+    assert np.array_equal(plan.tile_class(flat.size).cpu().numpy().astype(np.int8), flat)
+    assert hdr["n_items"] == len(oitems)
+    assert np.array_equal(plan.items(len(oitems)).cpu().numpy()[:, :8], oitems)
 
 
 # ----------------------------------------------------------------- fp32
