@@ -77,7 +77,7 @@ extern "C" {
 
 /* ---- limits ----------------------------------------------------------- */
 #define FM_MAX_SEQS        16383  /* B: sequences per call                 */
-#define FM_MAX_COST        16383  /* key blocks one q tile may visit        */
+#define FM_MAX_COST        8191   /* key blocks one work item may visit    */
 
 /* Status word bits written by the preprocessing kernel. */
 #define FM_STATUS_CU0      0x1    /* cu_seqlens[0] != 0                     */
@@ -90,6 +90,15 @@ const char* fm_last_error(void);
 
 /* Library version, e.g. 100 for 0.1.0. */
 int fm_version(void);
+
+/*
+ * Host-only check of the fixed tables the kernels derive addresses from
+ * (which wave copies which K/V block of a tile, and the row and byte each
+ * lane reads): every block is copied exactly once and every lane stays
+ * inside its tile.  Needs no GPU.  Returns FM_OK, or FM_E_INVAL with the
+ * first violation in fm_last_error().
+ */
+int fm_self_check(void);
 
 /*
  * Default tile sizes (Br query rows x Bc key columns) of fm_attn_fwd for a

@@ -65,6 +65,7 @@ def _load():
     sig = {
         "fm_last_error": (ctypes.c_char_p, []),
         "fm_version": (I, []),
+        "fm_self_check": (I, []),
         "fm_get_tile_config": (I, [I, I, P, P]),
         "fm_auto_split": (I, [I64, I, I, I, I]),
         "fm_workspace_layout": (I, [I64, I, I, I, I, I, I, I, P]),
@@ -84,7 +85,7 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("fm_last_error", "fm_version", "fm_get_tile_config", "fm_auto_split",
+EXPORTED = ("fm_last_error", "fm_version", "fm_self_check", "fm_get_tile_config", "fm_auto_split",
             "fm_workspace_layout", "fm_workspace_size", "fm_worklist_scratch_size",
             "fm_preprocess_mask", "fm_build_worklist", "fm_build_plan", "fm_attn_fwd",
             "fm_read_status")
@@ -120,6 +121,11 @@ def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
 # ---------------------------------------------------------------- queries
 def version() -> int:
     return _lib.fm_version()
+
+
+def self_check() -> None:
+    """Host-only check of the kernels' fixed copy tables (no GPU needed)."""
+    _check(_lib.fm_self_check())
 
 
 def tile_config(dtype: torch.dtype, head_dim: int):

@@ -4,6 +4,7 @@
 // stream synchronisation (except the fm_read_status test helper).
 #include "fm_api.h"
 #include "fm_internal.h"
+#include "fm_bf16_copies.h"
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -257,6 +258,37 @@ extern "C" {
 const char* fm_last_error(void) { return g_err.c_str(); }
 
 int fm_version(void) { return 100; }
+
+int fm_self_check(void) {
+    using namespace fm::bf16c;
+    for (int g = 0; g < 2; ++g) {
+        const int nblk = g == 0 ? KBLK : VBLK, ch = g == 0 ? KCH : VCH;
+        int seen[SLOT_BLK] = {0};
+        for (int t = 0; t < GW; ++t)
+            for (int i = 0; i < NCOPY; ++i) {
+                const int blk = copy_block(t, i);
+                if (blk < 0 || blk >= SLOT_BLK)
+                    return fail(FM_E_INVAL, "copy table: group %d wave %d copy %d fills block %d", g, t, i, blk);
+                seen[blk]++;
+                for (int lane = 0; lane < 64; ++lane) {
+                    const uint32_t cp = copy_lane(g, t, i, lane);
+                    const int row = (int)(cp & 0xffu), byte = (int)(cp >> 8);
+                    if (row >= BC || byte > 16 * 15 || byte % 16)
+                        return fail(FM_E_INVAL, "copy table: group %d wave %d copy %d lane %d reads row %d byte %d",
+                                    g, t, i, lane, row, byte);
+                    // a data block must hold exactly the chunk the kernel reads there
+                    if (blk < nblk) {
+                        const int q = 64 * blk + lane;
+                        if (row != q / ch || (q % ch < 16 && byte != 16 * (q % ch)))
+                            return fail(FM_E_INVAL, "copy table: group %d block %d lane %d misplaced", g, blk, lane);
+                    }
+                }
+            }
+        for (int b = 0; b < SLOT_BLK; ++b)
+            if (seen[b] != 1) return fail(FM_E_INVAL, "copy table: group %d block %d filled %d times", g, b, seen[b]);
+    }
+    return FM_OK;
+}
 
 int fm_get_tile_config(int dtype, int head_dim, int* block_q, int* block_k) {
     if (!block_q || !block_k) return fail(FM_E_INVAL, "null pointer argument");

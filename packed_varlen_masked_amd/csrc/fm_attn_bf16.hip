@@ -13,29 +13,37 @@
 //
 // Layout and schedule (this file's own):
 //   * one workgroup = 8 waves = one 256-row q tile; wave w owns rows
-//     32w..32w+31.  Every staged K/V tile feeds 256 query rows, which halves
-//     the global->LDS traffic per MFMA against 128-row tiles.  The kernel is persistent: workgroups pull items from the
-//     longest-first work list with one atomic counter.
+//     32w..32w+31.  Every staged K/V tile feeds 256 query rows.  The kernel
+//     is persistent: workgroups pull items from the longest-first work list
+//     with one atomic counter.
 //   * scores are computed transposed, S^T = K Q^T, so that in the MFMA
 //     result each lane holds ONE query (lane & 31) and 16 keys per 32x32
 //     tile.  Row max / row sum are per-lane reductions plus one exchange
 //     with lane ^ 32, and O^T = V^T P^T keeps that ownership, so the
 //     online-softmax rescale of O is a per-lane scalar.
-//   * K and V tiles sit row-major in LDS ([key][channel], rows padded to
-//     272 B).  The V^T operand is read with the gfx950 LDS transpose read
-//     (ds_read_b64_tr_b16): each 16-lane group receives a 16-channel x
-//     4-key block with one channel per lane.
-//   * two LDS buffers: the global loads of the next visited tile are issued
-//     before the current tile's MFMAs and written to the other buffer after
-//     them, so HBM/L2 latency hides behind the matrix work.
+//   * K and V tiles sit row-major in LDS ([key][channel], rows padded); the
+//     V^T operand is read with the gfx950 LDS transpose read
+//     (ds_read_b64_tr_b16).
+//   * ping-pong: waves 0-3 (group 0) and 4-7 (group 1) hold one wave per
+//     SIMD each and run half a step apart.  A step of tile m is an MFMA
+//     phase (S_m = K_m Q^T, then O += V_{m-1} P_{m-1}) and a softmax phase
+//     (mask, online softmax of S_m -> P_m).  While one group is in its MFMA
+//     phase the other is in its softmax phase, so every SIMD has matrix and
+//     vector work in flight at once; a workgroup barrier separates phases.
+//   * a 3-deep ring of K and V buffers filled by asynchronous global->LDS
+//     copies.  Everything that is not matrix work (issuing copies, walking
+//     the visit list) sits in the softmax phase: at its start a group-0 wave
+//     issues its shares of K_{m+2} and V_{m+1} (and the mask vectors of tile
+//     m+2), a group-1 wave, one tile further ahead, of K_{m+3} and V_{m+2};
+//     each waits for a batch two phases after the next one was issued.
 //   * long rows are split over several items; each writes an fp32 partial
-//     (O, m, l) and the last one to finish merges all partials in split
-//     order (deterministic), then resets its counter.
+//     (O, m, l) that the merge kernel combines in split order.
 #include <algorithm>
 
 #include "fm_common.hpp"
 #include "fm_internal.h"
 #include "fm_api.h"
+#include "fm_bf16_copies.h"
 
 namespace fm {
 
@@ -49,6 +57,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BR = 256, BC = 64, HD = 128;
 constexpr int NW = 8, NTH = 64 * NW;    // 8 waves, 32 query rows each
+constexpr int GW = NW / 2;              // waves per ping-pong group
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr int PART = BR * HD + 2 * BR;  // floats per split partial: O row-major, then m, l
 // Lazy rescale: the running row max used for the exponentials moves only when
@@ -65,64 +74,60 @@ constexpr float RESCALE_LOG2 = 8.0f;
 constexpr int KCH = 17, VCH = 20;                  // 16-byte chunks per row
 constexpr int KBYTES = BC * KCH * 16;              // 17408
 constexpr int VBYTES = BC * VCH * 16;              // 20480
-constexpr int BUFBYTES = KBYTES + VBYTES;          // one K/V buffer
-constexpr int KBLK = KBYTES / 1024, VBLK = VBYTES / 1024;   // 1 KB load blocks: 17, 20
+constexpr int KBLK = KBYTES / 1024, VBLK = VBYTES / 1024;   // 1 KB copy blocks: 17, 20
+constexpr int MVW = 4 * BC;                        // mask-vector words per tile
+static_assert(KCH == bf16c::KCH && VCH == bf16c::VCH && BC == bf16c::BC && NW == 2 * bf16c::GW &&
+              KBLK == bf16c::KBLK && VBLK == bf16c::VBLK, "copy table and kernel agree");
 
-// Asynchronous global -> LDS loads of one K/V tile into buffer `buf`.  A
-// wave instruction writes 1 KB of LDS in lane order (16 B per lane); lane L of
-// block blk fills chunk q = 64*blk + L of the tile, i.e. row q / CH, chunk
-// q % CH.  Wave w issues blocks w, w+4, ...: q grows by 256 per block, so the
-// lane's (row, chunk) advances by a fixed step and the address is a uniform
-// tile base plus a 32-bit lane offset.  Padding
-// chunks load chunk 0 of their row (never read).  Rows past the sequence end
-// read its last valid key (finite data, masked out later), so every address
-// stays inside the tensor.
-__device__ __attribute__((always_inline)) inline void tile_issue(
-    char* kdst, char* vdst, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, int64_t rs,
-    int64_t hoff, int c0, int c1, int w, int lane) {
-    const int last = c1 - 1 - c0;                       // last valid row of the tile
-    const char* kt = (const char*)(K + (int64_t)c0 * rs + hoff);
-    const char* vt = (const char*)(V + (int64_t)c0 * rs + hoff);
-    const uint32_t rsb = (uint32_t)(rs * 2);            // row stride in bytes
-    // wave w issues blocks w, w + NW, ...: the chunk index q grows by 64 * NW
-    // per block, i.e. (row, chunk) advances by (KSTEP_R, KSTEP_C)
-    constexpr int QS = 64 * NW;
-    constexpr int KSTEP_R = QS / KCH, KSTEP_C = QS % KCH;
-    constexpr int VSTEP_R = QS / VCH, VSTEP_C = QS % VCH;
-    const int q = 64 * w + lane;
-    int r = q / KCH, c = q - r * KCH;
-#pragma unroll
-    for (int i = 0; i < (KBLK + NW - 1) / NW; ++i) {
-        if (NW * i + w < KBLK) {
-            const uint32_t off = (uint32_t)min(r, last) * rsb + 16u * (uint32_t)(c < 16 ? c : 0);
-            __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void*)(kdst + (NW * i + w) * 1024), 16, 0, 0);
-        }
-        c += KSTEP_C; r += KSTEP_R;
-        if (c >= KCH) { c -= KCH; r += 1; }
-    }
-    r = q / VCH; c = q - r * VCH;
-#pragma unroll
-    for (int i = 0; i < (VBLK + NW - 1) / NW; ++i) {
-        if (NW * i + w < VBLK) {
-            const uint32_t off = (uint32_t)min(r, last) * rsb + 16u * (uint32_t)(c < 16 ? c : 0);
-            __builtin_amdgcn_global_load_lds((const void*)(vt + off), (lds_void*)(vdst + (NW * i + w) * 1024), 16, 0, 0);
-        }
-        c += VSTEP_C; r += VSTEP_R;
-        if (c >= VCH) { c -= VCH; r += 1; }
-    }
+// The ring: three K slots, then three V slots, 20 KB each (a K tile fills 17
+// KB, the rest of its slot takes the copies that keep every wave's count
+// even), then the mask-vector slots.  Copies into the ring are issued with
+// inline assembly, so the compiler does not track them: every wait for them
+// is explicit (see the step below).
+constexpr int SLOT_BYTES = bf16c::SLOT_BLK * 1024;
+__shared__ __attribute__((aligned(1024))) char s_kv[6 * SLOT_BYTES];
+__shared__ __attribute__((aligned(16))) int32_t s_mv[3 * MVW];
+__shared__ __attribute__((aligned(16))) int32_t s_sink[GW * BC];   // mask rows of absent vectors (never read)
+__device__ __attribute__((always_inline)) inline char* kbuf(int i) { return s_kv + i * SLOT_BYTES; }
+__device__ __attribute__((always_inline)) inline char* vbuf(int i) { return s_kv + (3 + i) * SLOT_BYTES; }
+
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __attribute__((always_inline)) inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+// One asynchronous copy instruction: 64 lanes x 16 B (or x 4 B) from
+// base + voff (per lane) to LDS at dst + 16 * lane (4 * lane).  The leading
+// s_nop covers the wait states between the scalar writes of the base / M0
+// and their use by the copy.
+__device__ __attribute__((always_inline)) inline void dma16(void* dst, const void* base, uint32_t voff) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(base), "{m0}"(lds_addr(dst))
+                 : "memory");
+}
+__device__ __attribute__((always_inline)) inline void dma4(void* dst, const void* base, uint32_t voff) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" :: "v"(voff), "s"(base), "{m0}"(lds_addr(dst))
+                 : "memory");
 }
 
-__device__ __attribute__((always_inline)) inline void stage_mv(const AttnArgs& a, int32_t* mv, int c0, int c1,
-                                                               int tid) {
-    if (tid < BC) {
-        const int64_t col = (int64_t)c0 + tid;
-        const Vec4 f = col < c1 ? fill_column(a.sv, a.n_vec, a.causal, a.N, col)
-                                : Vec4{INT_MIN, INT_MAX, INT_MIN, INT_MAX};
-        mv[tid] = f.lts; mv[BC + tid] = f.lte; mv[2 * BC + tid] = f.uts; mv[3 * BC + tid] = f.ute;
-    }
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (s_waitcnt immediate; expcnt and lgkmcnt untouched).
+template <int N>
+__device__ __attribute__((always_inline)) inline void wait_vm() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
+// Workgroup barrier between phases.  No implied wait: every wave has already
+// waited for the copies the next phase reads, and LDS reads of a phase are
+// consumed (hence complete) inside it.  The memory clobber and scheduling
+// barriers keep the compiler from moving work across phases.
+__device__ __attribute__((always_inline)) inline void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
 
 // Combine a per-lane value with the one of lane ^ 32 (the other half of the
 // same query row) using the gfx950 lane swap: every lane receives both halves
@@ -137,105 +142,105 @@ __device__ inline float halves_sum(float x) {
 }
 __device__ inline uint32_t bf16_bits(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); }
 
-__device__ inline int64_t partial_index(const AttnArgs& a, int b, int qt, int s, int h, int Tc) {
-    const int MS = (a.S > 0 && Tc > 0) ? ceil_div(Tc, a.S) : 1;
-    return ((int64_t)a.sl_off[b] + (int64_t)qt * MS + s) * a.H + h;
-}
-
 struct Item {
     int b, h, qt, kbb, kbe, sidx, nsp;
-    int s_b, e_b, Tc, r0, r1, kb_hi;
+    int s_b, e_b, Tc, r0, r1;
     int64_t hoff;
     const int32_t* xb;
 };
-
-// Visit and interval bits of a window of up to 64 key blocks [base, base+64),
-// one bit per block, from one vector load of the extrema per lane and two
-// ballots (FlashMask article §3.2 rules): the KV loop does no lookups.
-struct Win {
-    int base;
-    uint64_t visit, iv;
-};
-
-__device__ __attribute__((always_inline)) inline void load_window(Win& W, const AttnArgs& a, const Item& I,
-                                                                  int base, bool no_skip, int lane) {
-    const int kb = base + lane;
-    bool v = false, iv = false;
-    if (kb < I.kb_hi) {
-        const u32x4 x0 = *(const u32x4*)(I.xb + (int64_t)kb * 8);
-        const u32x4 x1 = *(const u32x4*)(I.xb + (int64_t)kb * 8 + 4);
-        const int x[8] = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-        const int c0 = I.s_b + kb * BC, c1 = min(c0 + BC, I.e_b);
-        const TileInfo ti = classify_tile(I.r0, I.r1, c0, c1, x, a.causal);
-        v = !ti.causal_full && (ti.cls != CLS_FULL || no_skip);
-        iv = ti.need_lt || ti.need_ut;
-    }
-    W.base = base;
-    W.visit = __ballot(v);
-    W.iv = __ballot(iv);
-}
-
-// First visited key block at or after kb (loading windows as needed); *iv
-// receives whether its interval vectors must be applied element-wise.
-__device__ __attribute__((always_inline)) inline int next_visit(Win& W, const AttnArgs& a, const Item& I,
-                                                                int kb, bool no_skip, int lane, bool* iv) {
-    for (;;) {
-        if (kb >= I.kb_hi) return I.kb_hi;
-        if (kb >= W.base + 64) load_window(W, a, I, kb, no_skip, lane);
-        const uint64_t m = W.visit >> (kb - W.base);
-        if (m) {
-            kb += __builtin_ctzll(m);
-            *iv = (W.iv >> (kb - W.base)) & 1;
-            return kb;
-        }
-        kb = W.base + 64;
-    }
-}
 
 struct State {
     float m_run, l_run;
     f32x16 o[4];
 };
 
-// One key block, computed from `cur` while the next visited block streams
-// into `nxt`.  Returns the next visited key block (*niv: its interval flag).
-__device__ __attribute__((always_inline)) inline int kv_step(
-    const AttnArgs& a, const Item& I, Win& W, int kb, bool iv, bool* niv, const char* kbase, const char* vbase,
-    const int32_t* cmv, char* nk, char* nv, int32_t* nmv,
-    const bf16x8 (&qf)[8], State& st, bool no_skip, int tid, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, int64_t rs) {
-    const int lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
-    const int grp = lane >> 4, gi = lane & 15;
-    const int c0 = I.s_b + kb * BC, c1 = min(c0 + BC, I.e_b);
-    const bool ragged = (c1 - c0) < BC;
-    const bool causal = a.causal && (c1 > I.r0 + 1);   // tile reaches above the diagonal
-    const float sl2 = a.scale_log2;
-    const int qrow = I.r0 + 32 * w + n;
+// Per-wave constants of the item loop.
+struct Wave {
+    int tid, lane, w, g, t, n, hh, qrow;   // t: wave index inside its group
+    int mv_src;        // group 0: stored vector behind mask vector t (-1: absent)
+    uint32_t rsb;      // row stride of q/k/v in bytes
+    uint32_t cp[5];    // per-lane source of the wave's copies: row | (byte in row << 8)
+    uint32_t vo[5];    // the same as byte offsets for a tile of 64 rows
+    bool no_skip;
+};
 
-    // ---- prefetch the next visited tile (asynchronous, straight to LDS) ----
-    const int nkb = next_visit(W, a, I, kb + 1, no_skip, lane, niv);
-    if (nkb < I.kb_hi) {
-        const int nc0 = I.s_b + nkb * BC, nc1 = min(nc0 + BC, I.e_b);
-        tile_issue(nk, nv, K, V, rs, I.hoff, nc0, nc1, w, lane);
-        if (*niv) stage_mv(a, nmv, nc0, nc1, tid);
-    }
-
-    // ---- S^T = K Q^T : two 32-key tiles x 8 k-steps ----
-    f32x16 sacc[2];
+// MFMA phase, part 1: S^T = K Q^T, two 32-key tiles x 8 k-steps.  K
+// fragments are read two k-steps ahead of the MFMAs that use them.
+__device__ __attribute__((always_inline)) inline void s_part(const char* kl, const bf16x8 (&qf)[8],
+                                                             f32x16 (&sacc)[2], int n, int hh) {
+    const char* kp = kl + n * (KCH * 16) + 16 * hh;
+    auto kfrag = [&](int t, int s) { return as_bf16x8(*(const u32x4*)(kp + 32 * t * (KCH * 16) + 32 * s)); };
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
+    bf16x8 ka[3][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) ka[s][t] = kfrag(t, s);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
+        if (s + 2 < 8) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const bf16x8 ka = as_bf16x8(*(const u32x4*)(kbase + (32 * t + n) * (KCH * 16) + 32 * s + 16 * hh));
-            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[t], 0, 0, 0);
+            for (int t = 0; t < 2; ++t) ka[(s + 2) % 3][t] = kfrag(t, s + 2);
         }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % 3][t], qf[s], sacc[t], 0, 0, 0);
     }
-    // ---- element masks; register e of tile t holds key 32t + 8(e>>2) + 4hh + (e&3) ----
+    // keep the order: 4 reads, then (2 reads, 2 MFMAs) x 6, then 4 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+// MFMA phase, part 2: O^T += V^T P^T; V^T read with the LDS transpose read,
+// one 16-key group ahead of the MFMAs that use it.
+__device__ __attribute__((always_inline)) inline void pv_part(const char* vb, const bf16x8 (&pb)[2][2],
+                                                              State& st, int lane) {
+    const int hh = lane >> 5, grp = lane >> 4, gi = lane & 15;
+    // lane part of the address: rows 4hh + gi/4, chunk 2(grp&1) + (gi&3)/2, half gi&1
+    const char* vl = vb + (4 * hh + (gi >> 2)) * (VCH * 16) + 16 * (2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+    auto vfrag = [&](int kg, int dt) {   // key group kg = 2t + c: keys 16kg..16kg+15
+        const char* p = vl + 16 * kg * (VCH * 16) + 64 * dt;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)p);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)(p + 8 * VCH * 16));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8 va[2][4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) va[0][dt] = vfrag(0, dt);
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+        if (kg + 1 < 4) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) va[(kg + 1) & 1][dt] = vfrag(kg + 1, dt);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kg & 1][dt], pb[kg >> 1][kg & 1], st.o[dt], 0, 0, 0);
+    }
+    // keep the order: 8 reads, then (8 reads, 4 MFMAs) x 3, then 4 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int kg = 0; kg < 3; ++kg) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+// Softmax phase of one tile: element masks (only where the tile needs them),
+// online softmax in base 2 with the scale folded in and lazy rescaling of O,
+// then P in bf16.  Register e of tile t holds key 32t + 8(e>>2) + 4hh + (e&3).
+__device__ __attribute__((always_inline)) inline void softmax_part(
+    f32x16 (&sacc)[2], State& st, bf16x8 (&pb)[2][2], bool causal, bool ragged, bool iv, int c0, int c1,
+    int qrow, const int32_t* cmv, float sl2, int hh) {
     if (causal || ragged || iv) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -265,7 +270,6 @@ __device__ __attribute__((always_inline)) inline int kv_step(
             }
         }
     }
-    // ---- online softmax (base 2, scale folded, lazy rescale) ----
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -284,7 +288,6 @@ __device__ __attribute__((always_inline)) inline int kv_step(
     }
     const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
     float rsum = 0.f;
-    bf16x8 pb[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -298,55 +301,169 @@ __device__ __attribute__((always_inline)) inline int kv_step(
         }
     }
     st.l_run += halves_sum(rsum);
-    // ---- O^T += V^T P^T ; V^T read with the LDS transpose read ----
+}
+
+// ---- copies -----------------------------------------------------------
+// Group 0 copies K tiles (and the mask vectors), group 1 copies V tiles: a
+// tile is 20 blocks of 1 KB in its slot, wave t of the group fills blocks
+// t, t+4, ..., t+16 with one copy instruction each (lane L of a block
+// carries chunk 64*blk + L of the tile, i.e. row q / CH, chunk q % CH;
+// chunks >= 16 are row padding).
+constexpr int VIS_CAP = FM_MAX_COST + 1;   // visited key blocks per item
+constexpr int WIN_CAP = VIS_CAP / 64;      // 64-block windows of the visit scan
+
+// Tile geometry of key block kb of the item: first row, last valid row
+// index inside the tile, and the byte offset of its first row from the
+// item's head base.
+struct Tile {
+    int c0, last;
+    size_t off;
+};
+__device__ __attribute__((always_inline)) inline Tile tile_at(const Item& I, const Wave& Wv, int kb) {
+    Tile t;
+    t.c0 = I.s_b + kb * BC;
+    t.last = min(BC, I.e_b - t.c0) - 1;
+    t.off = (size_t)t.c0 * Wv.rsb;
+    return t;
+}
+
+// This wave's five block copies of the tile at `src` into the slot at `dst`
+// (rows past the tile's last valid row repeat it: finite data, masked later).
+__device__ __attribute__((always_inline)) inline void copy_tile(const Wave& Wv, const char* src, int last,
+                                                                char* dst) {
+    if (last == BC - 1) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+        for (int i = 0; i < 5; ++i) dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src, Wv.vo[i]);
+    } else {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            // lane part of the address: rows 4hh + gi/4, chunk 2(grp&1) + (gi&3)/2, half gi&1
-            const char* vl = vbase + (4 * hh + (gi >> 2)) * (VCH * 16) +
-                             16 * (2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const char* p = vl + (32 * t + 16 * c) * (VCH * 16) + 64 * dt;
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)p);
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)(p + 8 * VCH * 16));
-                const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t][c], st.o[dt], 0, 0, 0);
-            }
-        }
+        for (int i = 0; i < 5; ++i)
+            dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src,
+                  (uint32_t)min((int)(Wv.cp[i] & 0xffu), last) * Wv.rsb + (Wv.cp[i] >> 8));
     }
-    __builtin_amdgcn_s_waitcnt(0);  // the next tile's LDS writes have landed
-    __syncthreads();
-    return nkb;
+}
+
+// Group 0: mask vector t of the tile (absent vectors go to the sink).
+__device__ __attribute__((always_inline)) inline void copy_mask(const AttnArgs& a, const Wave& Wv, const Tile& tl,
+                                                                int32_t* slot) {
+    const bool own = Wv.mv_src >= 0;
+    const int32_t* src = a.sv + (own ? (int64_t)Wv.mv_src * a.N : 0) + tl.c0;
+    dma4(own ? slot + Wv.t * BC : s_sink + Wv.t * BC, src, 4u * (uint32_t)min(Wv.lane, tl.last));
+}
+
+// One batch: group 0 copies K and the mask vectors of the tile into K slot
+// u / mask slot u (6 instructions), group 1 copies V into V slot u (5).
+__device__ __attribute__((always_inline)) inline void copy_batch(const AttnArgs& a, const Item& I, const Wave& Wv,
+                                                                 const char* Kh, const char* Vh, int kb, int u) {
+    const Tile tl = tile_at(I, Wv, kb);
+    if (Wv.g == 0) {
+        copy_tile(Wv, Kh + tl.off, tl.last, kbuf(u));
+        copy_mask(a, Wv, tl, s_mv + u * MVW);
+    } else {
+        copy_tile(Wv, Vh + tl.off, tl.last, vbuf(u));
+    }
+}
+constexpr int BATCH_G0 = 6, BATCH_G1 = 5;   // copy instructions per batch
+
+// Visit queue: key blocks of the visited tiles m .. m+3 (indices past the
+// item's last visited tile repeat it) and the interval flags of m .. m+3.
+struct Queue {
+    int k0, k1, k2, k3;
+    uint32_t iv;   // bit j: tile m + j needs the interval vectors
+};
+
+__shared__ uint16_t s_vis[VIS_CAP];       // visited key blocks of the item, bit 15 = interval flag
+__shared__ uint64_t s_wvis[WIN_CAP], s_wiv[WIN_CAP];
+__shared__ int32_t s_wcnt[WIN_CAP];
+
+__device__ __attribute__((always_inline)) inline int vis_entry(int i) {
+    return __builtin_amdgcn_readfirstlane((int)s_vis[i]);
+}
+
+// Ring slots of the current step: tile m sits in slot u0 = m mod 3,
+// u1 = (m+1) mod 3, u2 = (m+2) mod 3 (= the slot of tile m-1).
+struct Slots {
+    int u0, u1, u2;
+    __device__ void next() { const int t = u0; u0 = u1; u1 = u2; u2 = t; }
+};
+
+// One step (tile m, T visited tiles).  At the start of its softmax phase of
+// tile m a wave copies tile m+2: group 0 its K (and mask vectors) into K
+// slot u2, last read two phases before; group 1 its V into V slot u2, last
+// read one phase before.  A batch is waited for two phases after the next
+// one was issued: group 0 at the end of its softmax phase of tile m+1,
+// group 1 at the end of its MFMA phase of tile m+3.
+template <bool FIRST>
+__device__ __attribute__((always_inline)) inline void kv_step(
+    const AttnArgs& a, const Item& I, Queue& Qu, const Wave& Wv, Slots& sl, int m, int T, bool& rec_pending,
+    int nxt, int& nrec, int n_items, const bf16x8 (&qf)[8], f32x16 (&sacc)[2], bf16x8 (&pb)[2][2], State& st,
+    const char* Kh, const char* Vh) {
+    // ---- MFMA phase: S_m, then O += V_{m-1} P_{m-1} ----
+    __builtin_amdgcn_s_setprio(1);
+    s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh);
+    if constexpr (!FIRST) pv_part(vbuf(sl.u2), pb, st, Wv.lane);
+    __builtin_amdgcn_s_setprio(0);
+    if (Wv.g == 1) wait_vm<BATCH_G1>();
+    phase_barrier();
+    // ---- softmax phase of tile m, copies in flight ----
+    const int nk = vis_entry(min(m + 4, T - 1));
+    if (rec_pending) {   // wave 0: the next item's record, ahead of this batch
+        const int nx = __builtin_amdgcn_readfirstlane(nxt);
+        if (nx < n_items && Wv.lane < ITEM_WORDS) nrec = a.items[(int64_t)nx * ITEM_WORDS + Wv.lane];
+        rec_pending = false;
+    }
+    copy_batch(a, I, Wv, Kh, Vh, Qu.k2, sl.u2);
+    {
+        const int c0 = I.s_b + Qu.k0 * BC, c1 = min(c0 + BC, I.e_b);
+        const bool causal = a.causal && (c1 > I.r0 + 1);
+        softmax_part(sacc, st, pb, causal, (c1 - c0) < BC, (Qu.iv & 1u) != 0, c0, c1, Wv.qrow,
+                     s_mv + sl.u0 * MVW, a.scale_log2, Wv.hh);
+    }
+    Qu.k0 = Qu.k1; Qu.k1 = Qu.k2; Qu.k2 = Qu.k3; Qu.k3 = nk & 0x7fff;
+    Qu.iv = (Qu.iv >> 1) | ((uint32_t)(nk >> 15) << 3);
+    sl.next();
+    if (Wv.g == 0) wait_vm<BATCH_G0>();
+    phase_barrier();
 }
 
 __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
-    static_assert(NTH / 64 == NW && BR == 32 * NW, "one wave per 32 query rows");
-    // two K/V buffers as distinct LDS objects, so that the compiler can tell
-    // the tile being read from the one being loaded asynchronously
-    __shared__ __attribute__((aligned(1024))) char k0[KBYTES];
-    __shared__ __attribute__((aligned(1024))) char v0[VBYTES];
-    __shared__ __attribute__((aligned(1024))) char k1[KBYTES];
-    __shared__ __attribute__((aligned(1024))) char v1[VBYTES];
-    __shared__ __attribute__((aligned(16))) int32_t mv0[4 * BC];
-    __shared__ __attribute__((aligned(16))) int32_t mv1[4 * BC];
+    static_assert(NTH / 64 == NW && BR == 32 * NW && GW == 4, "one wave per 32 query rows, one per SIMD per group");
     __shared__ __attribute__((aligned(16))) int32_t s_rec[ITEM_WORDS];
     __shared__ int32_t s_next;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+    Wave Wv;
+    Wv.tid = threadIdx.x; Wv.lane = Wv.tid & 63; Wv.w = __builtin_amdgcn_readfirstlane(Wv.tid >> 6);
+    Wv.g = Wv.w / GW; Wv.t = Wv.w % GW; Wv.n = Wv.lane & 31; Wv.hh = Wv.lane >> 5;
+    Wv.no_skip = (a.flags & FM_FLAG_NO_SKIP) != 0;
+    Wv.rsb = (uint32_t)(a.H * HD * 2);
+    const int tid = Wv.tid, lane = Wv.lane, w = Wv.w;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        Wv.cp[i] = bf16c::copy_lane(Wv.g, Wv.t, i, lane);
+        Wv.vo[i] = (Wv.cp[i] & 0xffu) * Wv.rsb + (Wv.cp[i] >> 8);
+    }
     const int n_items = __builtin_amdgcn_readfirstlane(*a.n_items);
     const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
-    const uint16_t* __restrict__ K = (const uint16_t*)a.k;
-    const uint16_t* __restrict__ V = (const uint16_t*)a.v;
     const int64_t rs = (int64_t)a.H * HD;
-    const bool no_skip = (a.flags & FM_FLAG_NO_SKIP) != 0;
+
+    // Stored vector behind each logical mask vector (LTS, LTE, UTS, UTE) for
+    // the accepted (n_vec, causal) pairs; wave t of group 0 stages vector t.
+    // Absent ones take their default (LTE: N; UTS, UTE: 0), written into
+    // every mask slot once.
+    auto vsrc = [&](int t) {
+        return t == 0 ? 0
+             : t == 1 ? ((a.n_vec == 4 || (a.causal && a.n_vec == 2)) ? 1 : -1)
+             : t == 2 ? (a.n_vec == 4 ? 2 : -1)
+             : (a.n_vec == 4 ? 3 : (!a.causal && a.n_vec == 2) ? 1 : -1);
+    };
+    Wv.mv_src = Wv.g == 0 ? vsrc(Wv.t) : -1;
+    for (int i = tid; i < 3 * MVW; i += NTH) {
+        const int t = (i % MVW) / BC;
+        if (vsrc(t) < 0) s_mv[i] = t == 1 ? (int)a.N : 0;
+    }
 
     // Work fetch: every fetch returns the next index; a workgroup stops at its
     // first index >= n_items.  The launch's last fetch (index
-    // n_items + gridDim.x - 1) resets the counter for the next call.  The
-    // next item's index and record are fetched while the current item's first
-    // tile loads, and handed over through LDS when the item ends.
+    // n_items + gridDim.x - 1) resets the counter for the next call.
     const int last_fetch = n_items + (int)gridDim.x - 1;
     if (tid == 0) {
         const int v = atomicAdd(a.sched_counter, 1);
@@ -358,62 +475,77 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
     if (it < n_items && tid < ITEM_WORDS) s_rec[tid] = a.items[(int64_t)it * ITEM_WORDS + tid];
     __syncthreads();
     while (it < n_items) {
-        int nxt = 0;
-        if (tid == 0) nxt = atomicAdd(a.sched_counter, 1);   // consumed below, after the tile loads issue
+        int nxt = 0, nrec = 0;
+        if (tid == 0) nxt = atomicAdd(a.sched_counter, 1);
         Item I;
-        I.b = s_rec[0]; I.h = s_rec[1]; I.qt = s_rec[2]; I.kbb = s_rec[3]; I.kbe = s_rec[4];
-        I.sidx = s_rec[5]; I.nsp = s_rec[6];
-        I.s_b = s_rec[8]; I.e_b = s_rec[9];
-        const int kb_base = s_rec[10], slot0 = s_rec[11];
+        // the record is the same for every lane: keep it in scalar registers
+        auto rec = [&](int i) { return __builtin_amdgcn_readfirstlane(s_rec[i]); };
+        I.b = rec(0); I.h = rec(1); I.qt = rec(2); I.kbb = rec(3); I.kbe = rec(4);
+        I.sidx = rec(5); I.nsp = rec(6);
+        I.s_b = rec(8); I.e_b = rec(9);
+        const int kb_base = rec(10), slot0 = rec(11);
         I.Tc = ceil_div(I.e_b - I.s_b, BC);
         I.r0 = I.s_b + I.qt * BR; I.r1 = min(I.r0 + BR, I.e_b);
         I.xb = a.extrema + (int64_t)kb_base * 8;
         I.hoff = (int64_t)I.h * HD;
-        I.kb_hi = no_skip ? I.Tc : I.kbe;
-        const int qrow = I.r0 + 32 * w + n;
+        Wv.qrow = I.r0 + 32 * w + Wv.n;
+        const char* Kh = (const char*)a.k + I.hoff * 2;
+        const char* Vh = (const char*)a.v + I.hoff * 2;
+        const int lo = Wv.no_skip ? 0 : I.kbb, hi = Wv.no_skip ? I.Tc : I.kbe;
 
-        // first tile (kb_begin is visited by construction of the work list),
-        // Q fragments and the first flag window go out together
-        Win W;
-        W.base = INT_MIN / 2;
-        W.visit = 0;
-        W.iv = 0;
-        bool iv = false, niv = false;
-        int kb = no_skip ? I.kb_hi : I.kbb;
-        if (no_skip) kb = next_visit(W, a, I, 0, no_skip, lane, &iv);
-        if (kb < I.kb_hi) {
-            const int c0 = I.s_b + kb * BC, c1 = min(c0 + BC, I.e_b);
-            tile_issue(k0, v0, K, V, rs, I.hoff, c0, c1, w, lane);
-        }
-        // Q^T fragments (B operand): lane holds query n, channels 16s+8hh..+7
-        bf16x8 qf[8];
-        if (qrow < I.r1) {
-            const uint16_t* qp = Q + (int64_t)qrow * rs + I.hoff + 8 * hh;
+        // Q fragments and the first tile (kb_begin is visited by construction
+        // of the work list) go out before the visit scan
+        bf16x8 qf[8];   // Q^T fragments (B operand): lane holds query n, channels 16s+8hh..+7
+        if (Wv.qrow < I.r1) {
+            const uint16_t* qp = Q + (int64_t)Wv.qrow * rs + I.hoff + 8 * Wv.hh;
 #pragma unroll
             for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
         } else {
 #pragma unroll
             for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
         }
-        // next item's record: waits only for the fetch issued first, not for
-        // the tile and Q loads behind it
-        int nrec = 0;
-        if (w == 0) {
-            nxt = __builtin_amdgcn_readfirstlane(nxt);
-            if (nxt == last_fetch && lane == 0) atomicExch(a.sched_counter, 0);
-            if (nxt < n_items && lane < ITEM_WORDS) nrec = a.items[(int64_t)nxt * ITEM_WORDS + lane];
-        }
-        if (kb < I.kb_hi) {
-            if (!no_skip) {
-                load_window(W, a, I, kb, no_skip, lane);
-                iv = W.iv & 1;
+
+        if (!Wv.no_skip && lo < hi) copy_batch(a, I, Wv, Kh, Vh, lo, 0);
+
+        // Visit scan (FlashMask article §3.2 rules): windows of 64 key blocks,
+        // one extrema row per lane; wave w takes windows w, w+8, ...
+        const int nwin = lo < hi ? ceil_div(hi - lo, 64) : 0;
+        for (int j = w; j < nwin; j += NW) {
+            const int kb = lo + 64 * j + lane;
+            bool v = false, iv = false;
+            if (kb < hi) {
+                const u32x4 x0 = *(const u32x4*)(I.xb + (int64_t)kb * 8);
+                const u32x4 x1 = *(const u32x4*)(I.xb + (int64_t)kb * 8 + 4);
+                const int x[8] = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                  (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                const int c0 = I.s_b + kb * BC, c1 = min(c0 + BC, I.e_b);
+                const TileInfo ti = classify_tile(I.r0, I.r1, c0, c1, x, a.causal);
+                v = !ti.causal_full && (ti.cls != CLS_FULL || Wv.no_skip);
+                iv = ti.need_lt || ti.need_ut;
             }
-            if (iv) {
-                const int c0 = I.s_b + kb * BC;
-                stage_mv(a, mv0, c0, min(c0 + BC, I.e_b), tid);
+            const uint64_t vm = __ballot(v), im = __ballot(iv);
+            if (lane == 0) { s_wvis[j] = vm; s_wiv[j] = im; s_wcnt[j] = __popcll(vm); }
+        }
+        __syncthreads();
+        int T = 0;
+        for (int j0 = 0; j0 < nwin; j0 += 64) {   // total visited tiles
+            const int j = j0 + lane;
+            T += __reduce_add_sync(~0ull, j < nwin ? s_wcnt[j] : 0);
+        }
+        T = __builtin_amdgcn_readfirstlane(T);
+        for (int j = w; j < nwin; j += NW) {
+            int base = 0;
+            for (int j0 = 0; j0 < j; j0 += 64) {
+                const int jj = j0 + lane;
+                base += __reduce_add_sync(~0ull, jj < j ? s_wcnt[jj] : 0);
+            }
+            const uint64_t vm = s_wvis[j], im = s_wiv[j];
+            if ((vm >> lane) & 1ull) {
+                const int pos = base + __popcll(vm & lanemask_lt());
+                if (pos < VIS_CAP) s_vis[pos] = (uint16_t)((lo + 64 * j + lane) | (int)(((im >> lane) & 1ull) << 15));
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
+        T = min(T, VIS_CAP);
         __syncthreads();
 
         State st;
@@ -422,14 +554,37 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) st.o[dt][e] = 0.f;
-        while (kb < I.kb_hi) {
-            kb = kv_step(a, I, W, kb, iv, &niv, k0, v0, mv0, k1, v1, mv1, qf, st, no_skip, tid, K, V, rs);
-            if (kb >= I.kb_hi) break;
-            kb = kv_step(a, I, W, kb, niv, &iv, k1, v1, mv1, k0, v0, mv0, qf, st, no_skip, tid, K, V, rs);
+        bool rec_pending = (w == 0);
+        if (T > 0) {
+            Queue Qu;
+            const int e0 = vis_entry(0), e1 = vis_entry(min(1, T - 1)), e2 = vis_entry(min(2, T - 1)),
+                      e3 = vis_entry(min(3, T - 1));
+            Qu.k0 = e0 & 0x7fff; Qu.k1 = e1 & 0x7fff; Qu.k2 = e2 & 0x7fff; Qu.k3 = e3 & 0x7fff;
+            Qu.iv = (uint32_t)((e0 >> 15) | ((e1 >> 15) << 1) | ((e2 >> 15) << 2) | ((e3 >> 15) << 3));
+            // prologue: tile 0 (when not sent yet) must land before the first
+            // phase, tile 1 before the third (group 1 waits at the end of its
+            // first MFMA phase, group 0 at the end of its first softmax phase)
+            if (Wv.no_skip) copy_batch(a, I, Wv, Kh, Vh, Qu.k0, 0);
+            copy_batch(a, I, Wv, Kh, Vh, Qu.k1, 1);
+            if (Wv.g == 0) wait_vm<BATCH_G0>(); else wait_vm<BATCH_G1>();
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+            phase_barrier();
+            f32x16 sacc[2];
+            bf16x8 pb[2][2];
+            if (Wv.g == 1) phase_barrier();   // group 1 runs one phase behind
+            Slots sl{0, 1, 2};
+            kv_step<true>(a, I, Qu, Wv, sl, 0, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh);
+            for (int m = 1; m < T; ++m)
+                kv_step<false>(a, I, Qu, Wv, sl, m, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh);
+            // last MFMA phase: O += V_{T-1} P_{T-1} (tile T-1 sits in slot u2 now)
+            __builtin_amdgcn_s_setprio(1);
+            pv_part(vbuf(sl.u2), pb, st, lane);
+            __builtin_amdgcn_s_setprio(0);
+            phase_barrier();
         }
 
         // ---- epilogue: normalised bf16 row, or the fp32 partial of a split row ----
-        const int lr = 32 * w + n;
+        const int lr = 32 * w + Wv.n, hh = Wv.hh;
         if (I.nsp > 1) {
             float* po = a.partial + ((int64_t)(slot0 + I.sidx) * a.H + I.h) * PART;
 #pragma unroll
@@ -439,10 +594,10 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
                     *(float4*)(po + lr * HD + 32 * dt + 8 * g + 4 * hh) =
                         float4{st.o[dt][4 * g], st.o[dt][4 * g + 1], st.o[dt][4 * g + 2], st.o[dt][4 * g + 3]};
             if (hh == 0) { po[BR * HD + lr] = st.m_run; po[BR * HD + BR + lr] = st.l_run; }
-        } else if (qrow < I.r1) {
+        } else if (Wv.qrow < I.r1) {
             const float l = st.l_run;
             const float inv = l > 0.f ? 1.f / l : 0.f;
-            uint16_t* op = (uint16_t*)a.out + (int64_t)qrow * rs + I.hoff + 4 * hh;
+            uint16_t* op = (uint16_t*)a.out + (int64_t)Wv.qrow * rs + I.hoff + 4 * hh;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -452,16 +607,28 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
                     wv.y = bf16_bits(st.o[dt][4 * g + 2] * inv) | (bf16_bits(st.o[dt][4 * g + 3] * inv) << 16);
                     *(u32x2*)(op + 32 * dt + 8 * g) = wv;
                 }
-            if (hh == 0) a.lse[(int64_t)I.h * a.N + qrow] = l > 0.f ? (st.m_run + __log2f(l)) * LN2 : -INFINITY;
+            if (hh == 0) a.lse[(int64_t)I.h * a.N + Wv.qrow] = l > 0.f ? (st.m_run + __log2f(l)) * LN2 : -INFINITY;
         }
-        __syncthreads();  // every wave is done with s_rec and the LDS buffers
+        if (T > 0 && Wv.g == 0) phase_barrier();   // pairs with group 1's last MFMA phase
+
+        if (rec_pending) {
+            nxt = __builtin_amdgcn_readfirstlane(nxt);
+            if (nxt < n_items && lane < ITEM_WORDS) nrec = a.items[(int64_t)nxt * ITEM_WORDS + lane];
+        }
+        // copies past the item's last tile may still be in flight: drain them
+        // before the next item refills the ring
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // every wave is done with s_rec, the visit list and the LDS buffers
         if (w == 0) {
+            nxt = __builtin_amdgcn_readfirstlane(nxt);
+            if (nxt == last_fetch && lane == 0) atomicExch(a.sched_counter, 0);
             if (lane < ITEM_WORDS) s_rec[lane] = nrec;
             if (lane == 0) s_next = nxt;
         }
         __syncthreads();
         it = __builtin_amdgcn_readfirstlane(s_next);
     }
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // N5: merge of split partials in split order (deterministic).  Task =

@@ -32,6 +32,12 @@ def pv():
     return pytest.importorskip("packed_varlen_masked_amd")
 
 
+def test_copy_tables(pv):
+    """The bf16 kernel's copy table: every K/V block copied once, every lane
+    reading a row inside its 64-row tile (checked on the host)."""
+    pv.self_check()
+
+
 def test_tile_config(pv):
     import torch
     assert pv.tile_config(torch.bfloat16, 128) == (256, 64)
