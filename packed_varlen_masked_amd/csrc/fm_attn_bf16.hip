@@ -24,18 +24,16 @@
 //   * K and V tiles sit row-major in LDS ([key][channel], rows padded); the
 //     V^T operand is read with the gfx950 LDS transpose read
 //     (ds_read_b64_tr_b16).
-//   * ping-pong: waves 0-3 (group 0) and 4-7 (group 1) hold one wave per
-//     SIMD each and run half a step apart.  A step of tile m is an MFMA
-//     phase (S_m = K_m Q^T, then O += V_{m-1} P_{m-1}) and a softmax phase
-//     (mask, online softmax of S_m -> P_m).  While one group is in its MFMA
-//     phase the other is in its softmax phase, so every SIMD has matrix and
-//     vector work in flight at once; a workgroup barrier separates phases.
+//   * software pipeline inside every wave: a step issues the MFMAs of
+//     S_j = K_j Q^T beside the exponentials of tile j-1, then the MFMAs of
+//     O += V_{j-1} P_{j-1} beside the masks and row max of tile j, so the
+//     vector work of the softmax runs in the shadow of the wave's own matrix
+//     work, and the two waves of a SIMD share its matrix pipe.  All waves
+//     advance together, one workgroup barrier per step.
 //   * a 3-deep ring of K and V buffers filled by asynchronous global->LDS
-//     copies.  Everything that is not matrix work (issuing copies, walking
-//     the visit list) sits in the softmax phase: at its start a group-0 wave
-//     issues its shares of K_{m+2} and V_{m+1} (and the mask vectors of tile
-//     m+2), a group-1 wave, one tile further ahead, of K_{m+3} and V_{m+2};
-//     each waits for a batch two phases after the next one was issued.
+//     copies (inline assembly, waited for explicitly): in step j waves 0-3
+//     copy K_{j+2} and its mask vectors, waves 4-7 copy V_{j+1}; a step
+//     ends by waiting for the copies of the step before.
 //   * long rows are split over several items; each writes an fp32 partial
 //     (O, m, l) that the merge kernel combines in split order.
 #include <algorithm>
@@ -159,8 +157,7 @@ struct Wave {
     int tid, lane, w, g, t, n, hh, qrow;   // t: wave index inside its group
     int mv_src;        // group 0: stored vector behind mask vector t (-1: absent)
     uint32_t rsb;      // row stride of q/k/v in bytes
-    uint32_t cp[5];    // per-lane source of the wave's copies: row | (byte in row << 8)
-    uint32_t vo[5];    // the same as byte offsets for a tile of 64 rows
+    uint32_t vo[5];    // per-lane source byte offsets of the wave's copies in a tile of 64 rows
     bool no_skip;
 };
 
@@ -235,12 +232,15 @@ __device__ __attribute__((always_inline)) inline void pv_part(const char* vb, co
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
-// Softmax phase of one tile: element masks (only where the tile needs them),
-// online softmax in base 2 with the scale folded in and lazy rescaling of O,
-// then P in bf16.  Register e of tile t holds key 32t + 8(e>>2) + 4hh + (e&3).
-__device__ __attribute__((always_inline)) inline void softmax_part(
-    f32x16 (&sacc)[2], State& st, bf16x8 (&pb)[2][2], bool causal, bool ragged, bool iv, int c0, int c1,
-    int qrow, const int32_t* cmv, float sl2, int hh) {
+// Softmax of a tile, split in two so that each part runs beside matrix work:
+//   mask_max: element masks (only where the tile needs them) and the row
+//             maximum of the scaled scores;
+//   exp_tail: p = exp2(scale * s - m) in base 2 with the scale folded in,
+//             P in bf16 and the row sum, one tile later.
+// Register e of tile t holds key 32t + 8(e>>2) + 4hh + (e&3).
+__device__ __attribute__((always_inline)) inline float mask_max(f32x16 (&sacc)[2], bool causal, bool ragged, bool iv,
+                                                                int c0, int c1, int qrow, const int32_t* cmv,
+                                                                float sl2, int hh) {
     if (causal || ragged || iv) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -270,24 +270,29 @@ __device__ __attribute__((always_inline)) inline void softmax_part(
             }
         }
     }
-    float mx = -INFINITY;
+    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[t][e]);
-    mx = halves_max(mx) * sl2;
+        for (int e = 0; e < 16; ++e) mq[e & 3] = fmaxf(mq[e & 3], sacc[t][e]);
+    return halves_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * sl2;
+}
+
+// Exponentials of a tile against the running max, after the lazy max
+// update: the max used for the exponentials moves only when a score exceeds
+// it by more than 2^RESCALE_LOG2 (p then stays <= 2^8).  Returns the factor
+// alpha by which O and l must be rescaled (1 when the max did not move);
+// the new row sum is added to l after that rescale by the caller.
+__device__ __attribute__((always_inline)) inline float exp_tile(const f32x16 (&sacc)[2], float mx, State& st,
+                                                                bf16x8 (&pb)[2][2], float sl2, float& rsum) {
+    float alpha = 1.f;
     if (__any(mx > st.m_run + RESCALE_LOG2)) {
         const float m_new = fmaxf(st.m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(st.m_run - (m_new == -INFINITY ? 0.f : m_new));
-        st.l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
+        alpha = __builtin_amdgcn_exp2f(st.m_run - (m_new == -INFINITY ? 0.f : m_new));
         st.m_run = m_new;
     }
     const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
-    float rsum = 0.f;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -295,12 +300,13 @@ __device__ __attribute__((always_inline)) inline void softmax_part(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][8 * c + e], sl2, -m_use));
-                rsum += p;
+                rs[e & 3] += p;
                 pb[t][c][e] = (__bf16)p;
             }
         }
     }
-    st.l_run += halves_sum(rsum);
+    rsum = halves_sum((rs[0] + rs[1]) + (rs[2] + rs[3]));
+    return alpha;
 }
 
 // ---- copies -----------------------------------------------------------
@@ -334,11 +340,12 @@ __device__ __attribute__((always_inline)) inline void copy_tile(const Wave& Wv, 
     if (last == BC - 1) {
 #pragma unroll
         for (int i = 0; i < 5; ++i) dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src, Wv.vo[i]);
-    } else {
+    } else {   // the last tile of a sequence: rows past `last` repeat it
 #pragma unroll
-        for (int i = 0; i < 5; ++i)
-            dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src,
-                  (uint32_t)min((int)(Wv.cp[i] & 0xffu), last) * Wv.rsb + (Wv.cp[i] >> 8));
+        for (int i = 0; i < 5; ++i) {
+            const uint32_t cp = bf16c::copy_lane(Wv.g, Wv.t, i, Wv.lane);
+            dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src, (uint32_t)min((int)(cp & 0xffu), last) * Wv.rsb + (cp >> 8));
+        }
     }
 }
 
@@ -350,19 +357,19 @@ __device__ __attribute__((always_inline)) inline void copy_mask(const AttnArgs& 
     dma4(own ? slot + Wv.t * BC : s_sink + Wv.t * BC, src, 4u * (uint32_t)min(Wv.lane, tl.last));
 }
 
-// One batch: group 0 copies K and the mask vectors of the tile into K slot
-// u / mask slot u (6 instructions), group 1 copies V into V slot u (5).
-__device__ __attribute__((always_inline)) inline void copy_batch(const AttnArgs& a, const Item& I, const Wave& Wv,
-                                                                 const char* Kh, const char* Vh, int kb, int u) {
+// First tile of an item: group 0 copies its K and mask vectors into slot 0,
+// group 1 its V into slot 0.
+__device__ __attribute__((always_inline)) inline void copy_tile_pair(const AttnArgs& a, const Item& I, const Wave& Wv,
+                                                                     const char* Kh, const char* Vh, int kb) {
     const Tile tl = tile_at(I, Wv, kb);
     if (Wv.g == 0) {
-        copy_tile(Wv, Kh + tl.off, tl.last, kbuf(u));
-        copy_mask(a, Wv, tl, s_mv + u * MVW);
+        copy_tile(Wv, Kh + tl.off, tl.last, kbuf(0));
+        copy_mask(a, Wv, tl, s_mv);
     } else {
-        copy_tile(Wv, Vh + tl.off, tl.last, vbuf(u));
+        copy_tile(Wv, Vh + tl.off, tl.last, vbuf(0));
     }
 }
-constexpr int BATCH_G0 = 6, BATCH_G1 = 5;   // copy instructions per batch
+constexpr int BATCH_G0 = 6, BATCH_G1 = 5;   // copy instructions per wave per step (groups 0, 1)
 
 // Visit queue: key blocks of the visited tiles m .. m+3 (indices past the
 // item's last visited tile repeat it) and the interval flags of m .. m+3.
@@ -379,49 +386,67 @@ __device__ __attribute__((always_inline)) inline int vis_entry(int i) {
     return __builtin_amdgcn_readfirstlane((int)s_vis[i]);
 }
 
-// Ring slots of the current step: tile m sits in slot u0 = m mod 3,
-// u1 = (m+1) mod 3, u2 = (m+2) mod 3 (= the slot of tile m-1).
+// Ring slots of step j: K_j and V_j sit in slot u0 = j mod 3, K_{j+1} and
+// V_{j+1} in u1, and u2 = (j+2) mod 3 = (j-1) mod 3 still holds V_{j-1}.
 struct Slots {
     int u0, u1, u2;
     __device__ void next() { const int t = u0; u0 = u1; u1 = u2; u2 = t; }
 };
 
-// One step (tile m, T visited tiles).  At the start of its softmax phase of
-// tile m a wave copies tile m+2: group 0 its K (and mask vectors) into K
-// slot u2, last read two phases before; group 1 its V into V slot u2, last
-// read one phase before.  A batch is waited for two phases after the next
-// one was issued: group 0 at the end of its softmax phase of tile m+1,
-// group 1 at the end of its MFMA phase of tile m+3.
-template <bool FIRST>
+// Step j of the KV loop, j = 0..T-1 (all waves in step).  Every wave is
+// software-pipelined over two tiles:
+//   S_j = K_j Q^T on MFMA; then the masks and row max of tile j;
+//   O += V_{j-1} P_{j-1} on MFMA, beside the exponentials of tile j (P_j);
+//   then the lazy rescale of O and l for tile j.
+// P_{-1} is zero and the V slot of step 0 holds zeros, so step 0 adds
+// exactly nothing to O; the product of the last tile follows the loop.  At
+// the start of a step group 0 copies K_{j+2} (and its mask vectors) into K
+// slot u2 and group 1 copies V_{j+1} into V slot u1, both last read in step
+// j-1; a step ends by waiting for the previous step's copies, then a
+// barrier.
 __device__ __attribute__((always_inline)) inline void kv_step(
-    const AttnArgs& a, const Item& I, Queue& Qu, const Wave& Wv, Slots& sl, int m, int T, bool& rec_pending,
-    int nxt, int& nrec, int n_items, const bf16x8 (&qf)[8], f32x16 (&sacc)[2], bf16x8 (&pb)[2][2], State& st,
-    const char* Kh, const char* Vh) {
-    // ---- MFMA phase: S_m, then O += V_{m-1} P_{m-1} ----
-    __builtin_amdgcn_s_setprio(1);
-    s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh);
-    if constexpr (!FIRST) pv_part(vbuf(sl.u2), pb, st, Wv.lane);
-    __builtin_amdgcn_s_setprio(0);
-    if (Wv.g == 1) wait_vm<BATCH_G1>();
-    phase_barrier();
-    // ---- softmax phase of tile m, copies in flight ----
-    const int nk = vis_entry(min(m + 4, T - 1));
-    if (rec_pending) {   // wave 0: the next item's record, ahead of this batch
+    const AttnArgs& a, const Item& I, Queue& Qu, const Wave& Wv, Slots& sl, int j, int T, bool& rec_pending,
+    int nxt, int& nrec, int n_items, const bf16x8 (&qf)[8], f32x16 (&sacc)[2], bf16x8 (&pb)[2][2],
+    State& st, const char* Kh, const char* Vh) {
+    const int nk_raw = s_vis[min(j + 4, T - 1)];
+    if (rec_pending) {   // wave 0: the next item's record, ahead of this step's copies
         const int nx = __builtin_amdgcn_readfirstlane(nxt);
         if (nx < n_items && Wv.lane < ITEM_WORDS) nrec = a.items[(int64_t)nx * ITEM_WORDS + Wv.lane];
         rec_pending = false;
     }
-    copy_batch(a, I, Wv, Kh, Vh, Qu.k2, sl.u2);
-    {
-        const int c0 = I.s_b + Qu.k0 * BC, c1 = min(c0 + BC, I.e_b);
-        const bool causal = a.causal && (c1 > I.r0 + 1);
-        softmax_part(sacc, st, pb, causal, (c1 - c0) < BC, (Qu.iv & 1u) != 0, c0, c1, Wv.qrow,
-                     s_mv + sl.u0 * MVW, a.scale_log2, Wv.hh);
+    if (Wv.g == 0) {
+        const Tile tl = tile_at(I, Wv, Qu.k2);
+        copy_tile(Wv, Kh + tl.off, tl.last, kbuf(sl.u2));
+        copy_mask(a, Wv, tl, s_mv + sl.u2 * MVW);
+    } else {
+        const Tile tl = tile_at(I, Wv, Qu.k1);
+        copy_tile(Wv, Vh + tl.off, tl.last, vbuf(sl.u1));
     }
+    s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh);
+    const int c0 = I.s_b + Qu.k0 * BC, c1 = min(c0 + BC, I.e_b);
+    const bool causal = a.causal && (c1 > I.r0 + 1);
+    const float mx = mask_max(sacc, causal, (c1 - c0) < BC, (Qu.iv & 1u) != 0, c0, c1, Wv.qrow,
+                              s_mv + sl.u0 * MVW, a.scale_log2, Wv.hh);
+    bf16x8 pn[2][2];
+    float rsum;
+    const float alpha = exp_tile(sacc, mx, st, pn, a.scale_log2, rsum);
+    pv_part(vbuf(sl.u2), pb, st, Wv.lane);
+    if (alpha != 1.f) {   // rare: the running max moved
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
+    }
+    st.l_run = st.l_run * alpha + rsum;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) pb[t][c] = pn[t][c];
+    const int nk = __builtin_amdgcn_readfirstlane(nk_raw);
     Qu.k0 = Qu.k1; Qu.k1 = Qu.k2; Qu.k2 = Qu.k3; Qu.k3 = nk & 0x7fff;
     Qu.iv = (Qu.iv >> 1) | ((uint32_t)(nk >> 15) << 3);
     sl.next();
-    if (Wv.g == 0) wait_vm<BATCH_G0>();
+    if (Wv.g == 0) wait_vm<BATCH_G0>(); else wait_vm<BATCH_G1>();
     phase_barrier();
 }
 
@@ -438,8 +463,8 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
     const int tid = Wv.tid, lane = Wv.lane, w = Wv.w;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
-        Wv.cp[i] = bf16c::copy_lane(Wv.g, Wv.t, i, lane);
-        Wv.vo[i] = (Wv.cp[i] & 0xffu) * Wv.rsb + (Wv.cp[i] >> 8);
+        const uint32_t cp = bf16c::copy_lane(Wv.g, Wv.t, i, lane);
+        Wv.vo[i] = (cp & 0xffu) * Wv.rsb + (cp >> 8);
     }
     const int n_items = __builtin_amdgcn_readfirstlane(*a.n_items);
     const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
@@ -505,7 +530,7 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
             for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
         }
 
-        if (!Wv.no_skip && lo < hi) copy_batch(a, I, Wv, Kh, Vh, lo, 0);
+        if (!Wv.no_skip && lo < hi) copy_tile_pair(a, I, Wv, Kh, Vh, lo);
 
         // Visit scan (FlashMask article §3.2 rules): windows of 64 key blocks,
         // one extrema row per lane; wave w takes windows w, w+8, ...
@@ -561,26 +586,30 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
                       e3 = vis_entry(min(3, T - 1));
             Qu.k0 = e0 & 0x7fff; Qu.k1 = e1 & 0x7fff; Qu.k2 = e2 & 0x7fff; Qu.k3 = e3 & 0x7fff;
             Qu.iv = (uint32_t)((e0 >> 15) | ((e1 >> 15) << 1) | ((e2 >> 15) << 2) | ((e3 >> 15) << 3));
-            // prologue: tile 0 (when not sent yet) must land before the first
-            // phase, tile 1 before the third (group 1 waits at the end of its
-            // first MFMA phase, group 0 at the end of its first softmax phase)
-            if (Wv.no_skip) copy_batch(a, I, Wv, Kh, Vh, Qu.k0, 0);
-            copy_batch(a, I, Wv, Kh, Vh, Qu.k1, 1);
-            if (Wv.g == 0) wait_vm<BATCH_G0>(); else wait_vm<BATCH_G1>();
+            // prologue: K_0 and its mask vectors land before step 0; K_1 (and
+            // masks) and V_0 are waited for at the end of step 0.  V slot 2,
+            // read in step 0 against P = 0, is cleared.
+            if (Wv.no_skip) copy_tile_pair(a, I, Wv, Kh, Vh, Qu.k0);
+            if (Wv.g == 0) {
+                const Tile t1 = tile_at(I, Wv, Qu.k1);
+                copy_tile(Wv, Kh + t1.off, t1.last, kbuf(1));
+                copy_mask(a, Wv, t1, s_mv + MVW);
+                wait_vm<BATCH_G0>();
+            }
+            for (int i = tid; i < SLOT_BYTES / 16; i += NTH) ((u32x4*)vbuf(2))[i] = u32x4{0, 0, 0, 0};
             __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
             phase_barrier();
             f32x16 sacc[2];
             bf16x8 pb[2][2];
-            if (Wv.g == 1) phase_barrier();   // group 1 runs one phase behind
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) pb[t][c] = as_bf16x8(u32x4{0, 0, 0, 0});   // P_{-1}
             Slots sl{0, 1, 2};
-            kv_step<true>(a, I, Qu, Wv, sl, 0, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh);
-            for (int m = 1; m < T; ++m)
-                kv_step<false>(a, I, Qu, Wv, sl, m, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh);
-            // last MFMA phase: O += V_{T-1} P_{T-1} (tile T-1 sits in slot u2 now)
-            __builtin_amdgcn_s_setprio(1);
+            for (int j = 0; j < T; ++j)
+                kv_step(a, I, Qu, Wv, sl, j, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh);
+            // O += V_{T-1} P_{T-1} (tile T-1 sits in slot u2 now)
             pv_part(vbuf(sl.u2), pb, st, lane);
-            __builtin_amdgcn_s_setprio(0);
-            phase_barrier();
         }
 
         // ---- epilogue: normalised bf16 row, or the fp32 partial of a split row ----
@@ -609,7 +638,6 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
                 }
             if (hh == 0) a.lse[(int64_t)I.h * a.N + Wv.qrow] = l > 0.f ? (st.m_run + __log2f(l)) * LN2 : -INFINITY;
         }
-        if (T > 0 && Wv.g == 0) phase_barrier();   // pairs with group 1's last MFMA phase
 
         if (rec_pending) {
             nxt = __builtin_amdgcn_readfirstlane(nxt);
