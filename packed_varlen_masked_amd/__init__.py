@@ -76,6 +76,7 @@ def _load():
         "fm_build_plan": (I, [P, I, I64, I, I, I, P, I, I, I, I, I, I, P, SZ, P]),
         "fm_attn_fwd": (I, [P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, I, I, I, P, SZ, U, P]),
         "fm_read_status": (I, [P, P, P]),
+        "fm_fused_path": (I, [I64, I, I, I, I, I, I, I, U]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -88,7 +89,7 @@ _lib = _load()
 EXPORTED = ("fm_last_error", "fm_version", "fm_self_check", "fm_get_tile_config", "fm_auto_split",
             "fm_workspace_layout", "fm_workspace_size", "fm_worklist_scratch_size",
             "fm_preprocess_mask", "fm_build_worklist", "fm_build_plan", "fm_attn_fwd",
-            "fm_read_status")
+            "fm_read_status", "fm_fused_path")
 
 
 def _check(rc: int):
@@ -139,6 +140,15 @@ def auto_split(N: int, B: int, H: int, dtype: torch.dtype, head_dim: int) -> int
     if s < 0:
         raise FMError(FM_E_INVAL, "bad sizes")
     return s
+
+
+def fused_path(N: int, B: int, H: int, head_dim: int, dtype: torch.dtype, n_vec: int, causal: bool,
+               max_kb_per_item: int = -1, flags: int = 0) -> bool:
+    """True if attn_fwd takes the fused one-launch path for these sizes."""
+    r = _lib.fm_fused_path(N, B, H, head_dim, _dtype_code(dtype), n_vec, int(causal), max_kb_per_item, flags)
+    if r < 0:
+        raise FMError(FM_E_INVAL, "bad sizes")
+    return r == 1
 
 
 def workspace_layout(N: int, B: int, H: int, head_dim: int, block_q: int, block_k: int,
@@ -254,7 +264,7 @@ def build_plan(cu_seqlens: torch.Tensor, startend: torch.Tensor, n_vec: int, cau
     B = cu.numel() - 1
     bq, bk, S = _resolve(N, B, H, head_dim, dtype, block_q, block_k, max_kb_per_item)
     lay = workspace_layout(N, B, H, head_dim, bq, bk, S, want_class_map)
-    ws = torch.empty(lay.bytes, dtype=torch.uint8, device=cu.device)
+    ws = torch.zeros(lay.bytes, dtype=torch.uint8, device=cu.device)
     _check(_lib.fm_build_plan(_ptr(cu), B, N, H, head_dim, _dtype_code(dtype),
                               _ptr(startend) if N > 0 else None, n_vec, int(causal), bq, bk, S,
                               int(want_class_map), _ptr(ws), ws.numel(), _stream()))
@@ -305,7 +315,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
         bq, bk, S = _resolve(N, B, H, D, q.dtype, block_q, block_k, max_kb_per_item)
         if workspace is None:
             lay = workspace_layout(N, B, H, D, bq, bk, S, False)
-            ws = torch.empty(lay.bytes, dtype=torch.uint8, device=q.device)
+            ws = torch.zeros(lay.bytes, dtype=torch.uint8, device=q.device)
         else:
             ws = workspace
     if out is None:

@@ -5,6 +5,7 @@
 #include "fm_api.h"
 #include "fm_internal.h"
 #include "fm_bf16_copies.h"
+#include "fm_lds_plan.h"
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -125,6 +126,19 @@ int auto_split(int64_t N, int B, int H, int dtype) {
     return est_items >= 512 ? 0 : 6;
 }
 
+// The fused path (one launch that plans in LDS and attends) takes a call
+// when every bound of the in-workgroup planner holds for these sizes.
+bool fused_eligible(int64_t N, int B, int H, int dtype, int D, int bq, int bk, int S, int n_vec,
+                    unsigned flags, int n_cu) {
+    if (dtype != FM_BF16 || D != 128 || bq != 256 || bk != 64 || N <= 0) return false;
+    if (flags & (FM_FLAG_NO_SKIP | FM_FLAG_PLAN_READY)) return false;
+    if (B > fm::LP_MAX_B || (int64_t)n_vec * N > fm::LP_MAX_SV) return false;
+    Caps c;
+    if (!compute_caps(N, B, H, bq, bk, S, &c)) return false;
+    return c.kb <= fm::LP_MAX_KB && c.qt <= fm::LP_MAX_ROWS && c.map <= fm::LP_MAX_TILES &&
+           c.slot <= fm::LP_MAX_SLOTS && c.item <= (int64_t)fm::LP_MAX_MY * fm::fused_grid(n_cu);
+}
+
 int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_map,
                 fm_ws_layout* out) {
     int rc = check_sizes(N, B, H);
@@ -137,6 +151,8 @@ int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_
     if (c.cost > FM_MAX_COST)
         return fail(FM_E_UNSUPPORTED, "a q tile may visit %d key blocks (> %d); raise block_k or split",
                     c.cost, FM_MAX_COST);
+    if (cdiv(N, Bc) > 32767)   // visit-list entries hold the key block in 15 bits
+        return fail(FM_E_UNSUPPORTED, "more than 32767 key blocks (N / block_k); raise block_k");
     const fm::ScratchLayout sl = scratch_layout(B, c);
     fm_ws_layout L;
     memset(&L, 0, sizeof(L));
@@ -400,12 +416,13 @@ int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t 
     if ((rc = layout_impl(N, B, H, D, bq, bk, S, 0, &w.L))) return rc;
     if (ws_bytes < w.L.bytes) return fail(FM_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.L.bytes);
     w.base = (char*)workspace;
-    if (!(flags & FM_FLAG_PLAN_READY)) {
+    int n_cu = 0;
+    if ((rc = device_cus(&n_cu))) return rc;
+    const bool fused = fused_eligible(N, B, H, dtype, D, bq, bk, S, n_vec, flags, n_cu);
+    if (!fused && !(flags & FM_FLAG_PLAN_READY)) {
         if ((rc = build_plan_impl(w, cu_seqlens, B, N, H, startend, n_vec, causal, stream))) return rc;
     }
     if (N == 0) return ok();
-    int n_cu = 0;
-    if ((rc = device_cus(&n_cu))) return rc;
     fm::AttnArgs a;
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = softmax_lse;
     a.N = N; a.H = H; a.D = D; a.B = B;
@@ -427,10 +444,26 @@ int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t 
     a.partial = S > 0 ? (float*)(w.base + w.L.off_partial) : nullptr;
     a.merge_counter = S > 0 ? (int32_t*)(w.base + w.L.off_merge) : nullptr;
     a.flags = flags;
-    const hipError_t e = dtype == FM_BF16 ? fm::launch_attn_bf16(a, n_cu, stream)
+    a.w_hdr = w.hdr();
+    a.w_kb_off = (int32_t*)(w.base + w.L.off_kb_off);
+    a.w_ext = (int32_t*)(w.base + w.L.off_extrema);
+    a.w_items = (int32_t*)(w.base + w.L.off_items);
+    a.w_counts = w.counts();
+    const hipError_t e = fused ? fm::launch_fused_bf16(a, n_cu, stream)
+                       : dtype == FM_BF16 ? fm::launch_attn_bf16(a, n_cu, stream)
                                           : fm::launch_attn_f32(a, n_cu, stream);
     if ((rc = hip_check(e, "attention launch"))) return rc;
     return ok();
+}
+
+int fm_fused_path(int64_t N, int B, int H, int head_dim, int dtype, int n_vec, int causal,
+                  int max_kb_per_item, unsigned flags) {
+    int bq, bk;
+    if (check_sizes(N, B, H) || tile_config(dtype, head_dim, &bq, &bk) || !mask_form_ok(n_vec, causal)) return -1;
+    const int S = max_kb_per_item < 0 ? auto_split(N, B, H, dtype) : max_kb_per_item;
+    int n_cu = 0;
+    if (device_cus(&n_cu)) return -1;
+    return fused_eligible(N, B, H, dtype, head_dim, bq, bk, S, n_vec, flags, n_cu) ? 1 : 0;
 }
 
 int fm_read_status(const void* workspace, hipStream_t stream, int32_t* status) {

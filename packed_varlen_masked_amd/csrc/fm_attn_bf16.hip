@@ -36,12 +36,16 @@
 //     ends by waiting for the copies of the step before.
 //   * long rows are split over several items; each writes an fp32 partial
 //     (O, m, l) that the merge kernel combines in split order.
+//   * two entry kernels share the item code: the standard one reads the plan
+//     from the workspace and pulls items from a counter; the fused one plans
+//     a small problem in LDS in every workgroup and runs a static share.
 #include <algorithm>
 
 #include "fm_common.hpp"
 #include "fm_internal.h"
 #include "fm_api.h"
 #include "fm_bf16_copies.h"
+#include "fm_lds_plan.h"
 
 namespace fm {
 
@@ -141,8 +145,8 @@ __device__ inline float halves_sum(float x) {
 __device__ inline uint32_t bf16_bits(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); }
 
 struct Item {
-    int b, h, qt, kbb, kbe, sidx, nsp;
-    int s_b, e_b, Tc, r0, r1;
+    int b, h, qt, kbb, kbe, sidx, nsp, cost;
+    int s_b, e_b, Tc, r0, r1, slot0;
     int64_t hoff;
     const int32_t* xb;
 };
@@ -371,19 +375,22 @@ __device__ __attribute__((always_inline)) inline void copy_tile_pair(const AttnA
 }
 constexpr int BATCH_G0 = 6, BATCH_G1 = 5;   // copy instructions per wave per step (groups 0, 1)
 
-// Visit queue: key blocks of the visited tiles m .. m+3 (indices past the
-// item's last visited tile repeat it) and the interval flags of m .. m+3.
+// Visit queue: key blocks of the visited tiles j .. j+3 (indices past the
+// item's last visited tile repeat it) and the interval flags of j .. j+3.
 struct Queue {
     int k0, k1, k2, k3;
-    uint32_t iv;   // bit j: tile m + j needs the interval vectors
+    uint32_t iv;   // bit i: tile j + i needs the interval vectors
 };
 
-__shared__ uint16_t s_vis[VIS_CAP];       // visited key blocks of the item, bit 15 = interval flag
+// Visit lists, entry = key block | interval flag << 15.  The standard kernel
+// builds the list of its current item here from the block extrema; the fused
+// kernel keeps the lists of every q tile of its plan here.
+__shared__ uint16_t s_vis[VIS_CAP];
 __shared__ uint64_t s_wvis[WIN_CAP], s_wiv[WIN_CAP];
 __shared__ int32_t s_wcnt[WIN_CAP];
 
-__device__ __attribute__((always_inline)) inline int vis_entry(int i) {
-    return __builtin_amdgcn_readfirstlane((int)s_vis[i]);
+__device__ __attribute__((always_inline)) inline int vis_entry(const uint16_t* vis, int i) {
+    return __builtin_amdgcn_readfirstlane((int)vis[i]);
 }
 
 // Ring slots of step j: K_j and V_j sit in slot u0 = j mod 3, K_{j+1} and
@@ -407,8 +414,8 @@ struct Slots {
 __device__ __attribute__((always_inline)) inline void kv_step(
     const AttnArgs& a, const Item& I, Queue& Qu, const Wave& Wv, Slots& sl, int j, int T, bool& rec_pending,
     int nxt, int& nrec, int n_items, const bf16x8 (&qf)[8], f32x16 (&sacc)[2], bf16x8 (&pb)[2][2],
-    State& st, const char* Kh, const char* Vh) {
-    const int nk_raw = s_vis[min(j + 4, T - 1)];
+    State& st, const char* Kh, const char* Vh, const uint16_t* vis) {
+    const int nk_raw = vis[min(j + 4, T - 1)];
     if (rec_pending) {   // wave 0: the next item's record, ahead of this step's copies
         const int nx = __builtin_amdgcn_readfirstlane(nxt);
         if (nx < n_items && Wv.lane < ITEM_WORDS) nrec = a.items[(int64_t)nx * ITEM_WORDS + Wv.lane];
@@ -450,26 +457,18 @@ __device__ __attribute__((always_inline)) inline void kv_step(
     phase_barrier();
 }
 
-__global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
-    static_assert(NTH / 64 == NW && BR == 32 * NW && GW == 4, "one wave per 32 query rows, one per SIMD per group");
-    __shared__ __attribute__((aligned(16))) int32_t s_rec[ITEM_WORDS];
-    __shared__ int32_t s_next;
 
-    Wave Wv;
+// ---- per-launch and per-item set-up ----------------------------------
+__device__ __attribute__((always_inline)) inline void wave_setup(const AttnArgs& a, Wave& Wv) {
     Wv.tid = threadIdx.x; Wv.lane = Wv.tid & 63; Wv.w = __builtin_amdgcn_readfirstlane(Wv.tid >> 6);
     Wv.g = Wv.w / GW; Wv.t = Wv.w % GW; Wv.n = Wv.lane & 31; Wv.hh = Wv.lane >> 5;
     Wv.no_skip = (a.flags & FM_FLAG_NO_SKIP) != 0;
     Wv.rsb = (uint32_t)(a.H * HD * 2);
-    const int tid = Wv.tid, lane = Wv.lane, w = Wv.w;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
-        const uint32_t cp = bf16c::copy_lane(Wv.g, Wv.t, i, lane);
+        const uint32_t cp = bf16c::copy_lane(Wv.g, Wv.t, i, Wv.lane);
         Wv.vo[i] = (cp & 0xffu) * Wv.rsb + (cp >> 8);
     }
-    const int n_items = __builtin_amdgcn_readfirstlane(*a.n_items);
-    const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
-    const int64_t rs = (int64_t)a.H * HD;
-
     // Stored vector behind each logical mask vector (LTS, LTE, UTS, UTE) for
     // the accepted (n_vec, causal) pairs; wave t of group 0 stages vector t.
     // Absent ones take their default (LTE: N; UTS, UTE: 0), written into
@@ -481,59 +480,114 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
              : (a.n_vec == 4 ? 3 : (!a.causal && a.n_vec == 2) ? 1 : -1);
     };
     Wv.mv_src = Wv.g == 0 ? vsrc(Wv.t) : -1;
-    for (int i = tid; i < 3 * MVW; i += NTH) {
+    for (int i = Wv.tid; i < 3 * MVW; i += NTH) {
         const int t = (i % MVW) / BC;
         if (vsrc(t) < 0) s_mv[i] = t == 1 ? (int)a.N : 0;
     }
+}
 
-    // Work fetch: every fetch returns the next index; a workgroup stops at its
-    // first index >= n_items.  The launch's last fetch (index
-    // n_items + gridDim.x - 1) resets the counter for the next call.
-    const int last_fetch = n_items + (int)gridDim.x - 1;
-    if (tid == 0) {
-        const int v = atomicAdd(a.sched_counter, 1);
-        if (v == last_fetch) atomicExch(a.sched_counter, 0);
-        s_next = v;
+// Item record (LDS, same for every lane) -> scalar fields.
+__device__ __attribute__((always_inline)) inline Item item_of(const AttnArgs& a, const int32_t* rec) {
+    auto r = [&](int i) { return __builtin_amdgcn_readfirstlane(rec[i]); };
+    Item I;
+    I.b = r(0); I.h = r(1); I.qt = r(2); I.kbb = r(3); I.kbe = r(4);
+    I.sidx = r(5); I.nsp = r(6); I.cost = r(7);
+    I.s_b = r(8); I.e_b = r(9);
+    const int kb_base = r(10);
+    I.slot0 = r(11);
+    I.Tc = ceil_div(I.e_b - I.s_b, BC);
+    I.r0 = I.s_b + I.qt * BR; I.r1 = min(I.r0 + BR, I.e_b);
+    I.xb = a.extrema + (int64_t)kb_base * 8;
+    I.hoff = (int64_t)I.h * HD;
+    return I;
+}
+
+// ---- epilogue -----------------------------------------------------------
+// bf16 row of out and its lse from an unnormalised O (per lane: query row
+// `qrow`, channels 32dt + 8g + 4hh + 0..3 of o[dt][4g .. 4g+3]).
+__device__ __attribute__((always_inline)) inline void write_row(const AttnArgs& a, const Wave& Wv, const Item& I,
+                                                                const f32x16& o, int dt, float inv) {
+    uint16_t* op = (uint16_t*)a.out + (int64_t)Wv.qrow * ((int64_t)a.H * HD) + I.hoff + 4 * Wv.hh;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        u32x2 wv;
+        wv.x = bf16_bits(o[4 * g] * inv) | (bf16_bits(o[4 * g + 1] * inv) << 16);
+        wv.y = bf16_bits(o[4 * g + 2] * inv) | (bf16_bits(o[4 * g + 3] * inv) << 16);
+        *(u32x2*)(op + 32 * dt + 8 * g) = wv;
     }
-    __syncthreads();
-    int it = __builtin_amdgcn_readfirstlane(s_next);
-    if (it < n_items && tid < ITEM_WORDS) s_rec[tid] = a.items[(int64_t)it * ITEM_WORDS + tid];
-    __syncthreads();
-    while (it < n_items) {
-        int nxt = 0, nrec = 0;
-        if (tid == 0) nxt = atomicAdd(a.sched_counter, 1);
-        Item I;
-        // the record is the same for every lane: keep it in scalar registers
-        auto rec = [&](int i) { return __builtin_amdgcn_readfirstlane(s_rec[i]); };
-        I.b = rec(0); I.h = rec(1); I.qt = rec(2); I.kbb = rec(3); I.kbe = rec(4);
-        I.sidx = rec(5); I.nsp = rec(6);
-        I.s_b = rec(8); I.e_b = rec(9);
-        const int kb_base = rec(10), slot0 = rec(11);
-        I.Tc = ceil_div(I.e_b - I.s_b, BC);
-        I.r0 = I.s_b + I.qt * BR; I.r1 = min(I.r0 + BR, I.e_b);
-        I.xb = a.extrema + (int64_t)kb_base * 8;
-        I.hoff = (int64_t)I.h * HD;
-        Wv.qrow = I.r0 + 32 * w + Wv.n;
-        const char* Kh = (const char*)a.k + I.hoff * 2;
-        const char* Vh = (const char*)a.v + I.hoff * 2;
-        const int lo = Wv.no_skip ? 0 : I.kbb, hi = Wv.no_skip ? I.Tc : I.kbe;
+}
+__device__ __attribute__((always_inline)) inline void write_lse(const AttnArgs& a, const Wave& Wv, const Item& I,
+                                                                float m, float l) {
+    if (Wv.hh == 0) a.lse[(int64_t)I.h * a.N + Wv.qrow] = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
+}
 
-        // Q fragments and the first tile (kb_begin is visited by construction
-        // of the work list) go out before the visit scan
-        bf16x8 qf[8];   // Q^T fragments (B operand): lane holds query n, channels 16s+8hh..+7
+// Split rows: every split writes its fp32 partial (O unnormalised, then m
+// and l per row); fm_merge_bf16_kernel combines them in split order after
+// the attention launch.  Partial of split s, head h at
+// ((slot0 + s) * H + h) * PART floats; its O part is lane-major: value e of
+// channel group (dt, g) of lane L of wave w at ((16 w + 4 dt + g) * 64 + L)
+// * 4 + e, so every store instruction of a wave writes 1 KB contiguously.
+__device__ __attribute__((always_inline)) inline int part_index(int w, int dt, int g, int lane) {
+    return ((16 * w + 4 * dt + g) * 64 + lane) * 4;
+}
+
+__device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a, const Wave& Wv, const Item& I,
+                                                               const State& st) {
+    if (I.nsp <= 1) {
         if (Wv.qrow < I.r1) {
-            const uint16_t* qp = Q + (int64_t)Wv.qrow * rs + I.hoff + 8 * Wv.hh;
+            const float l = st.l_run, inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
-        } else {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+            for (int dt = 0; dt < 4; ++dt) write_row(a, Wv, I, st.o[dt], dt, inv);
+            write_lse(a, Wv, I, st.m_run, l);
         }
+        return;
+    }
+    float* po = a.partial + ((int64_t)(I.slot0 + I.sidx) * a.H + I.h) * PART;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            *(float4*)(po + part_index(Wv.w, dt, g, Wv.lane)) =
+                float4{st.o[dt][4 * g], st.o[dt][4 * g + 1], st.o[dt][4 * g + 2], st.o[dt][4 * g + 3]};
+    const int lr = 32 * Wv.w + Wv.n;
+    if (Wv.hh == 0) { po[BR * HD + lr] = st.m_run; po[BR * HD + BR + lr] = st.l_run; }
+}
 
-        if (!Wv.no_skip && lo < hi) copy_tile_pair(a, I, Wv, Kh, Vh, lo);
+// ---- one work item ----------------------------------------------------
+// Q tile in registers, the first K/V tile on its way, the visit list, the KV
+// loop, the epilogue.  STD: the visit list is built here from the block
+// extrema in global memory (FlashMask article §3.2 rules) and the next
+// item's record is prefetched during the loop; otherwise the list is ready
+// in s_vis at `vis_off` (fused path).
+template <bool STD>
+__device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a, Wave& Wv, const Item& I,
+                                                               int vis_off, bool& rec_pending, int nxt, int& nrec,
+                                                               int n_items) {
+    const int tid = Wv.tid, lane = Wv.lane, w = Wv.w;
+    const int64_t rs = (int64_t)a.H * HD;
+    Wv.qrow = I.r0 + 32 * w + Wv.n;
+    const char* Kh = (const char*)a.k + I.hoff * 2;
+    const char* Vh = (const char*)a.v + I.hoff * 2;
+    const int lo = Wv.no_skip ? 0 : I.kbb, hi = Wv.no_skip ? I.Tc : I.kbe;
 
-        // Visit scan (FlashMask article §3.2 rules): windows of 64 key blocks,
-        // one extrema row per lane; wave w takes windows w, w+8, ...
+    // Q fragments and the first tile (kb_begin is visited by construction
+    // of the work list) go out before the visit list is read
+    bf16x8 qf[8];   // Q^T fragments (B operand): lane holds query n, channels 16s+8hh..+7
+    if (Wv.qrow < I.r1) {
+        const uint16_t* qp = (const uint16_t*)a.q + (int64_t)Wv.qrow * rs + I.hoff + 8 * Wv.hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
+    } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+    if (!Wv.no_skip && lo < hi) copy_tile_pair(a, I, Wv, Kh, Vh, lo);
+
+    int T;
+    const uint16_t* vis;
+    if constexpr (STD) {
+        // windows of 64 key blocks, one extrema row per lane; wave w takes
+        // windows w, w+8, ...
         const int nwin = lo < hi ? ceil_div(hi - lo, 64) : 0;
         for (int j = w; j < nwin; j += NW) {
             const int kb = lo + 64 * j + lane;
@@ -552,7 +606,7 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
             if (lane == 0) { s_wvis[j] = vm; s_wiv[j] = im; s_wcnt[j] = __popcll(vm); }
         }
         __syncthreads();
-        int T = 0;
+        T = 0;
         for (int j0 = 0; j0 < nwin; j0 += 64) {   // total visited tiles
             const int j = j0 + lane;
             T += __reduce_add_sync(~0ull, j < nwin ? s_wcnt[j] : 0);
@@ -571,74 +625,79 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
             }
         }
         T = min(T, VIS_CAP);
+        vis = s_vis;
         __syncthreads();
+    } else {
+        T = I.cost;
+        vis = s_vis + vis_off;
+    }
 
-        State st;
-        st.m_run = -INFINITY; st.l_run = 0.f;
+    State st;
+    st.m_run = -INFINITY; st.l_run = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) st.o[dt][e] = 0.f;
+        for (int e = 0; e < 16; ++e) st.o[dt][e] = 0.f;
+    if (T > 0) {
+        Queue Qu;
+        const int e0 = vis_entry(vis, 0), e1 = vis_entry(vis, min(1, T - 1)), e2 = vis_entry(vis, min(2, T - 1)),
+                  e3 = vis_entry(vis, min(3, T - 1));
+        Qu.k0 = e0 & 0x7fff; Qu.k1 = e1 & 0x7fff; Qu.k2 = e2 & 0x7fff; Qu.k3 = e3 & 0x7fff;
+        Qu.iv = (uint32_t)((e0 >> 15) | ((e1 >> 15) << 1) | ((e2 >> 15) << 2) | ((e3 >> 15) << 3));
+        // prologue: K_0 and its mask vectors land before step 0; K_1 (and
+        // masks) and V_0 are waited for at the end of step 0.  V slot 2,
+        // read in step 0 against P = 0, is cleared.
+        if (Wv.no_skip) copy_tile_pair(a, I, Wv, Kh, Vh, Qu.k0);
+        if (Wv.g == 0) {
+            const Tile t1 = tile_at(I, Wv, Qu.k1);
+            copy_tile(Wv, Kh + t1.off, t1.last, kbuf(1));
+            copy_mask(a, Wv, t1, s_mv + MVW);
+            wait_vm<BATCH_G0>();
+        }
+        for (int i = tid; i < SLOT_BYTES / 16; i += NTH) ((u32x4*)vbuf(2))[i] = u32x4{0, 0, 0, 0};
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+        phase_barrier();
+        f32x16 sacc[2];
+        bf16x8 pb[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) pb[t][c] = as_bf16x8(u32x4{0, 0, 0, 0});   // P_{-1}
+        Slots sl{0, 1, 2};
+        for (int j = 0; j < T; ++j)
+            kv_step(a, I, Qu, Wv, sl, j, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
+        // O += V_{T-1} P_{T-1} (tile T-1 sits in slot u2 now)
+        pv_part(vbuf(sl.u2), pb, st, lane);
+    }
+    epilogue(a, Wv, I, st);
+}
+
+// ---- standard kernel: plan in the workspace ---------------------------
+// Persistent grid.  Workgroup g starts with item g; further items come
+// from the work counter: fetch value v means item gridDim.x + v.  Every
+// workgroup that started an item fetches until it gets an index past the
+// list, so the fetches number exactly n_items and the one returning
+// n_items - 1 resets the counter for the next call.
+__global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
+    static_assert(NTH / 64 == NW && BR == 32 * NW && GW == 4, "one wave per 32 query rows, one per SIMD per group");
+    __shared__ __attribute__((aligned(16))) int32_t s_rec[ITEM_WORDS];
+    __shared__ int32_t s_next;
+
+    Wave Wv;
+    wave_setup(a, Wv);
+    const int tid = Wv.tid, lane = Wv.lane, w = Wv.w;
+    const int n_items = __builtin_amdgcn_readfirstlane(*a.n_items);
+    const int G = (int)gridDim.x;
+    const int last_fetch = n_items + G - 1;
+    int it = blockIdx.x;
+    if (it < n_items && tid < ITEM_WORDS) s_rec[tid] = a.items[(int64_t)it * ITEM_WORDS + tid];
+    __syncthreads();
+    while (it < n_items) {
+        int nxt = 0, nrec = 0;
+        if (tid == 0) nxt = G + atomicAdd(a.sched_counter, 1);
+        const Item I = item_of(a, s_rec);
         bool rec_pending = (w == 0);
-        if (T > 0) {
-            Queue Qu;
-            const int e0 = vis_entry(0), e1 = vis_entry(min(1, T - 1)), e2 = vis_entry(min(2, T - 1)),
-                      e3 = vis_entry(min(3, T - 1));
-            Qu.k0 = e0 & 0x7fff; Qu.k1 = e1 & 0x7fff; Qu.k2 = e2 & 0x7fff; Qu.k3 = e3 & 0x7fff;
-            Qu.iv = (uint32_t)((e0 >> 15) | ((e1 >> 15) << 1) | ((e2 >> 15) << 2) | ((e3 >> 15) << 3));
-            // prologue: K_0 and its mask vectors land before step 0; K_1 (and
-            // masks) and V_0 are waited for at the end of step 0.  V slot 2,
-            // read in step 0 against P = 0, is cleared.
-            if (Wv.no_skip) copy_tile_pair(a, I, Wv, Kh, Vh, Qu.k0);
-            if (Wv.g == 0) {
-                const Tile t1 = tile_at(I, Wv, Qu.k1);
-                copy_tile(Wv, Kh + t1.off, t1.last, kbuf(1));
-                copy_mask(a, Wv, t1, s_mv + MVW);
-                wait_vm<BATCH_G0>();
-            }
-            for (int i = tid; i < SLOT_BYTES / 16; i += NTH) ((u32x4*)vbuf(2))[i] = u32x4{0, 0, 0, 0};
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
-            phase_barrier();
-            f32x16 sacc[2];
-            bf16x8 pb[2][2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) pb[t][c] = as_bf16x8(u32x4{0, 0, 0, 0});   // P_{-1}
-            Slots sl{0, 1, 2};
-            for (int j = 0; j < T; ++j)
-                kv_step(a, I, Qu, Wv, sl, j, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh);
-            // O += V_{T-1} P_{T-1} (tile T-1 sits in slot u2 now)
-            pv_part(vbuf(sl.u2), pb, st, lane);
-        }
-
-        // ---- epilogue: normalised bf16 row, or the fp32 partial of a split row ----
-        const int lr = 32 * w + Wv.n, hh = Wv.hh;
-        if (I.nsp > 1) {
-            float* po = a.partial + ((int64_t)(slot0 + I.sidx) * a.H + I.h) * PART;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *(float4*)(po + lr * HD + 32 * dt + 8 * g + 4 * hh) =
-                        float4{st.o[dt][4 * g], st.o[dt][4 * g + 1], st.o[dt][4 * g + 2], st.o[dt][4 * g + 3]};
-            if (hh == 0) { po[BR * HD + lr] = st.m_run; po[BR * HD + BR + lr] = st.l_run; }
-        } else if (Wv.qrow < I.r1) {
-            const float l = st.l_run;
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            uint16_t* op = (uint16_t*)a.out + (int64_t)Wv.qrow * rs + I.hoff + 4 * hh;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x2 wv;
-                    wv.x = bf16_bits(st.o[dt][4 * g] * inv) | (bf16_bits(st.o[dt][4 * g + 1] * inv) << 16);
-                    wv.y = bf16_bits(st.o[dt][4 * g + 2] * inv) | (bf16_bits(st.o[dt][4 * g + 3] * inv) << 16);
-                    *(u32x2*)(op + 32 * dt + 8 * g) = wv;
-                }
-            if (hh == 0) a.lse[(int64_t)I.h * a.N + Wv.qrow] = l > 0.f ? (st.m_run + __log2f(l)) * LN2 : -INFINITY;
-        }
-
+        run_item<true>(a, Wv, I, 0, rec_pending, nxt, nrec, n_items);
         if (rec_pending) {
             nxt = __builtin_amdgcn_readfirstlane(nxt);
             if (nxt < n_items && lane < ITEM_WORDS) nrec = a.items[(int64_t)nxt * ITEM_WORDS + lane];
@@ -659,66 +718,134 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
 }
 
-// N5: merge of split partials in split order (deterministic).  Task =
-// (split row group, 8-row slab); thread = (row of the slab, 4 channels).
-constexpr int MNTH = 256, MROWS = MNTH / 32;
+// ---- fused kernel: plan in LDS, then attention -------------------------
+// Every workgroup builds the whole plan of the call (fm_lds_plan.h) and runs
+// items g, g + gridDim.x, ... of its longest-first order: one launch for the
+// whole forward of a small problem.
+__shared__ __attribute__((aligned(16))) int32_t s_myrec[LP_MAX_MY][ITEM_WORDS];
+static_assert(LP_TMP_BYTES <= 6 * SLOT_BYTES, "planner temporaries fit in the K/V ring");
+static_assert(LP_MAX_TILES <= VIS_CAP, "visit lists of the whole plan fit");
+
+__global__ __launch_bounds__(NTH, 2) void fm_fused_bf16_kernel(AttnArgs a) {
+    Wave Wv;
+    const LdsPlan P = plan_in_lds<BR, BC>(a, s_kv, s_vis, s_myrec);
+    if (P.status != 0) return;
+    wave_setup(a, Wv);
+    bool rec_pending = false;
+    int nrec = 0;
+    for (int k = 0; k < P.n_my; ++k) {
+        const Item I = item_of(a, s_myrec[k]);
+        const int vis_off = __builtin_amdgcn_readfirstlane(s_myrec[k][12]);
+        run_item<false>(a, Wv, I, vis_off, rec_pending, 0, nrec, P.n_items);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // the ring is free for the next item
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// ---- merge of split rows ----------------------------------------------
+// Combines the partials of every split row in split order (deterministic):
+// m = max_s m_s, l = sum_s 2^(m_s - m) l_s, O = sum_s 2^(m_s - m) O_s,
+// out = O / l, lse = (m + log2 l) ln 2.  Task = (split row and head, wave
+// slot w of the partial layout, channel group g); thread = (lane of that
+// wave, dt): every read instruction of a wave is 1 KB contiguous, and a
+// thread issues the reads of up to MSPL splits before using any of them.
+constexpr int MNTH = 256, MSPL = 16;
 
 __global__ __launch_bounds__(MNTH) void fm_merge_bf16_kernel(AttnArgs a) {
     const int n_items = *a.n_items;
-    const int tid = threadIdx.x, lr0 = tid >> 5, dq = (tid & 31) * 4;
-    const int n_tasks = n_items * (BR / MROWS);
-    for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
-        const int it = task / (BR / MROWS), slab = task % (BR / MROWS);
+    const int lane = threadIdx.x & 63, dt = threadIdx.x >> 6, n = lane & 31, hh = lane >> 5;
+    const int64_t n_tasks = (int64_t)n_items * NW * 4;
+    for (int64_t task = blockIdx.x; task < n_tasks; task += gridDim.x) {
+        const int it = (int)(task / (NW * 4)), w = (int)((task / 4) % NW), g = (int)(task % 4);
         const int32_t* rec = a.items + (int64_t)it * ITEM_WORDS;
         const int nsp = rec[6];
         if (rec[5] != 0 || nsp <= 1) continue;
         const int h = rec[1], qt = rec[2], s_b = rec[8], e_b = rec[9], slot0 = rec[11];
-        const int lr = slab * MROWS + lr0;
+        const int lr = 32 * w + n;
         const int64_t qrow = (int64_t)s_b + qt * BR + lr;
         if (qrow >= e_b) continue;
         const float* p0 = a.partial + ((int64_t)slot0 * a.H + h) * PART;
         const int64_t step = (int64_t)a.H * PART;
-        // all m first (independent loads), then one pass over the splits
+        const int oi = part_index(w, dt, g, lane);
+        // pass 1: row max over splits
         float m_all = -INFINITY;
-#pragma unroll 4
-        for (int s = 0; s < nsp; ++s) m_all = fmaxf(m_all, p0[s * step + BR * HD + lr]);
+        for (int s0 = 0; s0 < nsp; s0 += MSPL) {
+            float mv[MSPL];
+#pragma unroll
+            for (int u = 0; u < MSPL; ++u) mv[u] = s0 + u < nsp ? p0[(s0 + u) * step + BR * HD + lr] : -INFINITY;
+#pragma unroll
+            for (int u = 0; u < MSPL; ++u) m_all = fmaxf(m_all, mv[u]);
+        }
         const float m_use = (m_all == -INFINITY) ? 0.f : m_all;
+        // pass 2: weighted sums in split order
         float l_all = 0.f;
         float4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int s = 0; s < nsp; ++s) {
-            const float* ps = p0 + s * step;
-            const float ms = ps[BR * HD + lr], ls = ps[BR * HD + BR + lr];
-            const float4 v = *(const float4*)(ps + lr * HD + dq);
-            const float wgt = __builtin_amdgcn_exp2f(ms - m_use);
-            l_all += wgt * ls;
-            acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+        for (int s0 = 0; s0 < nsp; s0 += MSPL) {
+            float mv[MSPL], lv[MSPL];
+            float4 ov[MSPL];
+#pragma unroll
+            for (int u = 0; u < MSPL; ++u)
+                if (s0 + u < nsp) {
+                    const float* ps = p0 + (s0 + u) * step;
+                    mv[u] = ps[BR * HD + lr];
+                    lv[u] = ps[BR * HD + BR + lr];
+                    ov[u] = *(const float4*)(ps + oi);
+                }
+#pragma unroll
+            for (int u = 0; u < MSPL; ++u)
+                if (s0 + u < nsp) {
+                    const float wgt = __builtin_amdgcn_exp2f(mv[u] - m_use);
+                    l_all = __builtin_fmaf(wgt, lv[u], l_all);
+                    acc.x = __builtin_fmaf(wgt, ov[u].x, acc.x);
+                    acc.y = __builtin_fmaf(wgt, ov[u].y, acc.y);
+                    acc.z = __builtin_fmaf(wgt, ov[u].z, acc.z);
+                    acc.w = __builtin_fmaf(wgt, ov[u].w, acc.w);
+                }
         }
         const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
-        uint16_t* op = (uint16_t*)a.out + qrow * ((int64_t)a.H * HD) + (int64_t)h * HD + dq;
+        uint16_t* op = (uint16_t*)a.out + qrow * ((int64_t)a.H * HD) + (int64_t)h * HD + 32 * dt + 8 * g + 4 * hh;
         u32x2 wv;
         wv.x = bf16_bits(acc.x * inv) | (bf16_bits(acc.y * inv) << 16);
         wv.y = bf16_bits(acc.z * inv) | (bf16_bits(acc.w * inv) << 16);
         *(u32x2*)op = wv;
-        if (dq == 0) a.lse[(int64_t)h * a.N + qrow] = l_all > 0.f ? (m_all + __log2f(l_all)) * LN2 : -INFINITY;
+        if (dt == 0 && g == 0 && hh == 0)
+            a.lse[(int64_t)h * a.N + qrow] = l_all > 0.f ? (m_all + __log2f(l_all)) * LN2 : -INFINITY;
     }
 }
 
+namespace {
+int occupancy(const void* fn) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, fn, NTH, 0) != hipSuccess || o < 1) o = 1;
+    return o;
+}
+
+hipError_t launch_merge(const AttnArgs& a, int n_cu, hipStream_t s) {
+    if (a.S <= 0) return hipSuccess;
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.items_cap * NW * 4, (int64_t)n_cu * 16));
+    hipLaunchKernelGGL(fm_merge_bf16_kernel, dim3((unsigned)grid), dim3(MNTH), 0, s, a);
+    return hipGetLastError();
+}
+}  // namespace
+
+int fused_grid(int n_cu) {
+    static const int occ = occupancy((const void*)fm_fused_bf16_kernel);
+    return std::max(1, n_cu * occ);
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, int n_cu, hipStream_t s) {
-    static int occ = 0;
-    if (occ == 0) {
-        int o = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, fm_attn_bf16_kernel, NTH, 0) != hipSuccess || o < 1)
-            o = 1;
-        occ = o;
-    }
+    static const int occ = occupancy((const void*)fm_attn_bf16_kernel);
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.items_cap, (int64_t)n_cu * occ));
     hipLaunchKernelGGL(fm_attn_bf16_kernel, dim3((unsigned)grid), dim3(NTH), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.S <= 0) return e;
-    const int64_t mgrid = std::max<int64_t>(1, std::min<int64_t>(a.items_cap * (BR / MROWS), (int64_t)n_cu * 8));
-    hipLaunchKernelGGL(fm_merge_bf16_kernel, dim3((unsigned)mgrid), dim3(MNTH), 0, s, a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_merge(a, n_cu, s);
+}
+
+hipError_t launch_fused_bf16(const AttnArgs& a, int n_cu, hipStream_t s) {
+    hipLaunchKernelGGL(fm_fused_bf16_kernel, dim3((unsigned)fused_grid(n_cu)), dim3(NTH), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_merge(a, n_cu, s);
 }
 
 }  // namespace fm

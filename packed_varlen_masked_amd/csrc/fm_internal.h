@@ -68,11 +68,16 @@ struct AttnArgs {
     int32_t* sched_counter;
     const int32_t* sl_off;     // per-sequence first slot (split partial index)
     float* partial;            // split partials (S > 0)
-    int32_t* merge_counter;    // split arrival counters (S > 0)
+    int32_t* merge_counter;    // split arrival counters (S > 0), zero between calls
     unsigned flags;
+    // fused path only: where the in-kernel planner writes the plan
+    int32_t* w_hdr; int32_t* w_kb_off; int32_t* w_ext; int32_t* w_items; int64_t* w_counts;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int n_cu, hipStream_t s);
+// One launch that plans in LDS and attends (small bf16 problems).
+hipError_t launch_fused_bf16(const AttnArgs& a, int n_cu, hipStream_t s);
+int fused_grid(int n_cu);
 hipError_t launch_attn_f32(const AttnArgs& a, int n_cu, hipStream_t s);
 
 }  // namespace fm

@@ -1,0 +1,179 @@
+"""GPU tests of the fused one-launch path (plan built in LDS by every
+workgroup, items run from a static share, split rows merged by the last
+split to arrive).
+
+- the plan the fused launch writes into the workspace equals the oracle's
+  (bit-exact extrema, kb offsets, class counts, work items);
+- out / lse are within the parity bars of the fp64 oracle;
+- the fused path and the plan-in-workspace path give identical bits (same
+  plan, same item code, split merge independent of arrival order);
+- a workspace is reusable: the split arrival counters are back at zero
+  after every call, across paths.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-2
+LSE_TOL = 1e-3
+BR, BC = 256, 64
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def pv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import packed_varlen_masked_amd as pv
+    return pv
+
+
+def dev_inputs(w):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+    cu = torch.from_numpy(w.cu_seqlens.astype(np.int32)).cuda()
+    sv = torch.from_numpy(np.ascontiguousarray(w.startend.astype(np.int32))).cuda()
+    return t(w.q), t(w.k), t(w.v), cu, sv
+
+
+def fused_ws(pv, w, S):
+    lay = pv.workspace_layout(w.N, w.B, w.H, w.D, BR, BC, S, False)
+    return lay, torch.zeros(lay.bytes, dtype=torch.uint8, device="cuda")
+
+
+def run_fused(pv, w, S, ws=None):
+    q, k, v, cu, sv = dev_inputs(w)
+    assert pv.fused_path(w.N, w.B, w.H, w.D, torch.bfloat16, w.n_vec, w.causal, S)
+    if ws is None:
+        _, ws = fused_ws(pv, w, S)
+    out, lse = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), max_kb_per_item=S,
+                           workspace=ws)
+    torch.cuda.synchronize()
+    return out, lse, ws
+
+
+def run_planned(pv, w, S):
+    q, k, v, cu, sv = dev_inputs(w)
+    plan = pv.build_plan(cu, sv, w.n_vec, w.causal, w.N, w.H, w.D, torch.bfloat16, max_kb_per_item=S)
+    out, lse = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), plan=plan)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def compare(w, out, lse, tag):
+    oo, ol = O.attention(w.q, w.k, w.v, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(l), np.isneginf(ol)), "lse -inf pattern differs"
+    fin = np.isfinite(ol)
+    e_out = float(np.max(np.abs(o - oo))) if o.size else 0.0
+    e_lse = float(np.max(np.abs(l[fin] - ol[fin]), initial=0.0))
+    say("  %s max|dout|=%.3e max|dlse|=%.3e" % (tag, e_out, e_lse))
+    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+
+
+def check_written_plan(pv, w, S, ws, lay):
+    hdr = ws[:256].view(torch.int32).cpu().numpy()
+    counts = ws[64:88].view(torch.int64).cpu().tolist()
+    kb_off, ext = O.extrema(w.cu_seqlens, w.startend, w.n_vec, w.causal, BC)
+    cls = O.classify(w.cu_seqlens, kb_off, ext, w.causal, BR, BC)
+    oitems = O.worklist(cls, w.H, S)
+    assert hdr[0] == 0 and hdr[1] == len(ext) and hdr[2] == len(oitems) and hdr[3] == 0
+    assert counts == O.class_counts(cls).tolist()
+    g = lambda off, n: ws[off:off + 4 * n].view(torch.int32).cpu().numpy()
+    assert np.array_equal(g(lay.off_kb_off, w.B + 1), kb_off)
+    assert np.array_equal(g(lay.off_extrema, 8 * len(ext)).reshape(-1, 8), ext.reshape(-1, 8))
+    items = g(lay.off_items, 16 * len(oitems)).reshape(-1, 16)
+    assert np.array_equal(items[:, :8], oitems)
+    cu = w.cu_seqlens.astype(np.int64)
+    b = items[:, 0]
+    assert np.array_equal(items[:, 8], cu[b]) and np.array_equal(items[:, 9], cu[b + 1])
+    assert np.array_equal(items[:, 10], kb_off[b]) and np.all(items[:, 12:] == 0)
+    return items
+
+
+def test_fused_path_selection(pv):
+    w = W.make_config(2, with_qkv=False)
+    bf = torch.bfloat16
+    assert pv.fused_path(w.N, w.B, w.H, 128, bf, w.n_vec, w.causal)
+    assert not pv.fused_path(w.N, w.B, w.H, 128, bf, w.n_vec, w.causal, flags=pv.FM_FLAG_NO_SKIP)
+    assert not pv.fused_path(w.N, w.B, w.H, 128, bf, w.n_vec, w.causal, flags=pv.FM_FLAG_PLAN_READY)
+    assert not pv.fused_path(w.N, w.B, w.H, 32, torch.float32, w.n_vec, w.causal)
+    assert not pv.fused_path(16384, 20, 32, 128, bf, 1, True)          # SFT packing: too big
+    assert not pv.fused_path(4096, 300, 1, 128, bf, 1, True)           # too many sequences
+
+
+@pytest.mark.parametrize("S", [-1, 0, 3, 2, 1])
+def test_fused_cfg2(pv, S):
+    w = W.make_config(2)
+    S_eff = pv.auto_split(w.N, w.B, w.H, torch.bfloat16, 128) if S < 0 else S
+    say("fused cfg2 S", S, "->", S_eff)
+    if not pv.fused_path(w.N, w.B, w.H, w.D, torch.bfloat16, w.n_vec, w.causal, S_eff):
+        assert S_eff == 1, "the headline workload must take the fused path"
+        pytest.skip("split bound beyond the fused path")
+    lay, ws = fused_ws(pv, w, S_eff)
+    out, lse, _ = run_fused(pv, w, S_eff, ws)
+    check_written_plan(pv, w, S_eff, ws, lay)
+    compare(w, out, lse, "fused cfg2 S=%d" % S_eff)
+    o2, l2 = run_planned(pv, w, S_eff)
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_fused_random(pv, seed):
+    rng = np.random.default_rng(1000 + seed)
+    w = W.random_case(700 + seed, N_max=1500, H=int(rng.integers(1, 4)), D=128, dtype=W.BF16)
+    S = int(rng.choice([0, 1, 2, 6]))
+    if not pv.fused_path(w.N, w.B, w.H, w.D, torch.bfloat16, w.n_vec, w.causal, S):
+        pytest.skip("sizes outside the fused path")
+    say("fused random", w.name, "N=%d B=%d H=%d causal=%d n_vec=%d S=%d" % (w.N, w.B, w.H, w.causal, w.n_vec, S))
+    lay, ws = fused_ws(pv, w, S)
+    out, lse, _ = run_fused(pv, w, S, ws)
+    check_written_plan(pv, w, S, ws, lay)
+    compare(w, out, lse, "fused random")
+    o2, l2 = run_planned(pv, w, S)
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+@pytest.mark.parametrize("k,N,H", [(3, 6000, 2), (4, 4000, 2), (5, 4000, 1)])
+def test_fused_reduced_configs(pv, k, N, H):
+    w = W.make_config(k, N=N, H=H)
+    for S in (0, 3):
+        if not pv.fused_path(w.N, w.B, w.H, w.D, torch.bfloat16, w.n_vec, w.causal, S):
+            continue
+        say("fused reduced cfg", k, w.N, w.H, w.B, "S", S)
+        lay, ws = fused_ws(pv, w, S)
+        out, lse, _ = run_fused(pv, w, S, ws)
+        check_written_plan(pv, w, S, ws, lay)
+        compare(w, out, lse, "fused cfg%d S=%d" % (k, S))
+
+
+def test_workspace_reuse_across_paths(pv):
+    """Arrival counters return to zero: the same workspace serves fused,
+    planned and fused calls again with identical results."""
+    w = W.make_config(2)
+    S = 2
+    lay, ws = fused_ws(pv, w, S)
+    o1, l1, _ = run_fused(pv, w, S, ws)
+    merge = lambda: ws[lay.off_merge:lay.off_merge + 4 * lay.slot_cap * w.H].view(torch.int32)
+    assert torch.count_nonzero(merge()).item() == 0
+    q, k, v, cu, sv = dev_inputs(w)
+    pv.build_plan_into(pv.Plan(ws, lay, w.N, w.B, w.H, w.D, torch.bfloat16, w.causal, w.n_vec, S), cu, sv)
+    o2, l2 = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), max_kb_per_item=S,
+                         workspace=ws, flags=pv.FM_FLAG_PLAN_READY)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(merge()).item() == 0
+    o3, l3, _ = run_fused(pv, w, S, ws)
+    for o, l in ((o2, l2), (o3, l3)):
+        assert torch.equal(o1, o) and torch.equal(l1, l)
+    assert torch.count_nonzero(merge()).item() == 0
