@@ -17,6 +17,7 @@ on a bounded sample of the same workload as the CPU baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -47,6 +48,35 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+def source_hash():
+    """sha256 over the library sources: stored counter figures apply only to
+    the kernels they were taken from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "packed_varlen_masked_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(key):
+    """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs summarised in profiles/traffic.json (scaled by the copy
+    calibration recorded there), or None when absent or taken from other
+    sources."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get("entries", {}).get(key)
+    if not e or e.get("src_sha256") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
 
 
 def cpu_baseline(w, flops, budget_s):
@@ -166,6 +196,11 @@ def main():
     achieved = flops / (attn_avg * 1e-3) / 1e12
 
     hdr = (plan if not fused else pv.Plan(ws, plan.layout, w.N, w.B, w.H, w.D, dt, w.causal, w.n_vec, S)).header()
+    path = "fused" if fused else "planned"
+    kernel = ("fm_fused_bf16_kernel" if fused else "fm_attn_bf16_kernel") + (" + fm_merge_bf16_kernel" if S > 0 else "")
+    traffic = stored_traffic("%s:%s:S%d" % (w.name, path, S))
+    esz = 2 if dt == torch.bfloat16 else 4
+    algo_bytes = 4 * w.N * w.H * w.D * esz + 4 * w.N * w.H   # q, k, v read once, out and lse written
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
@@ -179,10 +214,11 @@ def main():
                    "effective_gflop": round(flops / 1e9, 4)},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "timing": {"host_enqueue_ms_per_step": round(host_ms, 4), "host_ran_ahead": host_ahead},
-        "path": "fused" if fused else "planned",
-        "roofline": {"bound": "mfma", "kernel": "fm_fused_bf16_kernel" if fused else "fm_attn_bf16_kernel",
+        "path": path,
+        "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_bytes": int(algo_bytes),
                      "avg_launch_ms": round(attn_avg, 6),
                      "p10_p50_p90_ms": [round(float(x), 6) for x in np.percentile(attn_ms, [10, 50, 90])]},
     }

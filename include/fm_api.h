@@ -131,12 +131,8 @@ int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim);
  *   tile_class: uint8 [map_cap]     per-tile classes (only if requested)
  *   scratch:    worklist scratch (fm_worklist_scratch_size bytes)
  *   partial:    fp32 split partials [slot_cap * H] x (Br*D + 2*Br) (S > 0)
- *   merge:      int32 [slot_cap * H] split arrival counters (S > 0); zeroed
- *               when the plan is built by the planning kernels and left at
- *               zero by every call.  A fresh workspace handed to
- *               fm_attn_fwd without FM_FLAG_PLAN_READY must therefore be
- *               zero-filled once (the fused path, below, builds its plan
- *               inside the attention launch and does not clear them).
+ *   merge:      int32 [slot_cap * H] reserved (S > 0); the planning
+ *               kernels zero it, no kernel of this version reads it.
  */
 typedef struct fm_ws_layout {
     size_t  bytes;
@@ -255,14 +251,14 @@ int fm_build_plan(const int32_t* cu_seqlens, int B, int64_t N, int H, int head_d
  * max_kb_per_item: < 0 auto (fm_auto_split), 0 = never split, else S.
  *   bf16 only; fp32 requires 0 or < 0 (treated as 0).
  * workspace: device, >= fm_workspace_layout(...).bytes for these sizes
- *   (class map not needed), zero-filled before its first use.  flags:
- *   FM_FLAG_*.
+ *   (class map not needed).  flags: FM_FLAG_*.
  * Without FM_FLAG_PLAN_READY the plan is built first.  Small bf16 problems
- * (see fm_fused_path) take the fused path: ONE launch in which every
- * workgroup rebuilds the plan in LDS and runs its share of the items; the
- * plan is still written to the workspace, identical to fm_build_plan's.
- * Split rows (S > 0) are combined by the last split to finish, in split
- * order.  Results are deterministic: the same inputs give the same bits.
+ * (see fm_fused_path) take the fused path: ONE attention launch in which
+ * every workgroup rebuilds the plan in LDS and runs its share of the
+ * items; the plan is still written to the workspace, identical to
+ * fm_build_plan's.  Split rows (S > 0) write fp32 partials that a second
+ * launch combines in split order.  Results are deterministic: the same
+ * inputs give the same bits, on either path.
  */
 int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype,
                 int64_t N, int H, int D, const int32_t* cu_seqlens, int B,
