@@ -122,8 +122,8 @@ int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim);
  * Workspace layout.  All offsets are bytes from the workspace base and are
  * 256-byte aligned.  `*_cap` are host-side upper bounds computed from
  * (N, B, H, Br, Bc, S) only.
- *   hdr:        int32 status, n_kblocks, n_items, sched_counter, n_slots
- *               at byte 0..19; int64 class_counts[3] at byte 64.
+ *   hdr:        int32 status, n_kblocks, n_items, sched_counter, n_slots,
+ *               n_merge at byte 0..23; int64 class_counts[3] at byte 64.
  *   kb_off:     int32 [B+1]         first key block of each sequence
  *   extrema:    int32 [kb_cap][8]   per key block: min/max of LTS, LTE,
  *                                   UTS, UTE (in that order)
@@ -131,8 +131,10 @@ int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim);
  *   tile_class: uint8 [map_cap]     per-tile classes (only if requested)
  *   scratch:    worklist scratch (fm_worklist_scratch_size bytes)
  *   partial:    fp32 split partials [slot_cap * H] x (Br*D + 2*Br) (S > 0)
- *   merge:      int32 [slot_cap * H] reserved (S > 0); the planning
- *               kernels zero it, no kernel of this version reads it.
+ *   merge:      int32 [slot_cap * H / 2 + 1][8] (S > 0): the split rows,
+ *               one entry per (split row, head): slot of split 0, head,
+ *               first row, end row, number of splits, 3 zero words;
+ *               n_merge entries, written by the planners for the merge.
  */
 typedef struct fm_ws_layout {
     size_t  bytes;

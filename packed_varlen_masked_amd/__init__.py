@@ -228,7 +228,7 @@ class Plan:
     def header(self):
         h = self.workspace[:256].view(torch.int32).cpu()
         return {"status": int(h[0]), "n_kblocks": int(h[1]), "n_items": int(h[2]),
-                "sched_counter": int(h[3]), "n_slots": int(h[4]),
+                "sched_counter": int(h[3]), "n_slots": int(h[4]), "n_merge": int(h[5]),
                 "class_counts": self.workspace[64:88].view(torch.int64).cpu().tolist()}
 
     def _view(self, off, n, dt, shape):

@@ -165,7 +165,9 @@ int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_
     L.off_scratch = off; L.scratch_bytes = sl.bytes; off = align256(off + sl.bytes);
     L.partial_bytes = S > 0 ? (size_t)c.slot * H * ((size_t)Br * D + 2 * (size_t)Br) * 4 : 0;
     L.off_partial = S > 0 ? off : 0; off = align256(off + L.partial_bytes);
-    L.off_merge = S > 0 ? off : 0; if (S > 0) off = align256(off + (size_t)c.slot * H * 4);
+    // split-row list: a split row has >= 2 slots, so slot_cap * H / 2 + 1 entries suffice
+    L.off_merge = S > 0 ? off : 0;
+    if (S > 0) off = align256(off + ((size_t)c.slot * H / 2 + 1) * fm::MERGE_WORDS * 4);
     if ((int64_t)off > kMaxBytes) return fail(FM_E_INVAL, "workspace would exceed 64 TiB");
     L.bytes = off;
     L.kb_cap = c.kb; L.item_cap = c.item; L.map_cap = want_map ? c.map : 0; L.slot_cap = c.slot;
@@ -225,7 +227,8 @@ int worklist_impl(const int32_t* cu, int B, int64_t N, int H, int Br, int Bc, co
     p.kb_off = kb_off; p.extrema = ext; p.status = status; p.status_rw = status_rw;
     p.items = items; p.items_cap = items_cap; p.n_items = n_items; p.class_counts = counts;
     p.sched_counter = sched; p.n_slots = n_slots; p.tile_class = map; p.tile_class_cap = map ? map_cap : 0;
-    p.scratch = (char*)scratch; p.sl = sl; p.cost_cap = c.cost; p.merge_counter = S > 0 ? merge : nullptr;
+    p.scratch = (char*)scratch; p.sl = sl; p.cost_cap = c.cost; p.merge_list = S > 0 ? merge : nullptr;
+    p.n_merge = nullptr;
     return hip_check(fm::launch_worklist(p, s), "worklist launch");
 }
 
@@ -261,7 +264,8 @@ int build_plan_impl(const Ws& w, const int32_t* cu, int B, int64_t N, int H, con
     p.tile_class = L.off_tile_class ? (uint8_t*)(w.base + L.off_tile_class) : nullptr;
     p.tile_class_cap = L.off_tile_class ? L.map_cap : 0;
     p.scratch = w.base + L.off_scratch; p.sl = scratch_layout(B, c); p.cost_cap = c.cost;
-    p.merge_counter = L.off_merge ? (int32_t*)(w.base + L.off_merge) : nullptr;
+    p.merge_list = L.off_merge ? (int32_t*)(w.base + L.off_merge) : nullptr;
+    p.n_merge = L.off_merge ? hdr + fm::HDR_NMERGE : nullptr;
     return hip_check(fm::launch_plan(sv, n_vec, (int32_t*)(w.base + L.off_extrema), L.kb_cap, hdr + fm::HDR_NKB,
                                      (int32_t*)(w.base + L.off_kb_off), p, s),
                      "plan launch");
@@ -442,13 +446,16 @@ int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t 
     }();
     a.sl_off = (const int32_t*)(w.base + w.L.off_scratch + sl.off_sl_off);
     a.partial = S > 0 ? (float*)(w.base + w.L.off_partial) : nullptr;
-    a.merge_counter = S > 0 ? (int32_t*)(w.base + w.L.off_merge) : nullptr;
+    a.merge_list = S > 0 ? (const int32_t*)(w.base + w.L.off_merge) : nullptr;
+    a.n_merge = w.hdr() + fm::HDR_NMERGE;
+    a.merge_cap = S > 0 ? (int64_t)(w.L.slot_cap * H / 2 + 1) : 0;
     a.flags = flags;
     a.w_hdr = w.hdr();
     a.w_kb_off = (int32_t*)(w.base + w.L.off_kb_off);
     a.w_ext = (int32_t*)(w.base + w.L.off_extrema);
     a.w_items = (int32_t*)(w.base + w.L.off_items);
     a.w_counts = w.counts();
+    a.w_merge = S > 0 ? (int32_t*)(w.base + w.L.off_merge) : nullptr;
     const hipError_t e = fused ? fm::launch_fused_bf16(a, n_cu, stream)
                        : dtype == FM_BF16 ? fm::launch_attn_bf16(a, n_cu, stream)
                                           : fm::launch_attn_f32(a, n_cu, stream);

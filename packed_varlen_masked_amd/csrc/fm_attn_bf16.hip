@@ -88,7 +88,7 @@ static_assert(KCH == bf16c::KCH && VCH == bf16c::VCH && BC == bf16c::BC && NW ==
 // is explicit (see the step below).
 constexpr int SLOT_BYTES = bf16c::SLOT_BLK * 1024;
 __shared__ __attribute__((aligned(1024))) char s_kv[6 * SLOT_BYTES];
-__shared__ __attribute__((aligned(16))) int32_t s_mv[3 * MVW];
+__shared__ __attribute__((aligned(16))) int32_t s_mv[4 * MVW];   // mask vectors of tile t in slot t mod 4
 __shared__ __attribute__((aligned(16))) int32_t s_sink[GW * BC];   // mask rows of absent vectors (never read)
 __device__ __attribute__((always_inline)) inline char* kbuf(int i) { return s_kv + i * SLOT_BYTES; }
 __device__ __attribute__((always_inline)) inline char* vbuf(int i) { return s_kv + (3 + i) * SLOT_BYTES; }
@@ -378,8 +378,8 @@ constexpr int BATCH_G0 = 6, BATCH_G1 = 5;   // copy instructions per wave per st
 // Visit queue: key blocks of the visited tiles j .. j+3 (indices past the
 // item's last visited tile repeat it) and the interval flags of j .. j+3.
 struct Queue {
-    int k0, k1, k2, k3;
-    uint32_t iv;   // bit i: tile j + i needs the interval vectors
+    int kp, k0, k1, k2, k3;   // kp: tile j - 1
+    uint32_t iv;   // bit i (i < 4): tile j + i needs the interval vectors; bit 4: tile j - 1
 };
 
 // Visit lists, entry = key block | interval flag << 15.  The standard kernel
@@ -400,17 +400,36 @@ struct Slots {
     __device__ void next() { const int t = u0; u0 = u1; u1 = u2; u2 = t; }
 };
 
-// Step j of the KV loop, j = 0..T-1 (all waves in step).  Every wave is
-// software-pipelined over two tiles:
-//   S_j = K_j Q^T on MFMA; then the masks and row max of tile j;
-//   O += V_{j-1} P_{j-1} on MFMA, beside the exponentials of tile j (P_j);
-//   then the lazy rescale of O and l for tile j.
+// Softmax of one tile (all vector work): element masks where the tile
+// needs them, the row max, the lazy max update, P in bf16 and its row sum.
+// Returns alpha, the factor by which O and l (relative to the old max) must
+// be rescaled; the caller applies it and adds the row sum to l.
+__device__ __attribute__((always_inline)) inline float softmax_tile(const AttnArgs& a, const Item& I, const Wave& Wv,
+                                                                    f32x16 (&sacc)[2], int kb, bool iv,
+                                                                    const int32_t* cmv, State& st, bf16x8 (&pb)[2][2],
+                                                                    float& rsum) {
+    const int c0 = I.s_b + kb * BC, c1 = min(c0 + BC, I.e_b);
+    const bool causal = a.causal && (c1 > I.r0 + 1);
+    const float mx = mask_max(sacc, causal, (c1 - c0) < BC, iv, c0, c1, Wv.qrow, cmv, a.scale_log2, Wv.hh);
+    return exp_tile(sacc, mx, st, pb, a.scale_log2, rsum);
+}
+
+// Step j of the KV loop, j = 0..T-1 (all waves in step).  Both groups
+// compute S_j = K_j Q^T and O += V_{j-1} P_{j-1} on MFMA and the softmax
+// of one tile in the step, in opposite orders so that the two waves of a
+// SIMD (one per group) keep its matrix unit and its vector unit busy at the
+// same time:
+//   group 0: S_j and PV_{j-1} (MFMA), then the softmax of tile j (P_j);
+//   group 1: the softmax of tile j-1 (S_{j-1}, kept from the step before),
+//            then PV_{j-1} and S_j.
+// O is rescaled by the softmax's alpha before the next PV adds to it.
 // P_{-1} is zero and the V slot of step 0 holds zeros, so step 0 adds
-// exactly nothing to O; the product of the last tile follows the loop.  At
-// the start of a step group 0 copies K_{j+2} (and its mask vectors) into K
-// slot u2 and group 1 copies V_{j+1} into V slot u1, both last read in step
-// j-1; a step ends by waiting for the previous step's copies, then a
-// barrier.
+// exactly nothing to O; the last tile's product (and, for group 1, its
+// softmax) follows the loop.  At the start of a step group 0 copies K_{j+2}
+// into K slot u2 and its mask vectors into mask slot (j+2) mod 4, group 1
+// copies V_{j+1} into V slot u1, all last read in step j-1; a step ends by
+// waiting for the previous step's copies, then a barrier.
+template <int G>
 __device__ __attribute__((always_inline)) inline void kv_step(
     const AttnArgs& a, const Item& I, Queue& Qu, const Wave& Wv, Slots& sl, int j, int T, bool& rec_pending,
     int nxt, int& nrec, int n_items, const bf16x8 (&qf)[8], f32x16 (&sacc)[2], bf16x8 (&pb)[2][2],
@@ -421,42 +440,47 @@ __device__ __attribute__((always_inline)) inline void kv_step(
         if (nx < n_items && Wv.lane < ITEM_WORDS) nrec = a.items[(int64_t)nx * ITEM_WORDS + Wv.lane];
         rec_pending = false;
     }
-    if (Wv.g == 0) {
+    if constexpr (G == 0) {
         const Tile tl = tile_at(I, Wv, Qu.k2);
         copy_tile(Wv, Kh + tl.off, tl.last, kbuf(sl.u2));
-        copy_mask(a, Wv, tl, s_mv + sl.u2 * MVW);
+        copy_mask(a, Wv, tl, s_mv + ((j + 2) & 3) * MVW);
+        s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh);
+        pv_part(vbuf(sl.u2), pb, st, Wv.lane);
+        float rsum;
+        const float alpha = softmax_tile(a, I, Wv, sacc, Qu.k0, (Qu.iv & 1u) != 0, s_mv + (j & 3) * MVW, st, pb, rsum);
+        if (alpha != 1.f) {   // rare: the running max moved
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
+        }
+        st.l_run = st.l_run * alpha + rsum;
     } else {
         const Tile tl = tile_at(I, Wv, Qu.k1);
         copy_tile(Wv, Vh + tl.off, tl.last, vbuf(sl.u1));
+        if (j > 0) {
+            float rsum;
+            const float alpha =
+                softmax_tile(a, I, Wv, sacc, Qu.kp, (Qu.iv & 16u) != 0, s_mv + ((j - 1) & 3) * MVW, st, pb, rsum);
+            if (alpha != 1.f) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
+            }
+            st.l_run = st.l_run * alpha + rsum;
+        }
+        pv_part(vbuf(sl.u2), pb, st, Wv.lane);
+        s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh);
     }
-    s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh);
-    const int c0 = I.s_b + Qu.k0 * BC, c1 = min(c0 + BC, I.e_b);
-    const bool causal = a.causal && (c1 > I.r0 + 1);
-    const float mx = mask_max(sacc, causal, (c1 - c0) < BC, (Qu.iv & 1u) != 0, c0, c1, Wv.qrow,
-                              s_mv + sl.u0 * MVW, a.scale_log2, Wv.hh);
-    bf16x8 pn[2][2];
-    float rsum;
-    const float alpha = exp_tile(sacc, mx, st, pn, a.scale_log2, rsum);
-    pv_part(vbuf(sl.u2), pb, st, Wv.lane);
-    if (alpha != 1.f) {   // rare: the running max moved
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
-    }
-    st.l_run = st.l_run * alpha + rsum;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) pb[t][c] = pn[t][c];
     const int nk = __builtin_amdgcn_readfirstlane(nk_raw);
+    Qu.kp = Qu.k0;
     Qu.k0 = Qu.k1; Qu.k1 = Qu.k2; Qu.k2 = Qu.k3; Qu.k3 = nk & 0x7fff;
-    Qu.iv = (Qu.iv >> 1) | ((uint32_t)(nk >> 15) << 3);
+    Qu.iv = ((Qu.iv >> 1) & 7u) | ((uint32_t)(nk >> 15) << 3) | ((Qu.iv & 1u) << 4);
     sl.next();
-    if (Wv.g == 0) wait_vm<BATCH_G0>(); else wait_vm<BATCH_G1>();
+    if constexpr (G == 0) wait_vm<BATCH_G0>(); else wait_vm<BATCH_G1>();
     phase_barrier();
 }
-
 
 // ---- per-launch and per-item set-up ----------------------------------
 __device__ __attribute__((always_inline)) inline void wave_setup(const AttnArgs& a, Wave& Wv) {
@@ -480,7 +504,7 @@ __device__ __attribute__((always_inline)) inline void wave_setup(const AttnArgs&
              : (a.n_vec == 4 ? 3 : (!a.causal && a.n_vec == 2) ? 1 : -1);
     };
     Wv.mv_src = Wv.g == 0 ? vsrc(Wv.t) : -1;
-    for (int i = Wv.tid; i < 3 * MVW; i += NTH) {
+    for (int i = Wv.tid; i < 4 * MVW; i += NTH) {
         const int t = (i % MVW) / BC;
         if (vsrc(t) < 0) s_mv[i] = t == 1 ? (int)a.N : 0;
     }
@@ -664,9 +688,27 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
 #pragma unroll
             for (int c = 0; c < 2; ++c) pb[t][c] = as_bf16x8(u32x4{0, 0, 0, 0});   // P_{-1}
         Slots sl{0, 1, 2};
-        for (int j = 0; j < T; ++j)
-            kv_step(a, I, Qu, Wv, sl, j, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
-        // O += V_{T-1} P_{T-1} (tile T-1 sits in slot u2 now)
+        Qu.kp = Qu.k0;
+        if (Wv.g == 0)
+            for (int j = 0; j < T; ++j)
+                kv_step<0>(a, I, Qu, Wv, sl, j, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
+        else
+            for (int j = 0; j < T; ++j)
+                kv_step<1>(a, I, Qu, Wv, sl, j, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
+        // the last tile (V_{T-1} sits in slot u2 now): group 1 still owes its
+        // softmax; then O += V_{T-1} P_{T-1}
+        if (Wv.g == 1) {
+            float rsum;
+            const float alpha = softmax_tile(a, I, Wv, sacc, Qu.kp, (Qu.iv & 16u) != 0, s_mv + ((T - 1) & 3) * MVW,
+                                             st, pb, rsum);
+            if (alpha != 1.f) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) st.o[dt][e] *= alpha;
+            }
+            st.l_run = st.l_run * alpha + rsum;
+        }
         pv_part(vbuf(sl.u2), pb, st, lane);
     }
     epilogue(a, Wv, I, st);
@@ -744,42 +786,34 @@ __global__ __launch_bounds__(NTH, 2) void fm_fused_bf16_kernel(AttnArgs a) {
 }
 
 // ---- merge of split rows ----------------------------------------------
-// Combines the partials of every split row in split order (deterministic):
-// m = max_s m_s, l = sum_s 2^(m_s - m) l_s, O = sum_s 2^(m_s - m) O_s,
-// out = O / l, lse = (m + log2 l) ln 2.  Task = (split row and head, wave
-// slot w of the partial layout, channel group g); thread = (lane of that
-// wave, dt): every read instruction of a wave is 1 KB contiguous, and a
-// thread issues the reads of up to MSPL splits before using any of them.
+// Combines the partials of every split row in split order (deterministic,
+// one pass with the running max): with m = max so far,
+//   m' = max(m, m_s),  l = l 2^(m - m') + l_s 2^(m_s - m'),
+//   O = O 2^(m - m') + O_s 2^(m_s - m'),
+// then out = O / l and lse = (m + log2 l) ln 2.  Work comes from the list of
+// split rows the planner wrote (one entry per split row and head).  Task =
+// (entry, wave slot w of the partial layout, channel group g); thread =
+// (lane of that wave, dt): every read instruction of a wave is 1 KB
+// contiguous, and a thread issues the reads of up to MSPL splits before
+// using any of them.
 constexpr int MNTH = 256, MSPL = 16;
 
 __global__ __launch_bounds__(MNTH) void fm_merge_bf16_kernel(AttnArgs a) {
-    const int n_items = *a.n_items;
+    const int n_merge = *a.n_merge;
     const int lane = threadIdx.x & 63, dt = threadIdx.x >> 6, n = lane & 31, hh = lane >> 5;
-    const int64_t n_tasks = (int64_t)n_items * NW * 4;
+    const int64_t n_tasks = (int64_t)min((int64_t)n_merge, a.merge_cap) * NW * 4;
     for (int64_t task = blockIdx.x; task < n_tasks; task += gridDim.x) {
-        const int it = (int)(task / (NW * 4)), w = (int)((task / 4) % NW), g = (int)(task % 4);
-        const int32_t* rec = a.items + (int64_t)it * ITEM_WORDS;
-        const int nsp = rec[6];
-        if (rec[5] != 0 || nsp <= 1) continue;
-        const int h = rec[1], qt = rec[2], s_b = rec[8], e_b = rec[9], slot0 = rec[11];
-        const int lr = 32 * w + n;
-        const int64_t qrow = (int64_t)s_b + qt * BR + lr;
-        if (qrow >= e_b) continue;
+        const int64_t k = task / (NW * 4);
+        const int w = (int)((task / 4) % NW), g = (int)(task % 4);
+        const int4 e0 = *(const int4*)(a.merge_list + k * MERGE_WORDS);
+        const int nsp = a.merge_list[k * MERGE_WORDS + 4];
+        const int slot0 = e0.x, h = e0.y, lr = 32 * w + n;
+        const int64_t qrow = (int64_t)e0.z + lr;
+        if (qrow >= e0.w) continue;
         const float* p0 = a.partial + ((int64_t)slot0 * a.H + h) * PART;
         const int64_t step = (int64_t)a.H * PART;
         const int oi = part_index(w, dt, g, lane);
-        // pass 1: row max over splits
-        float m_all = -INFINITY;
-        for (int s0 = 0; s0 < nsp; s0 += MSPL) {
-            float mv[MSPL];
-#pragma unroll
-            for (int u = 0; u < MSPL; ++u) mv[u] = s0 + u < nsp ? p0[(s0 + u) * step + BR * HD + lr] : -INFINITY;
-#pragma unroll
-            for (int u = 0; u < MSPL; ++u) m_all = fmaxf(m_all, mv[u]);
-        }
-        const float m_use = (m_all == -INFINITY) ? 0.f : m_all;
-        // pass 2: weighted sums in split order
-        float l_all = 0.f;
+        float m = -INFINITY, l = 0.f;
         float4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int s0 = 0; s0 < nsp; s0 += MSPL) {
             float mv[MSPL], lv[MSPL];
@@ -795,22 +829,25 @@ __global__ __launch_bounds__(MNTH) void fm_merge_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int u = 0; u < MSPL; ++u)
                 if (s0 + u < nsp) {
-                    const float wgt = __builtin_amdgcn_exp2f(mv[u] - m_use);
-                    l_all = __builtin_fmaf(wgt, lv[u], l_all);
-                    acc.x = __builtin_fmaf(wgt, ov[u].x, acc.x);
-                    acc.y = __builtin_fmaf(wgt, ov[u].y, acc.y);
-                    acc.z = __builtin_fmaf(wgt, ov[u].z, acc.z);
-                    acc.w = __builtin_fmaf(wgt, ov[u].w, acc.w);
+                    const float mn = fmaxf(m, mv[u]);
+                    const float mu = mn == -INFINITY ? 0.f : mn;
+                    const float ca = __builtin_amdgcn_exp2f(m - mu), cb = __builtin_amdgcn_exp2f(mv[u] - mu);
+                    l = __builtin_fmaf(l, ca, lv[u] * cb);
+                    acc.x = __builtin_fmaf(acc.x, ca, ov[u].x * cb);
+                    acc.y = __builtin_fmaf(acc.y, ca, ov[u].y * cb);
+                    acc.z = __builtin_fmaf(acc.z, ca, ov[u].z * cb);
+                    acc.w = __builtin_fmaf(acc.w, ca, ov[u].w * cb);
+                    m = mn;
                 }
         }
-        const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
         uint16_t* op = (uint16_t*)a.out + qrow * ((int64_t)a.H * HD) + (int64_t)h * HD + 32 * dt + 8 * g + 4 * hh;
         u32x2 wv;
         wv.x = bf16_bits(acc.x * inv) | (bf16_bits(acc.y * inv) << 16);
         wv.y = bf16_bits(acc.z * inv) | (bf16_bits(acc.w * inv) << 16);
         *(u32x2*)op = wv;
         if (dt == 0 && g == 0 && hh == 0)
-            a.lse[(int64_t)h * a.N + qrow] = l_all > 0.f ? (m_all + __log2f(l_all)) * LN2 : -INFINITY;
+            a.lse[(int64_t)h * a.N + qrow] = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
     }
 }
 
@@ -823,7 +860,7 @@ int occupancy(const void* fn) {
 
 hipError_t launch_merge(const AttnArgs& a, int n_cu, hipStream_t s) {
     if (a.S <= 0) return hipSuccess;
-    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.items_cap * NW * 4, (int64_t)n_cu * 16));
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.merge_cap * NW * 4, (int64_t)n_cu * 8));
     hipLaunchKernelGGL(fm_merge_bf16_kernel, dim3((unsigned)grid), dim3(MNTH), 0, s, a);
     return hipGetLastError();
 }

@@ -8,7 +8,10 @@
 namespace fm {
 
 // Header words of the workspace (int32 index) and class counts (byte offset).
-enum : int { HDR_STATUS = 0, HDR_NKB = 1, HDR_NITEMS = 2, HDR_SCHED = 3, HDR_NSLOTS = 4 };
+enum : int { HDR_STATUS = 0, HDR_NKB = 1, HDR_NITEMS = 2, HDR_SCHED = 3, HDR_NSLOTS = 4, HDR_NMERGE = 5 };
+// Split-row list entry (int32 x MERGE_WORDS): slot of split 0, head, first
+// row, end row (exclusive), number of splits, three zero words.
+constexpr int MERGE_WORDS = 8;
 constexpr int HDR_COUNTS_BYTE = 64;
 constexpr int ITEM_WORDS = 16;  // seq, head, q_tile, kb_begin, kb_end, split_idx, n_splits, cost,
                                 // seq_start, seq_end, kb_base, split0_slot, 0, 0, 0, 0
@@ -41,7 +44,8 @@ struct PlanPtrs {
     char* scratch;
     ScratchLayout sl;
     int cost_cap;              // largest cost a q tile can have (histogram size - 1)
-    int32_t* merge_counter;    // nullable: split arrival counters, zeroed for n_slots * H
+    int32_t* merge_list;       // nullable: split-row list (S > 0), MERGE_WORDS per entry
+    int32_t* n_merge;          // nullable: its entry count
 };
 
 hipError_t launch_extrema(const int32_t* sv, int n_vec, int causal, const int32_t* cu, int B,
@@ -68,10 +72,13 @@ struct AttnArgs {
     int32_t* sched_counter;
     const int32_t* sl_off;     // per-sequence first slot (split partial index)
     float* partial;            // split partials (S > 0)
-    int32_t* merge_counter;    // split arrival counters (S > 0), zero between calls
+    const int32_t* merge_list; // split-row list (S > 0)
+    const int32_t* n_merge;
+    int64_t merge_cap;         // entries the list can hold
     unsigned flags;
     // fused path only: where the in-kernel planner writes the plan
     int32_t* w_hdr; int32_t* w_kb_off; int32_t* w_ext; int32_t* w_items; int64_t* w_counts;
+    int32_t* w_merge;          // split-row list (S > 0), else null
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int n_cu, hipStream_t s);

@@ -95,7 +95,7 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
     int4* t_sinfo = (int4*)(tmp + LP_OFF_SINFO);
     int* t_byrank = (int*)(tmp + LP_OFF_BYRANK);
     int* t_sv = (int*)(tmp + LP_OFF_SV);
-    __shared__ int s_misc[8];            // status, FULL, PARTIAL, UNMASKED counts
+    __shared__ int s_misc[8];            // status, FULL, PARTIAL, UNMASKED counts, split rows
     __shared__ long long s_scan[17];
     int32_t* hdr = a.w_hdr;
     const bool writer = blockIdx.x == gridDim.x - 1;   // writes the plan to the workspace
@@ -105,7 +105,7 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
     if (B > LP_MAX_B) {   // host bound violated
         if (writer && tid == 0) {
             hdr[HDR_STATUS] = FM_STATUS_CAP; hdr[HDR_NKB] = 0; hdr[HDR_NITEMS] = 0; hdr[HDR_SCHED] = 0;
-            hdr[HDR_NSLOTS] = 0;
+            hdr[HDR_NSLOTS] = 0; hdr[HDR_NMERGE] = 0;
         }
         return LdsPlan{FM_STATUS_CAP, 0, 0};
     }
@@ -195,7 +195,7 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
         for (int b = tid; b <= B; b += blockDim.x) a.w_kb_off[b] = status ? 0 : t_kboff[b];
     if (status) {
         if (writer && tid == 0) {
-            hdr[HDR_NITEMS] = 0; hdr[HDR_NSLOTS] = 0;
+            hdr[HDR_NITEMS] = 0; hdr[HDR_NSLOTS] = 0; hdr[HDR_NMERGE] = 0;
             a.w_counts[0] = a.w_counts[1] = a.w_counts[2] = 0;
         }
         return LdsPlan{status, 0, 0};
@@ -294,7 +294,7 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
     const int n_valid = (int)carry;
     if (n_valid > LP_MAX_SLOTS || (long long)n_valid * H > (long long)LP_MAX_MY * gridDim.x) {
         if (writer && tid == 0) {
-            hdr[HDR_STATUS] = FM_STATUS_CAP; hdr[HDR_NKB] = 0; hdr[HDR_NITEMS] = 0; hdr[HDR_NSLOTS] = 0;
+            hdr[HDR_STATUS] = FM_STATUS_CAP; hdr[HDR_NKB] = 0; hdr[HDR_NITEMS] = 0; hdr[HDR_NSLOTS] = 0; hdr[HDR_NMERGE] = 0;
             a.w_counts[0] = a.w_counts[1] = a.w_counts[2] = 0;
         }
         return LdsPlan{FM_STATUS_CAP, 0, 0};
@@ -361,9 +361,22 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
             const int it = idx / ITEM_WORDS, w = idx - it * ITEM_WORDS;
             a.w_items[idx] = w < 12 ? record(it, w) : 0;
         }
+        // split rows: one merge entry per (split row, head), from its split 0
+        if (a.w_merge)
+            for (int it = tid; it < n_items; it += blockDim.x)
+                if (record(it, 5) == 0 && record(it, 6) > 1) {
+                    const int k = atomicAdd(&s_misc[4], 1);
+                    int32_t* m = a.w_merge + (int64_t)k * MERGE_WORDS;
+                    const int row0 = record(it, 8) + record(it, 2) * Br;
+                    m[0] = record(it, 11); m[1] = record(it, 1); m[2] = row0;
+                    m[3] = min(row0 + Br, record(it, 9)); m[4] = record(it, 6);
+                    m[5] = m[6] = m[7] = 0;
+                }
+        __syncthreads();
         if (tid == 0) {
             hdr[HDR_NITEMS] = n_items;
             hdr[HDR_NSLOTS] = t_slotbase[B];
+            hdr[HDR_NMERGE] = s_misc[4];
             a.w_counts[0] = s_misc[1]; a.w_counts[1] = s_misc[2]; a.w_counts[2] = s_misc[3];
         }
     }

@@ -378,12 +378,14 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
     const long long* __restrict__ seq_counts, int32_t* __restrict__ items, int64_t items_cap,
     int32_t* __restrict__ n_items, long long* __restrict__ class_counts,
     int32_t* __restrict__ sched_counter, int32_t* __restrict__ n_slots_out, int64_t slot_cap,
-    int32_t* __restrict__ merge_counter) {
+    int32_t* __restrict__ merge_list, int32_t* __restrict__ n_merge) {
     extern __shared__ int32_t hist[];  // [cost_cap + 1], then SORT_LDS_INTS of slot data
     int32_t* s_slot = hist + ((cost_cap + 4) & ~3);
     __shared__ long long tmp[17];
     __shared__ long long s_sum[4];
+    __shared__ int s_nmerge;
     const int tid = threadIdx.x;
+    if (tid == 0) s_nmerge = 0;
     const int st = *status;   // read together with the sizes below
     // total slots and class counts over sequences
     long long n_slots = 0;
@@ -404,6 +406,7 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
     }
     if (st != 0) {
         if (tid == 0) {
+            if (n_merge) *n_merge = 0;
             *n_items = 0;
             class_counts[0] = class_counts[1] = class_counts[2] = 0;
             if (sched_counter) *sched_counter = 0;
@@ -476,8 +479,6 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
         }
     }
     __syncthreads();
-    if (merge_counter)
-        for (long long idx = tid; idx < n_slots * H; idx += blockDim.x) merge_counter[idx] = 0;
     if (!overflow) {
         for (long long idx = tid; idx < n_slots * H; idx += blockDim.x) {
             const long long sl = idx / H;
@@ -491,14 +492,23 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
             // derived words: sequence bounds, first extrema block, slot of split 0
             it[8] = cu[b]; it[9] = cu[b + 1]; it[10] = kb_off[b]; it[11] = (int32_t)(sl - rec[2]);
             it[12] = it[13] = it[14] = it[15] = 0;
+            if (merge_list && rec[2] == 0 && rec[3] > 1) {   // split 0 of a split row: one merge entry per head
+                const int k = atomicAdd(&s_nmerge, 1);
+                int32_t* m = merge_list + (int64_t)k * MERGE_WORDS;
+                const int row0 = cu[b] + rec[1] * Br;
+                m[0] = it[11]; m[1] = h; m[2] = row0; m[3] = min(row0 + Br, cu[b + 1]); m[4] = rec[3];
+                m[5] = m[6] = m[7] = 0;
+            }
         }
     }
+    __syncthreads();
     if (tid == 0) {
         *n_items = overflow ? 0 : (int32_t)(total_valid * H);
         if (overflow) atomicOr(status_rw, FM_STATUS_CAP);
         class_counts[0] = s_sum[0]; class_counts[1] = s_sum[1]; class_counts[2] = s_sum[2];
         if (sched_counter) *sched_counter = 0;
         if (n_slots_out) *n_slots_out = (int32_t)n_slots;
+        if (n_merge) *n_merge = overflow ? 0 : s_nmerge;
     }
 }
 
@@ -531,7 +541,7 @@ hipError_t launch_plan(const int32_t* sv, int n_vec, int32_t* ext, int64_t ext_c
     hipLaunchKernelGGL(fm_sort_kernel, dim3(1), dim3(1024), lds, s, p.cu, p.B, p.H, p.Br, p.Bc,
                        p.S, p.cost_cap, p.kb_off, p.status, p.status_rw, slots, pos, seq_counts, p.items,
                        p.items_cap, p.n_items, (long long*)p.class_counts, p.sched_counter,
-                       p.n_slots, p.sl.slot_cap, p.merge_counter);
+                       p.n_slots, p.sl.slot_cap, p.merge_list, p.n_merge);
     return hipGetLastError();
 }
 
@@ -549,7 +559,7 @@ hipError_t launch_worklist(const PlanPtrs& p, hipStream_t s) {
     hipLaunchKernelGGL(fm_sort_kernel, dim3(1), dim3(1024), lds, s, p.cu, p.B, p.H, p.Br, p.Bc,
                        p.S, p.cost_cap, p.kb_off, p.status, p.status_rw, slots, pos, seq_counts, p.items,
                        p.items_cap, p.n_items, (long long*)p.class_counts, p.sched_counter,
-                       p.n_slots, p.sl.slot_cap, p.merge_counter);
+                       p.n_slots, p.sl.slot_cap, p.merge_list, p.n_merge);
     return hipGetLastError();
 }
 
