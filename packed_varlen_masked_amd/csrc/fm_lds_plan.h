@@ -37,12 +37,11 @@ constexpr int LP_OFF_ROWOFF = LP_OFF_KBOFF + 4 * LP_SEQ_INTS;
 constexpr int LP_OFF_TILEOFF = LP_OFF_ROWOFF + 4 * LP_SEQ_INTS;
 constexpr int LP_OFF_SLOTBASE = LP_OFF_TILEOFF + 4 * LP_SEQ_INTS;
 constexpr int LP_OFF_EXT = LP_OFF_SLOTBASE + 4 * LP_SEQ_INTS;     // int[LP_MAX_KB][8]
-constexpr int LP_OFF_ROWCOST = LP_OFF_EXT + 32 * LP_MAX_KB;       // int[LP_MAX_ROWS]
-constexpr int LP_OFF_ROWSLOT = LP_OFF_ROWCOST + 4 * LP_MAX_ROWS;  // int[LP_MAX_ROWS]
-constexpr int LP_OFF_KEY = LP_OFF_ROWSLOT + 4 * LP_MAX_ROWS;      // uint64[LP_MAX_SLOTS]
-constexpr int LP_OFF_SINFO = LP_OFF_KEY + 8 * LP_MAX_SLOTS;       // int4[LP_MAX_SLOTS]
-constexpr int LP_OFF_BYRANK = LP_OFF_SINFO + 16 * LP_MAX_SLOTS;   // int[LP_MAX_SLOTS]
-constexpr int LP_OFF_SV = LP_OFF_BYRANK + 4 * LP_MAX_SLOTS;       // int[LP_MAX_SV]
+constexpr int LP_OFF_SLOTAT = LP_OFF_EXT + 32 * LP_MAX_KB;        // int[LP_MAX_SLOTS]: slot at each rank
+constexpr int LP_OFF_KEY = LP_OFF_SLOTAT + 4 * LP_MAX_SLOTS;      // uint64[LP_MAX_SLOTS]: sort key per slot
+constexpr int LP_OFF_SINFO = LP_OFF_KEY + 8 * LP_MAX_SLOTS;       // int4[LP_MAX_SLOTS]: chunk per slot
+constexpr int LP_OFF_RANK = LP_OFF_SINFO + 16 * LP_MAX_SLOTS;     // int[LP_MAX_SLOTS]: rank per slot
+constexpr int LP_OFF_SV = LP_OFF_RANK + 4 * LP_MAX_SLOTS;         // int[LP_MAX_SV]
 constexpr int LP_TMP_BYTES = LP_OFF_SV + 4 * LP_MAX_SV;
 
 struct LdsPlan {
@@ -89,13 +88,12 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
     int* t_tileoff = (int*)(tmp + LP_OFF_TILEOFF);
     int* t_slotbase = (int*)(tmp + LP_OFF_SLOTBASE);
     int* t_ext = (int*)(tmp + LP_OFF_EXT);
-    int* t_rowcost = (int*)(tmp + LP_OFF_ROWCOST);
-    int* t_rowslot = (int*)(tmp + LP_OFF_ROWSLOT);
+    int* t_slot_at = (int*)(tmp + LP_OFF_SLOTAT);
     uint64_t* t_key = (uint64_t*)(tmp + LP_OFF_KEY);
     int4* t_sinfo = (int4*)(tmp + LP_OFF_SINFO);
-    int* t_byrank = (int*)(tmp + LP_OFF_BYRANK);
+    int* t_rank = (int*)(tmp + LP_OFF_RANK);
     int* t_sv = (int*)(tmp + LP_OFF_SV);
-    __shared__ int s_misc[8];            // status, FULL, PARTIAL, UNMASKED counts, split rows
+    __shared__ int s_misc[8];   // status, FULL, PARTIAL, UNMASKED counts, split rows, filled slots
     __shared__ long long s_scan[17];
     int32_t* hdr = a.w_hdr;
     const bool writer = blockIdx.x == gridDim.x - 1;   // writes the plan to the workspace
@@ -109,44 +107,29 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
         }
         return LdsPlan{FM_STATUS_CAP, 0, 0};
     }
-    for (int i = tid; i <= B; i += blockDim.x) t_cu[i] = a.cu[i];
-    // stage the stored mask vectors (SoA [n_vec][N], contiguous)
+    // cu first, then the stored mask vectors (SoA [n_vec][N], contiguous)
+    // into registers: the sequence prefix sums below run while the vector
+    // loads are in flight (one memory round trip: LP_MAX_SV values are at
+    // most 8 loads of 16 bytes per thread)
+    constexpr int U = LP_MAX_SV / 4 / 512;
+    static_assert(U * 4 * 512 == LP_MAX_SV, "one staging round covers the capacity");
     const int nsv = a.n_vec * (int)N;
-    const bool sv_fits = nsv <= LP_MAX_SV;
+    const bool sv_fits = nsv <= LP_MAX_SV && blockDim.x == 512;
+    const bool sv16 = ((uintptr_t)a.sv & 15) == 0;
+    const int n4 = sv16 ? (nsv >> 2) : 0;   // 16-byte loads; the rest one by one
+    for (int i = tid; i <= B; i += blockDim.x) t_cu[i] = a.cu[i];
+    int4 rv[U];
+    int r1[U];
     if (sv_fits) {
-        // all loads of a round in flight before any LDS store (one memory
-        // round trip per 8 vectors of 16 bytes per thread)
-        constexpr int U = 8;
-        if (((uintptr_t)a.sv & 15) == 0) {
-            const int n4 = nsv >> 2;
-            for (int base = 0; base < n4; base += U * (int)blockDim.x) {
-                int4 r[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = base + u * (int)blockDim.x + tid;
-                    if (i < n4) r[u] = ((const int4*)a.sv)[i];
-                }
+        for (int u = 0; u < U; ++u) {
+            const int i = u * 512 + tid;
+            if (i < n4) rv[u] = ((const int4*)a.sv)[i];
+        }
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = base + u * (int)blockDim.x + tid;
-                    if (i < n4) ((int4*)t_sv)[i] = r[u];
-                }
-            }
-            for (int i = 4 * n4 + tid; i < nsv; i += blockDim.x) t_sv[i] = a.sv[i];
-        } else {
-            for (int base = 0; base < nsv; base += U * (int)blockDim.x) {
-                int r[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = base + u * (int)blockDim.x + tid;
-                    if (i < nsv) r[u] = a.sv[i];
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = base + u * (int)blockDim.x + tid;
-                    if (i < nsv) t_sv[i] = r[u];
-                }
-            }
+        for (int u = 0; u < U; ++u) {
+            const int i = 4 * n4 + u * 512 + tid;
+            if (i < nsv && i < 4 * n4 + U * 512) r1[u] = a.sv[i];
         }
     }
     __syncthreads();
@@ -181,10 +164,25 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
         }
         if (lane == 0) { t_kboff[B] = ckb; t_rowoff[B] = crow; t_tileoff[B] = ctile; t_slotbase[B] = cslot; }
     }
+    if (sv_fits) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = u * 512 + tid;
+            if (i < n4) ((int4*)t_sv)[i] = rv[u];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = 4 * n4 + u * 512 + tid;
+            if (i < nsv && i < 4 * n4 + U * 512) t_sv[i] = r1[u];
+        }
+        // an unaligned vector array: the values past the first round
+        for (int i = 4 * n4 + U * 512 + tid; i < nsv; i += 512) t_sv[i] = a.sv[i];
+    }
     __syncthreads();
-    const int n_kb = t_kboff[B], R = t_rowoff[B], n_tiles = t_tileoff[B];
+    const int n_kb = t_kboff[B], R = t_rowoff[B], n_tiles = t_tileoff[B], n_std = t_slotbase[B];
     int status = s_misc[0];
-    if (!status && (!sv_fits || n_kb > LP_MAX_KB || R > LP_MAX_ROWS || n_tiles > LP_MAX_TILES))
+    if (!status && (!sv_fits || n_kb > LP_MAX_KB || R > LP_MAX_ROWS ||
+                    n_tiles > LP_MAX_TILES || n_std > LP_MAX_SLOTS))
         status = FM_STATUS_CAP;
     if (writer && tid == 0) {
         hdr[HDR_STATUS] = status;
@@ -201,49 +199,67 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
         return LdsPlan{status, 0, 0};
     }
 
-    // ---- block extrema (§3.1): one key block per thread, 64 columns from
-    // LDS, read in a rotated order so that the lanes of a wave hit distinct
-    // banks ----
-    // stored vector behind each logical vector (LTS, LTE, UTS, UTE) for the
-    // accepted (n_vec, causal) pairs; absent ones take their default (LTE:
-    // N; UTS, UTE: 0)
+    // ---- block extrema (§3.1): 8 threads per key block, 8 columns each,
+    // combined across the 8 lanes; the column order is rotated by the block
+    // so that the lanes of a wave hit distinct banks.  Stored vector behind
+    // each logical vector (LTS, LTE, UTS, UTE) for the accepted (n_vec,
+    // causal) pairs; absent ones take their default (LTE: N; UTS, UTE: 0).
+    // The sort keys and rank counters of the split slots are reset here too.
     const int n32 = (int)N;
     const int src[4] = {0, (a.n_vec == 4 || (a.causal && a.n_vec == 2)) ? 1 : -1, a.n_vec == 4 ? 2 : -1,
                         a.n_vec == 4 ? 3 : (!a.causal && a.n_vec == 2) ? 1 : -1};
-    for (int g = tid; g < n_kb; g += blockDim.x) {
-        const int b = owner_of(t_kboff, B, g);
-        const int s0 = t_cu[b], c0 = s0 + (g - t_kboff[b]) * Bc, last = min(c0 + Bc, t_cu[b + 1]) - 1;
+    for (int i = tid; i < n_std; i += blockDim.x) { t_key[i] = ~0ull; t_rank[i] = 0; }
+    for (int g0 = 0; g0 < n_kb; g0 += (int)blockDim.x / 8) {
+        const int g = g0 + tid / 8, sl = tid & 7;
+        const bool act = g < n_kb;
+        int b = 0, c0 = 0, last = 0;
+        if (act) {
+            b = owner_of(t_kboff, B, g);
+            c0 = t_cu[b] + (g - t_kboff[b]) * Bc;
+            last = min(c0 + Bc, t_cu[b + 1]) - 1;
+        }
         int mn[4], mx[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            if (src[t] < 0) {
+            if (src[t] < 0) {   // uniform
                 mn[t] = mx[t] = t == 1 ? n32 : 0;
                 continue;
             }
-            const int* p = t_sv + src[t] * n32;
             int lo = INT_MAX, hi = INT_MIN;
-            // rows past the block's last column repeat it; the column order
-            // is rotated by g so that the lanes of a wave hit distinct banks
-#pragma unroll 16
-            for (int i = 0; i < Bc; ++i) {
-                const int x = p[min(c0 + ((i + g) & (Bc - 1)), last)];
-                lo = min(lo, x); hi = max(hi, x);
+            if (act) {
+                const int* p = t_sv + src[t] * n32;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {   // columns past the block's last repeat it
+                    const int x = p[min(c0 + 8 * sl + ((i + g) & 7), last)];
+                    lo = min(lo, x); hi = max(hi, x);
+                }
+            }
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) {
+                lo = min(lo, __shfl_xor(lo, o, 64));
+                hi = max(hi, __shfl_xor(hi, o, 64));
             }
             mn[t] = lo; mx[t] = hi;
         }
-        const int4 e0 = {mn[0], mx[0], mn[1], mx[1]}, e1 = {mn[2], mx[2], mn[3], mx[3]};
-        ((int4*)t_ext)[2 * g] = e0;
-        ((int4*)t_ext)[2 * g + 1] = e1;
-        if (writer) {
-            ((int4*)a.w_ext)[2 * (int64_t)g] = e0;
-            ((int4*)a.w_ext)[2 * (int64_t)g + 1] = e1;
+        if (act && sl == 0) {
+            const int4 e0 = {mn[0], mx[0], mn[1], mx[1]}, e1 = {mn[2], mx[2], mn[3], mx[3]};
+            ((int4*)t_ext)[2 * g] = e0;
+            ((int4*)t_ext)[2 * g + 1] = e1;
+            if (writer) {
+                ((int4*)a.w_ext)[2 * (int64_t)g] = e0;
+                ((int4*)a.w_ext)[2 * (int64_t)g + 1] = e1;
+            }
         }
     }
     __syncthreads();
 
     // ---- tile classes and visit lists (§3.2): one q tile per wave, one key
-    // block per lane ----
-    int cnt[3] = {0, 0, 0};
+    // block per lane; each q tile's split chunks go straight into its slots
+    // (slot numbering as in the workspace plan: sequences in order, q tiles
+    // in order, ceil(Tc / S) slots per q tile), keyed for the longest-first
+    // order: (-chunk size, slot) ----
+    auto n_split = [&](int cost) { return (S == 0 || cost <= S) ? 1 : ceil_div(cost, S); };
+    int cnt[3] = {0, 0, 0}, nv = 0;
     for (int r = wid; r < R; r += nw) {
         const int b = owner_of(t_rowoff, B, r);
         const int qt = r - t_rowoff[b];
@@ -269,7 +285,14 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
             if (v) vis[vbase + cost + __popcll(m & lanemask_lt())] = (uint16_t)(kb | ((int)iv << 15));
             cost += __popcll(m);
         }
-        if (lane == 0) t_rowcost[r] = cost;
+        const int n = n_split(cost), q = cost / n, rem = cost % n;
+        const int sb = t_slotbase[b] + qt * ((S > 0 && Tc > 0) ? ceil_div(Tc, S) : 1);
+        for (int s = lane; s < n; s += 64) {
+            const int size = q + (s < rem ? 1 : 0), start = s * q + min(s, rem);
+            t_key[sb + s] = ((uint64_t)(FM_MAX_COST - size) << 32) | (uint64_t)(sb + s);
+            t_sinfo[sb + s] = int4{(b << 16) | qt, s | (n << 16), start, size};
+        }
+        nv += n;
     }
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
@@ -278,20 +301,9 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
         for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
         if (lane == 0 && v) atomicAdd(&s_misc[1 + c], v);
     }
+    if (lane == 0 && nv) atomicAdd(&s_misc[5], nv);
     __syncthreads();
-
-    // ---- split chunks: compact index of each row's first chunk ----
-    auto n_split = [&](int cost) { return (S == 0 || cost <= S) ? 1 : ceil_div(cost, S); };
-    long long carry = 0;
-    for (int base = 0; base < R; base += blockDim.x) {
-        const int r = base + tid;
-        const long long n = r < R ? n_split(t_rowcost[r]) : 0;
-        long long tot;
-        const long long ex = block_exclusive_scan(n, s_scan, &tot);
-        if (r < R) t_rowslot[r] = (int)(carry + ex);
-        carry += tot;
-    }
-    const int n_valid = (int)carry;
+    const int n_valid = s_misc[5];
     if (n_valid > LP_MAX_SLOTS || (long long)n_valid * H > (long long)LP_MAX_MY * gridDim.x) {
         if (writer && tid == 0) {
             hdr[HDR_STATUS] = FM_STATUS_CAP; hdr[HDR_NKB] = 0; hdr[HDR_NITEMS] = 0; hdr[HDR_NSLOTS] = 0; hdr[HDR_NMERGE] = 0;
@@ -299,34 +311,33 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
         }
         return LdsPlan{FM_STATUS_CAP, 0, 0};
     }
-    for (int r = tid; r < R; r += blockDim.x) {
-        const int b = owner_of(t_rowoff, B, r);
-        const int qt = r - t_rowoff[b];
-        const int cost = t_rowcost[r], n = n_split(cost);
-        const int q = cost / n, rem = cost % n;
-        const int ci0 = t_rowslot[r];
-        for (int s = 0; s < n; ++s) {
-            const int size = q + (s < rem ? 1 : 0), start = s * q + min(s, rem);
-            // order: longest first, then (sequence, q tile, split) = compact index
-            t_key[ci0 + s] = ((uint64_t)(FM_MAX_COST - size) << 32) | (uint64_t)(ci0 + s);
-            t_sinfo[ci0 + s] = int4{(b << 16) | qt, s | (n << 16), start, size};
+    // ---- rank of every filled slot: the number of smaller keys, counted by
+    // `parts` threads per slot over disjoint ranges ----
+    {
+        const int parts = max(1, min(8, (int)blockDim.x / max(n_std, 1)));
+        const int chunk = ceil_div(n_std, parts);
+        for (int t = tid; t < n_std * parts; t += blockDim.x) {
+            const int i = t / parts, part = t - i * parts;
+            const uint64_t key = t_key[i];
+            if (key == ~0ull) continue;
+            const int j0 = part * chunk, j1 = min(j0 + chunk, n_std);
+            int rk = 0;
+#pragma unroll 8
+            for (int j = j0; j < j1; ++j) rk += t_key[j] < key ? 1 : 0;
+            if (rk) atomicAdd(&t_rank[i], rk);
         }
     }
     __syncthreads();
-    for (int i = tid; i < n_valid; i += blockDim.x) {
-        const uint64_t key = t_key[i];
-        int rk = 0;
-#pragma unroll 8
-        for (int j = 0; j < n_valid; ++j) rk += t_key[j] < key ? 1 : 0;
-        t_byrank[rk] = i;
-    }
+    // invert: the slot at each rank
+    for (int i = tid; i < n_std; i += blockDim.x)
+        if (t_key[i] != ~0ull) t_slot_at[t_rank[i]] = i;
     __syncthreads();
 
     // ---- items: rank * H + head ----
     const int n_items = n_valid * H;
     auto record = [&](int it, int w) {   // word w of item `it`
         const int rk = it / H, h = it - rk * H;
-        const int4 si = t_sinfo[t_byrank[rk]];
+        const int4 si = t_sinfo[t_slot_at[rk]];
         const int b = si.x >> 16, qt = si.x & 0xffff, s = si.y & 0xffff, n = si.y >> 16;
         const int start = si.z, size = si.w;
         const int s_b = t_cu[b], e_b = t_cu[b + 1];
