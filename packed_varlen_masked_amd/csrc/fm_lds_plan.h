@@ -50,13 +50,29 @@ struct LdsPlan {
     int n_my;     // items of this workgroup, in s_myrec[0 .. n_my)
 };
 
-__device__ inline int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(v, o, 64);
-        if (lane >= o) v += y;
-    }
+// Inclusive prefix sum across the 64 lanes of a wave with DPP row shifts
+// and row broadcasts (no LDS traffic).
+__device__ inline int wave_incl_scan(int v, int /*lane*/) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
     return v;
+}
+
+// min / max over aligned groups of 8 lanes (DPP quad permutes, then the
+// half-row mirror): every lane of the group receives the result.
+__device__ inline int min8(int x) {
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xf, 0xf, false));    // quad_perm [1,0,3,2]
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xf, 0xf, false));    // quad_perm [2,3,0,1]
+    return min(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xf, 0xf, false));   // row_half_mirror
+}
+__device__ inline int max8(int x) {
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xf, 0xf, false));
+    return max(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xf, 0xf, false));
 }
 
 // Index of the last entry <= x of an ascending int array of n + 1 entries
@@ -234,12 +250,7 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
                     lo = min(lo, x); hi = max(hi, x);
                 }
             }
-#pragma unroll
-            for (int o = 1; o < 8; o <<= 1) {
-                lo = min(lo, __shfl_xor(lo, o, 64));
-                hi = max(hi, __shfl_xor(hi, o, 64));
-            }
-            mn[t] = lo; mx[t] = hi;
+            mn[t] = min8(lo); mx[t] = max8(hi);
         }
         if (act && sl == 0) {
             const int4 e0 = {mn[0], mx[0], mn[1], mx[1]}, e1 = {mn[2], mx[2], mn[3], mx[3]};
