@@ -24,12 +24,12 @@
 //   * K and V tiles sit row-major in LDS ([key][channel], rows padded); the
 //     V^T operand is read with the gfx950 LDS transpose read
 //     (ds_read_b64_tr_b16).
-//   * software pipeline inside every wave: a step issues the MFMAs of
-//     S_j = K_j Q^T beside the exponentials of tile j-1, then the MFMAs of
-//     O += V_{j-1} P_{j-1} beside the masks and row max of tile j, so the
-//     vector work of the softmax runs in the shadow of the wave's own matrix
-//     work, and the two waves of a SIMD share its matrix pipe.  All waves
-//     advance together, one workgroup barrier per step.
+//   * two groups of four waves (one wave of each per SIMD) run the same
+//     step in opposite phase: group 0 issues the MFMAs of S_j = K_j Q^T and
+//     O += V_{j-1} P_{j-1}, then the softmax of tile j; group 1 the softmax
+//     of tile j-1, then the same MFMAs.  While one wave of a SIMD feeds its
+//     matrix unit the other keeps its vector unit busy.  All waves advance
+//     together, one workgroup barrier per step.
 //   * a 3-deep ring of K and V buffers filled by asynchronous global->LDS
 //     copies (inline assembly, waited for explicitly): in step j waves 0-3
 //     copy K_{j+2} and its mask vectors, waves 4-7 copy V_{j+1}; a step
@@ -167,8 +167,9 @@ struct Wave {
 
 // MFMA phase, part 1: S^T = K Q^T, two 32-key tiles x 8 k-steps.  K
 // fragments are read two k-steps ahead of the MFMAs that use them.
+template <typename CP>
 __device__ __attribute__((always_inline)) inline void s_part(const char* kl, const bf16x8 (&qf)[8],
-                                                             f32x16 (&sacc)[2], int n, int hh) {
+                                                             f32x16 (&sacc)[2], int n, int hh, CP&& cp) {
     const char* kp = kl + n * (KCH * 16) + 16 * hh;
     auto kfrag = [&](int t, int s) { return as_bf16x8(*(const u32x4*)(kp + 32 * t * (KCH * 16) + 32 * s)); };
 #pragma unroll
@@ -189,6 +190,7 @@ __device__ __attribute__((always_inline)) inline void s_part(const char* kl, con
 #pragma unroll
         for (int t = 0; t < 2; ++t)
             sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % 3][t], qf[s], sacc[t], 0, 0, 0);
+        cp(s);
     }
     // keep the order: 4 reads, then (2 reads, 2 MFMAs) x 6, then 4 MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -337,20 +339,23 @@ __device__ __attribute__((always_inline)) inline Tile tile_at(const Item& I, con
     return t;
 }
 
-// This wave's five block copies of the tile at `src` into the slot at `dst`
-// (rows past the tile's last valid row repeat it: finite data, masked later).
+// Block copy i (0..4) of this wave for the tile at `src` into the slot at
+// `dst` (rows past the tile's last valid row repeat it: finite data, masked
+// later).
+__device__ __attribute__((always_inline)) inline void copy_one(const Wave& Wv, const char* src, int last,
+                                                               char* dst, int i) {
+    if (last == BC - 1) {
+        dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src, Wv.vo[i]);
+    } else {   // the last tile of a sequence: rows past `last` repeat it
+        const uint32_t cp = bf16c::copy_lane(Wv.g, Wv.t, i, Wv.lane);
+        dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src, (uint32_t)min((int)(cp & 0xffu), last) * Wv.rsb + (cp >> 8));
+    }
+}
+// This wave's five block copies of a tile.
 __device__ __attribute__((always_inline)) inline void copy_tile(const Wave& Wv, const char* src, int last,
                                                                 char* dst) {
-    if (last == BC - 1) {
 #pragma unroll
-        for (int i = 0; i < 5; ++i) dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src, Wv.vo[i]);
-    } else {   // the last tile of a sequence: rows past `last` repeat it
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const uint32_t cp = bf16c::copy_lane(Wv.g, Wv.t, i, Wv.lane);
-            dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src, (uint32_t)min((int)(cp & 0xffu), last) * Wv.rsb + (cp >> 8));
-        }
-    }
+    for (int i = 0; i < 5; ++i) copy_one(Wv, src, last, dst, i);
 }
 
 // Group 0: mask vector t of the tile (absent vectors go to the sink).
@@ -425,10 +430,12 @@ __device__ __attribute__((always_inline)) inline float softmax_tile(const AttnAr
 // O is rescaled by the softmax's alpha before the next PV adds to it.
 // P_{-1} is zero and the V slot of step 0 holds zeros, so step 0 adds
 // exactly nothing to O; the last tile's product (and, for group 1, its
-// softmax) follows the loop.  At the start of a step group 0 copies K_{j+2}
-// into K slot u2 and its mask vectors into mask slot (j+2) mod 4, group 1
-// copies V_{j+1} into V slot u1, all last read in step j-1; a step ends by
-// waiting for the previous step's copies, then a barrier.
+// softmax) follows the loop.  Group 0 copies K_{j+2} into K slot u2 and its
+// mask vectors into mask slot (j+2) mod 4, group 1 copies V_{j+1} into V
+// slot u1, all last read in step j-1; the copy instructions sit between the
+// MFMAs of S_j, so that the CU's load path takes them while the matrix unit
+// works.  A step ends by waiting for the previous step's copies, then a
+// barrier.
 template <int G>
 __device__ __attribute__((always_inline)) inline void kv_step(
     const AttnArgs& a, const Item& I, Queue& Qu, const Wave& Wv, Slots& sl, int j, int T, bool& rec_pending,
@@ -442,9 +449,12 @@ __device__ __attribute__((always_inline)) inline void kv_step(
     }
     if constexpr (G == 0) {
         const Tile tl = tile_at(I, Wv, Qu.k2);
-        copy_tile(Wv, Kh + tl.off, tl.last, kbuf(sl.u2));
-        copy_mask(a, Wv, tl, s_mv + ((j + 2) & 3) * MVW);
-        s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh);
+        char* kd = kbuf(sl.u2);
+        int32_t* md = s_mv + ((j + 2) & 3) * MVW;
+        s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh, [&](int s) {
+            if (s < 5) copy_one(Wv, Kh + tl.off, tl.last, kd, s);
+            else if (s == 5) copy_mask(a, Wv, tl, md);
+        });
         pv_part(vbuf(sl.u2), pb, st, Wv.lane);
         float rsum;
         const float alpha = softmax_tile(a, I, Wv, sacc, Qu.k0, (Qu.iv & 1u) != 0, s_mv + (j & 3) * MVW, st, pb, rsum);
@@ -457,7 +467,7 @@ __device__ __attribute__((always_inline)) inline void kv_step(
         st.l_run = st.l_run * alpha + rsum;
     } else {
         const Tile tl = tile_at(I, Wv, Qu.k1);
-        copy_tile(Wv, Vh + tl.off, tl.last, vbuf(sl.u1));
+        char* vd = vbuf(sl.u1);
         if (j > 0) {
             float rsum;
             const float alpha =
@@ -471,7 +481,9 @@ __device__ __attribute__((always_inline)) inline void kv_step(
             st.l_run = st.l_run * alpha + rsum;
         }
         pv_part(vbuf(sl.u2), pb, st, Wv.lane);
-        s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh);
+        s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh, [&](int s) {
+            if (s < 5) copy_one(Wv, Vh + tl.off, tl.last, vd, s);
+        });
     }
     const int nk = __builtin_amdgcn_readfirstlane(nk_raw);
     Qu.kp = Qu.k0;
@@ -668,15 +680,19 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
                   e3 = vis_entry(vis, min(3, T - 1));
         Qu.k0 = e0 & 0x7fff; Qu.k1 = e1 & 0x7fff; Qu.k2 = e2 & 0x7fff; Qu.k3 = e3 & 0x7fff;
         Qu.iv = (uint32_t)((e0 >> 15) | ((e1 >> 15) << 1) | ((e2 >> 15) << 2) | ((e3 >> 15) << 3));
-        // prologue: K_0 and its mask vectors land before step 0; K_1 (and
-        // masks) and V_0 are waited for at the end of step 0.  V slot 2,
-        // read in step 0 against P = 0, is cleared.
+        // prologue: the Q fragments, K_0 (with its mask vectors) and V_0
+        // land before step 0; K_1 (and masks) is waited for at the end of
+        // step 0.  The full wait also tells the compiler that the Q loads are
+        // complete: it cannot see the copies, which share the hardware
+        // counter, so any wait it placed for the Q loads inside the loop
+        // would wait for the copies in flight.  V slot 2, read in step 0
+        // against P = 0, is cleared.
         if (Wv.no_skip) copy_tile_pair(a, I, Wv, Kh, Vh, Qu.k0);
+        wait_vm<0>();
         if (Wv.g == 0) {
             const Tile t1 = tile_at(I, Wv, Qu.k1);
             copy_tile(Wv, Kh + t1.off, t1.last, kbuf(1));
             copy_mask(a, Wv, t1, s_mv + MVW);
-            wait_vm<BATCH_G0>();
         }
         for (int i = tid; i < SLOT_BYTES / 16; i += NTH) ((u32x4*)vbuf(2))[i] = u32x4{0, 0, 0, 0};
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
