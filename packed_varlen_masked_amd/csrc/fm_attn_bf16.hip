@@ -54,6 +54,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -97,12 +98,13 @@ typedef __attribute__((address_space(3))) char lds_char;
 __device__ __attribute__((always_inline)) inline uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_char*)p;
 }
-// One asynchronous copy instruction: 64 lanes x 16 B (or x 4 B) from
-// base + voff (per lane) to LDS at dst + 16 * lane (4 * lane).  The leading
-// s_nop covers the wait states between the scalar writes of the base / M0
-// and their use by the copy.
-__device__ __attribute__((always_inline)) inline void dma16(void* dst, const void* base, uint32_t voff) {
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(base), "{m0}"(lds_addr(dst))
+// Asynchronous copy instructions (global -> LDS): 64 lanes x 16 B through
+// buffer resource `rs` (byte offset voff per lane; lanes past the resource's
+// byte count write zeros), or 64 lanes x 4 B from base + voff, into LDS at
+// dst + 16 * lane (4 * lane).  The leading s_nop covers the wait states
+// between the scalar writes of the resource / base / M0 and their use.
+__device__ __attribute__((always_inline)) inline void dmab16(void* dst, i32x4 rs, uint32_t voff) {
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(rs), "{m0}"(lds_addr(dst))
                  : "memory");
 }
 __device__ __attribute__((always_inline)) inline void dma4(void* dst, const void* base, uint32_t voff) {
@@ -238,43 +240,52 @@ __device__ __attribute__((always_inline)) inline void pv_part(const char* vb, co
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
-// Softmax of a tile, split in two so that each part runs beside matrix work:
-//   mask_max: element masks (only where the tile needs them) and the row
-//             maximum of the scaled scores;
-//   exp_tail: p = exp2(scale * s - m) in base 2 with the scale folded in,
-//             P in bf16 and the row sum, one tile later.
-// Register e of tile t holds key 32t + 8(e>>2) + 4hh + (e&3).
+// Rows [s, e) of a wave's 32 query rows as a bit mask (bit n = row n; s, e
+// relative to the wave's first row, clamped; empty when e <= s).
+__device__ __attribute__((always_inline)) inline uint32_t row_bits(int s, int e) {
+    s = min(max(s, 0), 32);
+    e = min(max(e, s), 32);
+    const int w = e - s;   // s <= 31 whenever w > 0
+    return w >= 32 ? 0xffffffffu : ((1u << w) - 1u) << (s & 31);
+}
+
+// x, or y where the lane's bit of the 64-lane mask {lo: lanes 0-31, hi:
+// lanes 32-63} is set (one v_cndmask with the mask in scalar registers).
+__device__ __attribute__((always_inline)) inline float select_lanes(float x, float y, uint32_t lo, uint32_t hi) {
+    const uint64_t m = ((uint64_t)hi << 32) | lo;
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "s"(m));
+    return r;
+}
+
+// Element masks of a tile and the row maximum of its scaled scores.
+// Register e of tile t holds key 32t + 8(e>>2) + 4hh + (e&3) for query row
+// q0 + (lane & 31), q0 the wave's first row.  Where the tile needs element
+// masks, lane L first builds the 32-row mask of key c0 + L: rows above the
+// diagonal (causal: row < key), every row when the key lies past the
+// sequence end, and the rows of the column intervals [LTS, LTE) and
+// [UTS, UTE) (FlashMask article, §3: masked rows of a key column).  The
+// masks of keys k and k + 4 read from lanes k and k + 4 are then exactly the
+// 64-lane condition that selects -inf for register e.
 __device__ __attribute__((always_inline)) inline float mask_max(f32x16 (&sacc)[2], bool causal, bool ragged, bool iv,
-                                                                int c0, int c1, int qrow, const int32_t* cmv,
-                                                                float sl2, int hh) {
+                                                                int c0, int c1, int q0, const int32_t* cmv,
+                                                                float sl2, int lane) {
     if (causal || ragged || iv) {
+        const int key = c0 + lane;
+        uint32_t mk = causal ? row_bits(0, key - q0) : 0u;
+        if (key >= c1) mk = 0xffffffffu;
+        if (iv) mk |= row_bits(cmv[lane] - q0, cmv[BC + lane] - q0) | row_bits(cmv[2 * BC + lane] - q0, cmv[3 * BC + lane] - q0);
+        const int mki = (int)mk;
+        const float ninf = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int kl0 = 32 * t + 8 * g + 4 * hh;
-                int4 lts, lte, uts, ute;
-                if (iv) {
-                    lts = *(const int4*)&cmv[kl0];
-                    lte = *(const int4*)&cmv[BC + kl0];
-                    uts = *(const int4*)&cmv[2 * BC + kl0];
-                    ute = *(const int4*)&cmv[3 * BC + kl0];
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int j = c0 + kl0 + q;
-                    bool msk = (causal && j > qrow) || (ragged && j >= c1);
-                    if (iv) {
-                        const int s0 = q == 0 ? lts.x : q == 1 ? lts.y : q == 2 ? lts.z : lts.w;
-                        const int e0 = q == 0 ? lte.x : q == 1 ? lte.y : q == 2 ? lte.z : lte.w;
-                        const int s1 = q == 0 ? uts.x : q == 1 ? uts.y : q == 2 ? uts.z : uts.w;
-                        const int e1 = q == 0 ? ute.x : q == 1 ? ute.y : q == 2 ? ute.z : ute.w;
-                        msk |= ((s0 <= qrow) & (qrow < e0)) | ((s1 <= qrow) & (qrow < e1));
-                    }
-                    if (msk) sacc[t][4 * g + q] = -INFINITY;
-                }
+            for (int e = 0; e < 16; ++e) {
+                const int k0 = 32 * t + 8 * (e >> 2) + (e & 3);
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(mki, k0);
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(mki, k0 + 4);
+                sacc[t][e] = select_lanes(sacc[t][e], ninf, lo, hi);
             }
-        }
     }
     float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -339,23 +350,29 @@ __device__ __attribute__((always_inline)) inline Tile tile_at(const Item& I, con
     return t;
 }
 
-// Block copy i (0..4) of this wave for the tile at `src` into the slot at
-// `dst` (rows past the tile's last valid row repeat it: finite data, masked
-// later).
-__device__ __attribute__((always_inline)) inline void copy_one(const Wave& Wv, const char* src, int last,
-                                                               char* dst, int i) {
-    if (last == BC - 1) {
-        dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src, Wv.vo[i]);
-    } else {   // the last tile of a sequence: rows past `last` repeat it
-        const uint32_t cp = bf16c::copy_lane(Wv.g, Wv.t, i, Wv.lane);
-        dma16(dst + 1024 * bf16c::copy_block(Wv.t, i), src, (uint32_t)min((int)(cp & 0xffu), last) * Wv.rsb + (cp >> 8));
-    }
+// Buffer resource of the K or V rows of a tile that lie inside the
+// sequence (rows 0..last from `src`): reads of rows past them return zeros,
+// so the last tile of a sequence needs no clamped addresses.  Zero rows give
+// scores that the tile's element mask sets to -inf and V rows that meet
+// P = 0: they add exactly nothing.
+__device__ __attribute__((always_inline)) inline i32x4 tile_rsrc(const Wave& Wv, const char* src, int last) {
+    const uint64_t b = (uint64_t)(uintptr_t)src;
+    i32x4 d;
+    d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    d[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));   // stride 0
+    d[2] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(last + 1) * Wv.rsb));
+    d[3] = 0x00020000;   // raw 32-bit access
+    return d;
+}
+// Block copy i (0..4) of this wave for the tile behind `rs` into the slot at
+// `dst`.
+__device__ __attribute__((always_inline)) inline void copy_one(const Wave& Wv, i32x4 rs, char* dst, int i) {
+    dmab16(dst + 1024 * bf16c::copy_block(Wv.t, i), rs, Wv.vo[i]);
 }
 // This wave's five block copies of a tile.
-__device__ __attribute__((always_inline)) inline void copy_tile(const Wave& Wv, const char* src, int last,
-                                                                char* dst) {
+__device__ __attribute__((always_inline)) inline void copy_tile(const Wave& Wv, i32x4 rs, char* dst) {
 #pragma unroll
-    for (int i = 0; i < 5; ++i) copy_one(Wv, src, last, dst, i);
+    for (int i = 0; i < 5; ++i) copy_one(Wv, rs, dst, i);
 }
 
 // Group 0: mask vector t of the tile (absent vectors go to the sink).
@@ -372,10 +389,10 @@ __device__ __attribute__((always_inline)) inline void copy_tile_pair(const AttnA
                                                                      const char* Kh, const char* Vh, int kb) {
     const Tile tl = tile_at(I, Wv, kb);
     if (Wv.g == 0) {
-        copy_tile(Wv, Kh + tl.off, tl.last, kbuf(0));
+        copy_tile(Wv, tile_rsrc(Wv, Kh + tl.off, tl.last), kbuf(0));
         copy_mask(a, Wv, tl, s_mv);
     } else {
-        copy_tile(Wv, Vh + tl.off, tl.last, vbuf(0));
+        copy_tile(Wv, tile_rsrc(Wv, Vh + tl.off, tl.last), vbuf(0));
     }
 }
 constexpr int BATCH_G0 = 6, BATCH_G1 = 5;   // copy instructions per wave per step (groups 0, 1)
@@ -415,7 +432,7 @@ __device__ __attribute__((always_inline)) inline float softmax_tile(const AttnAr
                                                                     float& rsum) {
     const int c0 = I.s_b + kb * BC, c1 = min(c0 + BC, I.e_b);
     const bool causal = a.causal && (c1 > I.r0 + 1);
-    const float mx = mask_max(sacc, causal, (c1 - c0) < BC, iv, c0, c1, Wv.qrow, cmv, a.scale_log2, Wv.hh);
+    const float mx = mask_max(sacc, causal, (c1 - c0) < BC, iv, c0, c1, Wv.qrow - Wv.n, cmv, a.scale_log2, Wv.lane);
     return exp_tile(sacc, mx, st, pb, a.scale_log2, rsum);
 }
 
@@ -449,10 +466,11 @@ __device__ __attribute__((always_inline)) inline void kv_step(
     }
     if constexpr (G == 0) {
         const Tile tl = tile_at(I, Wv, Qu.k2);
+        const i32x4 rs = tile_rsrc(Wv, Kh + tl.off, tl.last);
         char* kd = kbuf(sl.u2);
         int32_t* md = s_mv + ((j + 2) & 3) * MVW;
         s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh, [&](int s) {
-            if (s < 5) copy_one(Wv, Kh + tl.off, tl.last, kd, s);
+            if (s < 5) copy_one(Wv, rs, kd, s);
             else if (s == 5) copy_mask(a, Wv, tl, md);
         });
         pv_part(vbuf(sl.u2), pb, st, Wv.lane);
@@ -467,6 +485,7 @@ __device__ __attribute__((always_inline)) inline void kv_step(
         st.l_run = st.l_run * alpha + rsum;
     } else {
         const Tile tl = tile_at(I, Wv, Qu.k1);
+        const i32x4 rs = tile_rsrc(Wv, Vh + tl.off, tl.last);
         char* vd = vbuf(sl.u1);
         if (j > 0) {
             float rsum;
@@ -482,7 +501,7 @@ __device__ __attribute__((always_inline)) inline void kv_step(
         }
         pv_part(vbuf(sl.u2), pb, st, Wv.lane);
         s_part(kbuf(sl.u0), qf, sacc, Wv.n, Wv.hh, [&](int s) {
-            if (s < 5) copy_one(Wv, Vh + tl.off, tl.last, vd, s);
+            if (s < 5) copy_one(Wv, rs, vd, s);
         });
     }
     const int nk = __builtin_amdgcn_readfirstlane(nk_raw);
@@ -691,7 +710,7 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
         wait_vm<0>();
         if (Wv.g == 0) {
             const Tile t1 = tile_at(I, Wv, Qu.k1);
-            copy_tile(Wv, Kh + t1.off, t1.last, kbuf(1));
+            copy_tile(Wv, tile_rsrc(Wv, Kh + t1.off, t1.last), kbuf(1));
             copy_mask(a, Wv, t1, s_mv + MVW);
         }
         for (int i = tid; i < SLOT_BYTES / 16; i += NTH) ((u32x4*)vbuf(2))[i] = u32x4{0, 0, 0, 0};
