@@ -91,7 +91,7 @@ fm::ScratchLayout scratch_layout(int B, const Caps& c) {
     size_t off = 0;
     s.off_slots = off; off = align256(off + (size_t)c.slot * fm::SLOT_WORDS * sizeof(int32_t));
     s.off_pos = off; off = align256(off + (size_t)c.slot * sizeof(int32_t));
-    s.off_seq_counts = off; off = align256(off + (size_t)B * 3 * sizeof(long long));
+    s.off_seq_counts = off; off = align256(off + (size_t)B * fm::PLAN_RC * 3 * sizeof(long long));
     s.off_sl_off = off; off = align256(off + (size_t)(B + 1) * sizeof(int32_t));
     s.bytes = off;
     s.slot_cap = c.slot;
@@ -266,8 +266,10 @@ int build_plan_impl(const Ws& w, const int32_t* cu, int B, int64_t N, int H, con
     p.scratch = w.base + L.off_scratch; p.sl = scratch_layout(B, c); p.cost_cap = c.cost;
     p.merge_list = L.off_merge ? (int32_t*)(w.base + L.off_merge) : nullptr;
     p.n_merge = L.off_merge ? hdr + fm::HDR_NMERGE : nullptr;
+    int n_cu = 0;
+    if ((rc = device_cus(&n_cu))) return rc;
     return hip_check(fm::launch_plan(sv, n_vec, (int32_t*)(w.base + L.off_extrema), L.kb_cap, hdr + fm::HDR_NKB,
-                                     (int32_t*)(w.base + L.off_kb_off), p, s),
+                                     (int32_t*)(w.base + L.off_kb_off), p, n_cu, s),
                      "plan launch");
 }
 

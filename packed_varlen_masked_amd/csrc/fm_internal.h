@@ -16,6 +16,9 @@ constexpr int HDR_COUNTS_BYTE = 64;
 constexpr int ITEM_WORDS = 16;  // seq, head, q_tile, kb_begin, kb_end, split_idx, n_splits, cost,
                                 // seq_start, seq_end, kb_base, split0_slot, 0, 0, 0, 0
 constexpr int SLOT_WORDS = 8;   // seq, q_tile, split_idx, n_splits, kb_begin, kb_end, cost, valid
+// Workgroups per sequence of the tile-class launch (each classifies every
+// PLAN_RC-th group of q tiles); class counts are kept per (sequence, group).
+constexpr int PLAN_RC = 16;
 
 // Worklist scratch carved from one buffer (all offsets 256-aligned).
 struct ScratchLayout {
@@ -55,10 +58,10 @@ hipError_t launch_extrema(const int32_t* sv, int n_vec, int causal, const int32_
 
 hipError_t launch_worklist(const PlanPtrs& p, hipStream_t s);
 
-// Plan path: fused extrema + classification (one workgroup per sequence),
-// then the sort.  Writes kb_off, extrema, n_kblocks and the status word too.
+// Plan path: extrema, tile classes, sort (three launches).  Writes kb_off,
+// extrema, n_kblocks and the status word too.
 hipError_t launch_plan(const int32_t* sv, int n_vec, int32_t* ext, int64_t ext_cap, int32_t* n_kblocks,
-                       int32_t* kb_off_out, const PlanPtrs& p, hipStream_t s);
+                       int32_t* kb_off_out, const PlanPtrs& p, int n_cu, hipStream_t s);
 
 // Attention launch arguments shared by the bf16 and fp32 paths.
 struct AttnArgs {

@@ -119,9 +119,10 @@ __device__ inline SeqDims seq_dims(const int32_t* __restrict__ cu, int b, int Br
 __device__ void classify_rows(const SeqDims& d, int b, int Br, int Bc, int S, int causal,
                               const int4* __restrict__ xs, int32_t* __restrict__ slots, long long slot_base,
                               int64_t slot_cap, long long map_base, uint8_t* __restrict__ tile_class,
-                              int64_t tile_class_cap, long long (&my_cnt)[3]) {
+                              int64_t tile_class_cap, long long (&my_cnt)[3], int group) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    for (int qt = wid; qt < d.Tr; qt += nw) {
+    // q tiles group * nw + wid, then every PLAN_RC * nw-th
+    for (int qt = group * nw + wid; qt < d.Tr; qt += PLAN_RC * nw) {
         const int r0 = d.s + qt * Br, r1 = min(r0 + Br, d.e);
         int cost = 0, first = INT_MAX, last = -1;
         const int64_t map_row = map_base + (int64_t)qt * d.Tc;
@@ -191,7 +192,8 @@ __device__ void classify_rows(const SeqDims& d, int b, int Br, int Bc, int S, in
     }
 }
 
-// N3a: one workgroup per sequence.  The sequence's extrema are staged in LDS
+// N3a: PLAN_RC workgroups per sequence (workgroup b * PLAN_RC + r takes
+// q-tile group r of sequence b).  The sequence's extrema are staged in LDS
 // once (one round of coalesced loads); each wave then classifies q tiles from
 // LDS (one key block per lane), writes the class map, counts classes, and
 // writes the split slots of its q tiles.
@@ -205,161 +207,51 @@ __global__ __launch_bounds__(TILES_NTH) void fm_tiles_kernel(
     long long* __restrict__ seq_counts, int32_t* __restrict__ sl_off,
     uint8_t* __restrict__ tile_class, int64_t tile_class_cap, int64_t slot_cap) {
     if (*status != 0) return;
-    const int b = blockIdx.x;
+    const int b = blockIdx.x / PLAN_RC, group = blockIdx.x % PLAN_RC;
     __shared__ long long tmp[17];
     __shared__ long long s_cnt[3];
     __shared__ int4 s_ext[2 * TILES_LDS_KB];
+    const SeqDims d = seq_dims(cu, b, Br, Bc, S);
+    long long* cnt_out = seq_counts + ((int64_t)b * PLAN_RC + group) * 3;
+    if (group * (TILES_NTH / 64) >= d.Tr) {   // no q tile in this group
+        if (threadIdx.x < 3) cnt_out[threadIdx.x] = 0;
+        return;
+    }
     // offsets of this sequence: slots (sum of Tr*MS) and class map (Tr*Tc)
     long long slot_base = 0, map_base = 0;
     for (int base = 0; base < b; base += blockDim.x) {
         const int bb = base + threadIdx.x;
         long long ns = 0, nm = 0;
         if (bb < b) {
-            const SeqDims d = seq_dims(cu, bb, Br, Bc, S);
-            ns = (long long)d.Tr * d.MS;
-            nm = (long long)d.Tr * d.Tc;
+            const SeqDims e = seq_dims(cu, bb, Br, Bc, S);
+            ns = (long long)e.Tr * e.MS;
+            nm = (long long)e.Tr * e.Tc;
         }
         long long t1, t2;
         block_exclusive_scan(ns, tmp, &t1);
         block_exclusive_scan(nm, tmp, &t2);
         slot_base += t1; map_base += t2;
     }
-    const SeqDims d = seq_dims(cu, b, Br, Bc, S);
     const int4* __restrict__ xg = (const int4*)(ext + (int64_t)kb_off[b] * 8);
     const bool in_lds = d.Tc <= TILES_LDS_KB;
     if (in_lds)
         for (int i = threadIdx.x; i < 2 * d.Tc; i += blockDim.x) s_ext[i] = xg[i];
     if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
-    if (threadIdx.x == 0) sl_off[b] = (int32_t)slot_base;
+    if (threadIdx.x == 0 && group == 0) sl_off[b] = (int32_t)slot_base;
     __syncthreads();
     const int4* xs = in_lds ? s_ext : xg;
     long long my_cnt[3] = {0, 0, 0};
     classify_rows(d, b, Br, Bc, S, causal, xs, slots, slot_base, slot_cap, map_base, tile_class,
-                  tile_class_cap, my_cnt);
+                  tile_class_cap, my_cnt, group);
     const int lane = threadIdx.x & 63;
-    // class counts of this sequence
+    // class counts of this group of q tiles
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
         const long long t = wave_sum64(my_cnt[c]);
         if (lane == 0) atomicAdd((unsigned long long*)&s_cnt[c], (unsigned long long)t);
     }
     __syncthreads();
-    if (threadIdx.x < 3) seq_counts[(int64_t)b * 3 + threadIdx.x] = s_cnt[threadIdx.x];
-}
-
-// Fused preprocessing + classification for the plan path: one workgroup per
-// sequence.  Every workgroup reads all of cu_seqlens (validation and prefix
-// sums, B is small next to N), reduces the extrema of its own key blocks
-// (FlashMask article §3.1), keeps them in LDS, and classifies its q tiles
-// from LDS (§3.2).  Workgroup 0 writes kb_off, the key block count and the
-// status word.  Replaces the extrema and tiles launches of the plan path.
-__global__ __launch_bounds__(TILES_NTH) void fm_seqplan_kernel(
-    const int32_t* __restrict__ sv, int n_vec, int causal, const int32_t* __restrict__ cu, int B,
-    int64_t N, int Br, int Bc, int S, int64_t ext_cap, int64_t slot_cap,
-    int32_t* __restrict__ kb_off, int32_t* __restrict__ ext, int32_t* __restrict__ status,
-    int32_t* __restrict__ n_kblocks, int32_t* __restrict__ slots, long long* __restrict__ seq_counts,
-    int32_t* __restrict__ sl_off, uint8_t* __restrict__ tile_class, int64_t tile_class_cap) {
-    const int b = blockIdx.x;
-    __shared__ long long tmp[17];
-    __shared__ long long s_cnt[3];
-    __shared__ int s_bad;
-    __shared__ int4 s_ext[2 * TILES_LDS_KB];
-    if (threadIdx.x == 0) s_bad = (cu[0] != 0 ? FM_STATUS_CU0 : 0) | (cu[B] != (int)N ? FM_STATUS_CUN : 0);
-    __syncthreads();
-    long long kb_carry = 0, slot_base = 0, map_base = 0, kb_base = 0;
-    for (int base = 0; base < B; base += blockDim.x) {
-        const int bb = base + threadIdx.x;
-        long long tc = 0, ns = 0, nm = 0;
-        if (bb < B) {
-            const int L = cu[bb + 1] - cu[bb];
-            if (L < 0) atomicOr(&s_bad, FM_STATUS_ORDER);
-            const SeqDims d = seq_dims(cu, bb, Br, Bc, S);
-            tc = d.Tc;
-            if (bb < b) { ns = (long long)d.Tr * d.MS; nm = (long long)d.Tr * d.Tc; }
-        }
-        long long t0, t1, t2;
-        const long long ex = block_exclusive_scan(tc, tmp, &t0);
-        if (b == 0 && bb < B) kb_off[bb] = (int32_t)min(kb_carry + ex, (long long)INT_MAX);
-        if (bb == b) kb_base = kb_carry + ex;
-        kb_carry += t0;
-        block_exclusive_scan(ns, tmp, &t1);
-        block_exclusive_scan(nm, tmp, &t2);
-        slot_base += t1; map_base += t2;
-    }
-    if (threadIdx.x == 0 && kb_carry > ext_cap) atomicOr(&s_bad, FM_STATUS_CAP);
-    __syncthreads();
-    // kb_base was found by one thread: share it
-    if (threadIdx.x == (unsigned)(b % blockDim.x)) tmp[16] = kb_base;
-    __syncthreads();
-    kb_base = tmp[16];
-    const int bad = s_bad;
-    if (b == 0 && threadIdx.x == 0) {
-        kb_off[B] = (int32_t)min(kb_carry, (long long)INT_MAX);
-        *status = bad;
-        *n_kblocks = bad ? 0 : (int32_t)kb_carry;
-    }
-    if (bad) return;
-    const SeqDims d = seq_dims(cu, b, Br, Bc, S);
-    if (threadIdx.x == 0) sl_off[b] = (int32_t)slot_base;
-    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
-    // extrema of this sequence's key blocks: one wave per block
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const bool in_lds = d.Tc <= TILES_LDS_KB;
-    if (Bc <= 64) {
-        // one column per lane; the loads of 8 key blocks are in flight at once
-        constexpr int BATCH = 8;
-        for (int kb0 = wid; kb0 < d.Tc; kb0 += nw * BATCH) {
-            Vec4 f[BATCH];
-#pragma unroll
-            for (int j = 0; j < BATCH; ++j) {
-                const int kb = kb0 + j * nw;
-                const int64_t col = (int64_t)d.s + (int64_t)kb * Bc + lane;
-                const bool ok = kb < d.Tc && lane < Bc && col < d.e;
-                f[j] = ok ? fill_column(sv, n_vec, causal, N, col) : Vec4{INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-            }
-#pragma unroll
-            for (int j = 0; j < BATCH; ++j) {
-                const int kb = kb0 + j * nw;
-                if (kb >= d.Tc) break;
-                const int64_t col = (int64_t)d.s + (int64_t)kb * Bc + lane;
-                const bool ok = lane < Bc && col < d.e;
-                const int v4[4] = {f[j].lts, f[j].lte, f[j].uts, f[j].ute};
-                int outv = 0;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int a = wave_min(ok ? v4[t] : INT_MAX), z = wave_max(ok ? v4[t] : INT_MIN);
-                    if (lane == 2 * t) outv = a;
-                    if (lane == 2 * t + 1) outv = z;
-                }
-                if (lane < 8) {
-                    ext[(kb_base + kb) * 8 + lane] = outv;
-                    if (in_lds) ((int*)s_ext)[kb * 8 + lane] = outv;
-                }
-            }
-        }
-    } else {
-        for (int kb = wid; kb < d.Tc; kb += nw) {
-            const int64_t c0 = (int64_t)d.s + (int64_t)kb * Bc, c1 = min(c0 + Bc, (int64_t)d.e);
-            const int v = block_extrema(sv, n_vec, causal, N, c0, c1, lane);
-            if (lane < 8) {
-                ext[(kb_base + kb) * 8 + lane] = v;
-                if (in_lds) ((int*)s_ext)[kb * 8 + lane] = v;
-            }
-        }
-    }
-    if (!in_lds) __threadfence();  // long rows are classified from global memory
-    __syncthreads();
-    const int4* xs = in_lds ? s_ext : (const int4*)(ext + kb_base * 8);
-    long long my_cnt[3] = {0, 0, 0};
-    classify_rows(d, b, Br, Bc, S, causal, xs, slots, slot_base, slot_cap, map_base, tile_class,
-                  tile_class_cap, my_cnt);
-#pragma unroll
-    for (int c = 0; c < 3; ++c) {
-        const long long t = wave_sum64(my_cnt[c]);
-        if (lane == 0) atomicAdd((unsigned long long*)&s_cnt[c], (unsigned long long)t);
-    }
-    __syncthreads();
-    if (threadIdx.x < 3) seq_counts[(int64_t)b * 3 + threadIdx.x] = s_cnt[threadIdx.x];
+    if (threadIdx.x < 3) cnt_out[threadIdx.x] = s_cnt[threadIdx.x];
 }
 
 // N3b: one workgroup.  Stable counting sort of the valid slots by
@@ -397,8 +289,10 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
         if (b < B) {
             const SeqDims d = seq_dims(cu, b, Br, Bc, S);
             ns = (long long)d.Tr * d.MS;
-            for (int c = 0; c < 3; ++c)
-                atomicAdd((unsigned long long*)&s_sum[c], (unsigned long long)seq_counts[(int64_t)b * 3 + c]);
+            for (int r = 0; r < PLAN_RC; ++r)
+                for (int c = 0; c < 3; ++c)
+                    atomicAdd((unsigned long long*)&s_sum[c],
+                              (unsigned long long)seq_counts[((int64_t)b * PLAN_RC + r) * 3 + c]);
         }
         long long tot;
         block_exclusive_scan(ns, tmp, &tot);
@@ -527,22 +421,10 @@ hipError_t launch_extrema(const int32_t* sv, int n_vec, int causal, const int32_
 }
 
 hipError_t launch_plan(const int32_t* sv, int n_vec, int32_t* ext, int64_t ext_cap, int32_t* n_kblocks,
-                       int32_t* kb_off_out, const PlanPtrs& p, hipStream_t s) {
-    int32_t* slots = (int32_t*)(p.scratch + p.sl.off_slots);
-    int32_t* pos = (int32_t*)(p.scratch + p.sl.off_pos);
-    long long* seq_counts = (long long*)(p.scratch + p.sl.off_seq_counts);
-    int32_t* sl_off = (int32_t*)(p.scratch + p.sl.off_sl_off);
-    hipLaunchKernelGGL(fm_seqplan_kernel, dim3(p.B), dim3(TILES_NTH), 0, s, sv, n_vec, p.causal, p.cu, p.B,
-                       p.N, p.Br, p.Bc, p.S, ext_cap, p.sl.slot_cap, kb_off_out, ext, p.status_rw, n_kblocks,
-                       slots, seq_counts, sl_off, p.tile_class, p.tile_class_cap);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const size_t lds = (size_t)(((p.cost_cap + 4) & ~3) + SORT_LDS_INTS) * sizeof(int32_t);
-    hipLaunchKernelGGL(fm_sort_kernel, dim3(1), dim3(1024), lds, s, p.cu, p.B, p.H, p.Br, p.Bc,
-                       p.S, p.cost_cap, p.kb_off, p.status, p.status_rw, slots, pos, seq_counts, p.items,
-                       p.items_cap, p.n_items, (long long*)p.class_counts, p.sched_counter,
-                       p.n_slots, p.sl.slot_cap, p.merge_list, p.n_merge);
-    return hipGetLastError();
+                       int32_t* kb_off_out, const PlanPtrs& p, int n_cu, hipStream_t s) {
+    const hipError_t e = launch_extrema(sv, n_vec, p.causal, p.cu, p.B, p.N, p.Bc, kb_off_out, ext, ext_cap,
+                                        n_kblocks, p.status_rw, n_cu, s);
+    return e != hipSuccess ? e : launch_worklist(p, s);
 }
 
 hipError_t launch_worklist(const PlanPtrs& p, hipStream_t s) {
@@ -550,7 +432,7 @@ hipError_t launch_worklist(const PlanPtrs& p, hipStream_t s) {
     int32_t* pos = (int32_t*)(p.scratch + p.sl.off_pos);
     long long* seq_counts = (long long*)(p.scratch + p.sl.off_seq_counts);
     int32_t* sl_off = (int32_t*)(p.scratch + p.sl.off_sl_off);
-    hipLaunchKernelGGL(fm_tiles_kernel, dim3(p.B), dim3(TILES_NTH), 0, s, p.cu, p.B, p.Br, p.Bc, p.S,
+    hipLaunchKernelGGL(fm_tiles_kernel, dim3((unsigned)p.B * PLAN_RC), dim3(TILES_NTH), 0, s, p.cu, p.B, p.Br, p.Bc, p.S,
                        p.causal, p.kb_off, p.extrema, p.status, slots, seq_counts, sl_off,
                        p.tile_class, p.tile_class_cap, p.sl.slot_cap);
     hipError_t e = hipGetLastError();
