@@ -261,6 +261,7 @@ __global__ __launch_bounds__(TILES_NTH) void fm_tiles_kernel(
 // scatter when they fit.
 constexpr int SORT_LDS_INTS = 16384;            // 64 KB: slot records (<= 2048) or slot costs
 constexpr int SORT_LDS_RECS = SORT_LDS_INTS / SLOT_WORDS;
+constexpr int SORT_POS_LDS = 4096;              // 16 KB: rank of each slot
 
 __global__ __launch_bounds__(1024) void fm_sort_kernel(
     const int32_t* __restrict__ cu, int B, int H, int Br, int Bc, int S, int cost_cap,
@@ -271,8 +272,9 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
     int32_t* __restrict__ n_items, long long* __restrict__ class_counts,
     int32_t* __restrict__ sched_counter, int32_t* __restrict__ n_slots_out, int64_t slot_cap,
     int32_t* __restrict__ merge_list, int32_t* __restrict__ n_merge) {
-    extern __shared__ int32_t hist[];  // [cost_cap + 1], then SORT_LDS_INTS of slot data
+    extern __shared__ int32_t hist[];  // [cost_cap + 1], SORT_LDS_INTS of slot data, SORT_POS_LDS ranks
     int32_t* s_slot = hist + ((cost_cap + 4) & ~3);
+    int32_t* s_pos = s_slot + SORT_LDS_INTS;
     __shared__ long long tmp[17];
     __shared__ long long s_sum[4];
     __shared__ int s_nmerge;
@@ -311,6 +313,7 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
     if (n_slots > slot_cap) n_slots = 0;  // cannot happen with a valid plan; no items then
     const bool recs_in_lds = n_slots <= SORT_LDS_RECS;
     const bool cost_in_lds = !recs_in_lds && n_slots <= SORT_LDS_INTS;
+    const bool pos_in_lds = n_slots <= SORT_POS_LDS;
     for (int c = tid; c <= cost_cap; c += blockDim.x) hist[c] = 0;
     if (recs_in_lds)
         for (long long i = tid; i < n_slots * (SLOT_WORDS / 4); i += blockDim.x)
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
             if (valid) {
                 const int before = __popcll(eq & lanemask_lt());
                 const int rk = hist[cost] + before;
-                pos[sl] = rk;
+                if (pos_in_lds) s_pos[sl] = rk; else pos[sl] = rk;
                 const bool leader = (eq >> lane) == 1ull;  // highest lane of its group
                 __builtin_amdgcn_wave_barrier();
                 if (leader) hist[cost] = rk + 1;
@@ -374,24 +377,47 @@ __global__ __launch_bounds__(1024) void fm_sort_kernel(
     }
     __syncthreads();
     if (!overflow) {
-        for (long long idx = tid; idx < n_slots * H; idx += blockDim.x) {
-            const long long sl = idx / H;
-            const int h = (int)(idx - sl * H);
-            const int32_t* rec = recs_in_lds ? s_slot + sl * SLOT_WORDS : slots + sl * SLOT_WORDS;
-            if (!rec[7]) continue;
-            int32_t* it = items + ((int64_t)pos[sl] * H + h) * ITEM_WORDS;
-            const int b = rec[0];
-            it[0] = b; it[1] = h; it[2] = rec[1]; it[3] = rec[4];
-            it[4] = rec[5]; it[5] = rec[2]; it[6] = rec[3]; it[7] = rec[6];
-            // derived words: sequence bounds, first extrema block, slot of split 0
-            it[8] = cu[b]; it[9] = cu[b + 1]; it[10] = kb_off[b]; it[11] = (int32_t)(sl - rec[2]);
-            it[12] = it[13] = it[14] = it[15] = 0;
-            if (merge_list && rec[2] == 0 && rec[3] > 1) {   // split 0 of a split row: one merge entry per head
-                const int k = atomicAdd(&s_nmerge, 1);
-                int32_t* m = merge_list + (int64_t)k * MERGE_WORDS;
-                const int row0 = cu[b] + rec[1] * Br;
-                m[0] = it[11]; m[1] = h; m[2] = row0; m[3] = min(row0 + Br, cu[b + 1]); m[4] = rec[3];
-                m[5] = m[6] = m[7] = 0;
+        // every thread gathers the words of U items (ranks from LDS, sequence
+        // bounds from global memory, all loads in flight together), then
+        // writes them as 16-byte stores
+        constexpr int U = 4;
+        const long long total = n_slots * H;
+        for (long long i0 = tid; i0 < total; i0 += (long long)U * blockDim.x) {
+            int4 v0[U], v1[U], v2[U];
+            int64_t dst[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const long long idx = i0 + (long long)u * blockDim.x;
+                ok[u] = false;
+                if (idx < total) {
+                    const long long sl = idx / H;
+                    const int h = (int)(idx - sl * H);
+                    const int32_t* rec = recs_in_lds ? s_slot + sl * SLOT_WORDS : slots + sl * SLOT_WORDS;
+                    if (rec[7]) {
+                        ok[u] = true;
+                        const int b = rec[0];
+                        dst[u] = ((int64_t)(pos_in_lds ? s_pos[sl] : pos[sl]) * H + h) * ITEM_WORDS;
+                        // seq, head, q tile, kb range, split index, splits, cost; then the
+                        // derived words: sequence bounds, first extrema block, slot of split 0
+                        v0[u] = int4{b, h, rec[1], rec[4]};
+                        v1[u] = int4{rec[5], rec[2], rec[3], rec[6]};
+                        v2[u] = int4{cu[b], cu[b + 1], kb_off[b], (int32_t)(sl - rec[2])};
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!ok[u]) continue;
+                int4* it = (int4*)(items + dst[u]);
+                it[0] = v0[u]; it[1] = v1[u]; it[2] = v2[u]; it[3] = int4{0, 0, 0, 0};
+                if (merge_list && v1[u].y == 0 && v1[u].z > 1) {   // split 0 of a split row: one entry per head
+                    const int k = atomicAdd(&s_nmerge, 1);
+                    int32_t* m = merge_list + (int64_t)k * MERGE_WORDS;
+                    const int row0 = v2[u].x + v0[u].z * Br;
+                    m[0] = v2[u].w; m[1] = v0[u].y; m[2] = row0; m[3] = min(row0 + Br, v2[u].y); m[4] = v1[u].z;
+                    m[5] = m[6] = m[7] = 0;
+                }
             }
         }
     }
@@ -437,7 +463,7 @@ hipError_t launch_worklist(const PlanPtrs& p, hipStream_t s) {
                        p.tile_class, p.tile_class_cap, p.sl.slot_cap);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = (size_t)(((p.cost_cap + 4) & ~3) + SORT_LDS_INTS) * sizeof(int32_t);
+    const size_t lds = (size_t)(((p.cost_cap + 4) & ~3) + SORT_LDS_INTS + SORT_POS_LDS) * sizeof(int32_t);
     hipLaunchKernelGGL(fm_sort_kernel, dim3(1), dim3(1024), lds, s, p.cu, p.B, p.H, p.Br, p.Bc,
                        p.S, p.cost_cap, p.kb_off, p.status, p.status_rw, slots, pos, seq_counts, p.items,
                        p.items_cap, p.n_items, (long long*)p.class_counts, p.sched_counter,
