@@ -120,6 +120,15 @@ __device__ __attribute__((always_inline)) inline void wait_vm() {
     __builtin_amdgcn_s_waitcnt(0xF70 | N);
 }
 
+// Barrier between items: this wave's LDS operations are complete, its
+// global stores may still be in flight (nothing after reads them).
+__device__ __attribute__((always_inline)) inline void item_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroup barrier between phases.  No implied wait: every wave has already
 // waited for the copies the next phase reads, and LDS reads of a phase are
 // consumed (hence complete) inside it.  The memory clobber and scheduling
@@ -746,6 +755,10 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
         }
         pv_part(vbuf(sl.u2), pb, st, lane);
     }
+    // copies past the item's last tile may still be in flight: drain them
+    // here, before the output stores, so that the next item can refill the
+    // ring without waiting for the stores to reach memory
+    wait_vm<0>();
     epilogue(a, Wv, I, st);
 }
 
@@ -779,10 +792,9 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
             nxt = __builtin_amdgcn_readfirstlane(nxt);
             if (nxt < n_items && lane < ITEM_WORDS) nrec = a.items[(int64_t)nxt * ITEM_WORDS + lane];
         }
-        // copies past the item's last tile may still be in flight: drain them
-        // before the next item refills the ring
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // every wave is done with s_rec, the visit list and the LDS buffers
+        // the ring copies were drained before the epilogue; the output stores
+        // need no wait
+        item_barrier();   // every wave is done with s_rec, the visit list and the LDS buffers
         if (w == 0) {
             nxt = __builtin_amdgcn_readfirstlane(nxt);
             if (nxt == last_fetch && lane == 0) atomicExch(a.sched_counter, 0);
@@ -814,8 +826,7 @@ __global__ __launch_bounds__(NTH, 2) void fm_fused_bf16_kernel(AttnArgs a) {
         const Item I = item_of(a, s_myrec[k]);
         const int vis_off = __builtin_amdgcn_readfirstlane(s_myrec[k][12]);
         run_item<false>(a, Wv, I, vis_off, rec_pending, 0, nrec, P.n_items);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // the ring is free for the next item
+        item_barrier();   // the ring is free for the next item
     }
     __builtin_amdgcn_s_waitcnt(0);
 }
