@@ -465,11 +465,11 @@ __device__ __attribute__((always_inline)) inline float softmax_tile(const AttnAr
 template <int G>
 __device__ __attribute__((always_inline)) inline void kv_step(
     const AttnArgs& a, const Item& I, Queue& Qu, const Wave& Wv, Slots& sl, int j, int T, bool& rec_pending,
-    int nxt, int& nrec, int n_items, const bf16x8 (&qf)[8], f32x16 (&sacc)[2], bf16x8 (&pb)[2][2],
+    int fv, int& nrec, int n_items, const bf16x8 (&qf)[8], f32x16 (&sacc)[2], bf16x8 (&pb)[2][2],
     State& st, const char* Kh, const char* Vh, const uint16_t* vis) {
     const int nk_raw = vis[min(j + 4, T - 1)];
     if (rec_pending) {   // wave 0: the next item's record, ahead of this step's copies
-        const int nx = __builtin_amdgcn_readfirstlane(nxt);
+        const int nx = (int)gridDim.x + __builtin_amdgcn_readfirstlane(fv);   // fetch value -> item
         if (nx < n_items && Wv.lane < ITEM_WORDS) nrec = a.items[(int64_t)nx * ITEM_WORDS + Wv.lane];
         rec_pending = false;
     }
@@ -569,15 +569,32 @@ __device__ __attribute__((always_inline)) inline Item item_of(const AttnArgs& a,
 // ---- epilogue -----------------------------------------------------------
 // bf16 row of out and its lse from an unnormalised O (per lane: query row
 // `qrow`, channels 32dt + 8g + 4hh + 0..3 of o[dt][4g .. 4g+3]).
-__device__ __attribute__((always_inline)) inline void write_row(const AttnArgs& a, const Wave& Wv, const Item& I,
-                                                                const f32x16& o, int dt, float inv) {
-    uint16_t* op = (uint16_t*)a.out + (int64_t)Wv.qrow * ((int64_t)a.H * HD) + I.hoff + 4 * Wv.hh;
+// Output rows of a finished item, through LDS: every wave writes its 32
+// rows of O / l (bf16) into its own 8.5 KB of the free K/V ring (rows of
+// 272 B: 16 bf16 groups of 8 B per lane land in distinct banks), then reads
+// them back 16 B per lane and writes 4 whole rows per store instruction
+// (1 KB, 256 B per row) instead of 16 scattered 8-byte pieces per lane.
+constexpr int OST_ROW = 272, OST_WAVE = 32 * OST_ROW;
+static_assert(NW * OST_WAVE <= 6 * 20 * 1024, "output staging fits in the ring");
+__device__ __attribute__((always_inline)) inline void write_rows(const AttnArgs& a, const Wave& Wv, const Item& I,
+                                                                 const State& st, float inv) {
+    char* stg = s_kv + Wv.w * OST_WAVE;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        u32x2 wv;
-        wv.x = bf16_bits(o[4 * g] * inv) | (bf16_bits(o[4 * g + 1] * inv) << 16);
-        wv.y = bf16_bits(o[4 * g + 2] * inv) | (bf16_bits(o[4 * g + 3] * inv) << 16);
-        *(u32x2*)(op + 32 * dt + 8 * g) = wv;
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 wv;
+            wv.x = bf16_bits(st.o[dt][4 * g] * inv) | (bf16_bits(st.o[dt][4 * g + 1] * inv) << 16);
+            wv.y = bf16_bits(st.o[dt][4 * g + 2] * inv) | (bf16_bits(st.o[dt][4 * g + 3] * inv) << 16);
+            *(u32x2*)(stg + Wv.n * OST_ROW + 2 * (32 * dt + 8 * g + 4 * Wv.hh)) = wv;
+        }
+    const int64_t rs = (int64_t)a.H * HD;   // row stride of out (elements)
+    const int q0 = I.r0 + 32 * Wv.w;       // the wave's first row
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (Wv.lane >> 4), c = Wv.lane & 15;   // row, 16-byte chunk
+        const u32x4 v = *(const u32x4*)(stg + r * OST_ROW + 16 * c);
+        if (q0 + r < I.r1) *(u32x4*)((uint16_t*)a.out + (int64_t)(q0 + r) * rs + I.hoff + 8 * c) = v;
     }
 }
 __device__ __attribute__((always_inline)) inline void write_lse(const AttnArgs& a, const Wave& Wv, const Item& I,
@@ -598,12 +615,12 @@ __device__ __attribute__((always_inline)) inline int part_index(int w, int dt, i
 __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a, const Wave& Wv, const Item& I,
                                                                const State& st) {
     if (I.nsp <= 1) {
-        if (Wv.qrow < I.r1) {
-            const float l = st.l_run, inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) write_row(a, Wv, I, st.o[dt], dt, inv);
-            write_lse(a, Wv, I, st.m_run, l);
-        }
+        // every wave is past its last ring read and its copies are drained:
+        // the ring is free for the output staging
+        phase_barrier();
+        const float l = st.l_run, inv = l > 0.f ? 1.f / l : 0.f;
+        write_rows(a, Wv, I, st, inv);
+        if (Wv.qrow < I.r1) write_lse(a, Wv, I, st.m_run, l);
         return;
     }
     float* po = a.partial + ((int64_t)(I.slot0 + I.sidx) * a.H + I.h) * PART;
@@ -625,7 +642,7 @@ __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a
 // in s_vis at `vis_off` (fused path).
 template <bool STD>
 __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a, Wave& Wv, const Item& I,
-                                                               int vis_off, bool& rec_pending, int nxt, int& nrec,
+                                                               int vis_off, bool& rec_pending, int fv, int& nrec,
                                                                int n_items) {
     const int tid = Wv.tid, lane = Wv.lane, w = Wv.w;
     const int64_t rs = (int64_t)a.H * HD;
@@ -735,10 +752,10 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
         Qu.kp = Qu.k0;
         if (Wv.g == 0)
             for (int j = 0; j < T; ++j)
-                kv_step<0>(a, I, Qu, Wv, sl, j, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
+                kv_step<0>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
         else
             for (int j = 0; j < T; ++j)
-                kv_step<1>(a, I, Qu, Wv, sl, j, T, rec_pending, nxt, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
+                kv_step<1>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
         // the last tile (V_{T-1} sits in slot u2 now): group 1 still owes its
         // softmax; then O += V_{T-1} P_{T-1}
         if (Wv.g == 1) {
@@ -783,13 +800,15 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
     if (it < n_items && tid < ITEM_WORDS) s_rec[tid] = a.items[(int64_t)it * ITEM_WORDS + tid];
     __syncthreads();
     while (it < n_items) {
-        int nxt = 0, nrec = 0;
-        if (tid == 0) nxt = G + atomicAdd(a.sched_counter, 1);
+        // the fetch value is only needed when the next record is read: no
+        // arithmetic on it here, so nothing waits for the atomic's return
+        int fv = 0, nrec = 0;
+        if (tid == 0) fv = atomicAdd(a.sched_counter, 1);
         const Item I = item_of(a, s_rec);
         bool rec_pending = (w == 0);
-        run_item<true>(a, Wv, I, 0, rec_pending, nxt, nrec, n_items);
+        run_item<true>(a, Wv, I, 0, rec_pending, fv, nrec, n_items);
+        int nxt = G + __builtin_amdgcn_readfirstlane(fv);
         if (rec_pending) {
-            nxt = __builtin_amdgcn_readfirstlane(nxt);
             if (nxt < n_items && lane < ITEM_WORDS) nrec = a.items[(int64_t)nxt * ITEM_WORDS + lane];
         }
         // the ring copies were drained before the epilogue; the output stores
