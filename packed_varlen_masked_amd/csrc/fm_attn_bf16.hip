@@ -651,8 +651,20 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
     const char* Vh = (const char*)a.v + I.hoff * 2;
     const int lo = Wv.no_skip ? 0 : I.kbb, hi = Wv.no_skip ? I.Tc : I.kbe;
 
-    // Q fragments and the first tile (kb_begin is visited by construction
-    // of the work list) go out before the visit list is read
+    // loads in the order they are needed (they complete in issue order): the
+    // block extrema of the wave's first visit window, the first K/V tile
+    // (kb_begin is visited by construction of the work list), then Q, which
+    // the loop needs last
+    const int nwin = (STD && lo < hi) ? ceil_div(hi - lo, 64) : 0;
+    u32x4 xw0 = {0, 0, 0, 0}, xw1 = {0, 0, 0, 0};
+    if constexpr (STD) {
+        const int kb = lo + 64 * w + lane;
+        if (w < nwin && kb < hi) {
+            xw0 = *(const u32x4*)(I.xb + (int64_t)kb * 8);
+            xw1 = *(const u32x4*)(I.xb + (int64_t)kb * 8 + 4);
+        }
+    }
+    if (!Wv.no_skip && lo < hi) copy_tile_pair(a, I, Wv, Kh, Vh, lo);
     bf16x8 qf[8];   // Q^T fragments (B operand): lane holds query n, channels 16s+8hh..+7
     if (Wv.qrow < I.r1) {
         const uint16_t* qp = (const uint16_t*)a.q + (int64_t)Wv.qrow * rs + I.hoff + 8 * Wv.hh;
@@ -662,20 +674,18 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
-    if (!Wv.no_skip && lo < hi) copy_tile_pair(a, I, Wv, Kh, Vh, lo);
 
     int T;
     const uint16_t* vis;
     if constexpr (STD) {
         // windows of 64 key blocks, one extrema row per lane; wave w takes
         // windows w, w+8, ...
-        const int nwin = lo < hi ? ceil_div(hi - lo, 64) : 0;
         for (int j = w; j < nwin; j += NW) {
             const int kb = lo + 64 * j + lane;
             bool v = false, iv = false;
             if (kb < hi) {
-                const u32x4 x0 = *(const u32x4*)(I.xb + (int64_t)kb * 8);
-                const u32x4 x1 = *(const u32x4*)(I.xb + (int64_t)kb * 8 + 4);
+                const u32x4 x0 = j == w ? xw0 : *(const u32x4*)(I.xb + (int64_t)kb * 8);
+                const u32x4 x1 = j == w ? xw1 : *(const u32x4*)(I.xb + (int64_t)kb * 8 + 4);
                 const int x[8] = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                                   (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
                 const int c0 = I.s_b + kb * BC, c1 = min(c0 + BC, I.e_b);

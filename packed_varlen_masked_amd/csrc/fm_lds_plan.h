@@ -322,6 +322,45 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
         }
         return LdsPlan{FM_STATUS_CAP, 0, 0};
     }
+    // ---- one item per workgroup: when the writer has no item
+    // (n_valid * H <= gridDim.x - 1), the longest-first order cannot change
+    // the schedule (every item starts at once), so a workgroup takes the
+    // (g / H)-th filled slot in slot order, head g % H, and skips the sort.
+    // The writer still sorts and writes the plan. ----
+    if (!writer && (long long)n_valid * H <= (long long)gridDim.x - 1) {
+        const int k = (int)blockIdx.x / H, h = (int)blockIdx.x - k * H;
+        if (k >= n_valid) return LdsPlan{0, n_valid * H, 0};
+        if (wid == 0) {
+            int base = 0, slot = -1;
+            for (int c0 = 0; c0 < n_std && slot < 0; c0 += 64) {
+                const int i = c0 + lane;
+                const bool f = i < n_std && t_key[i] != ~0ull;
+                const uint64_t m = __ballot(f);
+                const int r = base + __popcll(m & lanemask_lt());
+                const uint64_t hit = __ballot(f && r == k);
+                if (hit) slot = c0 + __builtin_ctzll(hit);
+                base += __popcll(m);
+            }
+            if (lane < ITEM_WORDS) {
+                const int4 si = t_sinfo[slot];
+                const int b = si.x >> 16, qt = si.x & 0xffff, sp = si.y & 0xffff, n = si.y >> 16;
+                const int start = si.z, size = si.w;
+                const int s_b = t_cu[b], e_b = t_cu[b + 1];
+                const int Tc = ceil_div(e_b - s_b, Bc);
+                const int vb = t_tileoff[b] + qt * Tc + start;
+                const int w = lane;
+                myrec[0][w] = w == 0 ? b : w == 1 ? h : w == 2 ? qt
+                            : w == 3 ? (size ? (int)(vis[vb] & 0x7fff) : 0)
+                            : w == 4 ? (size ? (int)(vis[vb + size - 1] & 0x7fff) + 1 : 0)
+                            : w == 5 ? sp : w == 6 ? n : w == 7 ? size : w == 8 ? s_b : w == 9 ? e_b
+                            : w == 10 ? t_kboff[b]
+                            : w == 11 ? t_slotbase[b] + qt * ((S > 0 && Tc > 0) ? ceil_div(Tc, S) : 1)
+                            : w == 12 ? vb : 0;
+            }
+        }
+        __syncthreads();
+        return LdsPlan{0, n_valid * H, 1};
+    }
     // ---- rank of every filled slot: the number of smaller keys, counted by
     // `parts` threads per slot over disjoint ranges ----
     {
