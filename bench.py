@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on oracle CPU time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--preprocess-sweep", action="store_true",
+                    help="instead of the step: time the block-extrema pass alone for N = 2^16 .. 2^26 "
+                         "(n_vec = 4, non-causal) and report its achieved HBM GB/s")
     return ap.parse_args()
 
 
@@ -116,8 +119,61 @@ def cpu_baseline(w, flops, budget_s):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def preprocess_sweep(args):
+    """Block-extrema pass (fm_preprocess_mask) alone: synthetic int32 mask
+    vectors [4, N] (uniform in [0, N)), documents of 2^20 tokens (one when N
+    is smaller), Bc = 64.  Algorithmic bytes: the vectors read once
+    (16 B per token), cu_seqlens read, kb_off and the extrema (32 B per key
+    block) written.  Time: K calls between HIP events after W warm-up calls."""
+    import torch
+    import packed_varlen_masked_amd as pv
+    dev = torch.device("cuda:0")
+    n_vec, Bc, K = 4, 64, max(args.steps, 10)
+    rows = []
+    for lg in range(16, 27, 2):
+        N = 1 << lg
+        B = max(1, N >> 20)
+        cu = (torch.arange(B + 1, dtype=torch.int64, device=dev) * (N // B)).to(torch.int32)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + lg)
+        sv = torch.randint(0, N, (n_vec, N), dtype=torch.int32, device=dev, generator=g)
+        cap = -(-N // Bc) + B
+        kb_off = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        ext = torch.empty(cap, 8, dtype=torch.int32, device=dev)
+        scal = torch.zeros(2, dtype=torch.int32, device=dev)
+
+        def call():
+            pv._check(pv._lib.fm_preprocess_mask(pv._ptr(sv), n_vec, 0, pv._ptr(cu), B, N, Bc, pv._ptr(kb_off),
+                                                 pv._ptr(ext), cap, pv._ptr(scal[0:1]),
+                                                 __import__("ctypes").c_void_p(scal.data_ptr() + 4), pv._stream()))
+        for _ in range(max(args.warmup, 3)):
+            call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        nkb, status = (int(x) for x in scal.cpu())
+        assert status == 0 and nkb == -(-N // Bc), (status, nkb)
+        us = e0.elapsed_time(e1) / K * 1e3
+        nbytes = 4 * n_vec * N + 4 * (B + 1) + 4 * (B + 1) + 32 * nkb
+        rows.append({"N": N, "B": B, "key_blocks": nkb, "us": round(us, 3), "algorithmic_bytes": nbytes,
+                     "GB_per_s": round(nbytes / us / 1e3, 1), "frac_of_8TB_s": round(nbytes / us / 1e3 / 8000.0, 4)})
+        del sv, ext
+    print(json.dumps({"metric": "block-extrema pass (fm_preprocess_mask) achieved HBM GB/s", "unit": "GB/s",
+                      "higher_is_better": True, "n_vec": n_vec, "causal": False, "block_k": Bc, "calls_timed": K,
+                      "peak_GB_per_s": 8000.0, "data": "synthetic (uniform random int32 mask vectors)",
+                      "sweep": rows}), flush=True)
+
+
 def main():
     args = parse()
+    if args.preprocess_sweep:
+        preprocess_sweep(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)

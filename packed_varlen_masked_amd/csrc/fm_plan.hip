@@ -15,9 +15,10 @@ namespace fm {
 // Per-workgroup scan of the key-block counts of all sequences into LDS.
 // Every workgroup of the extrema kernel repeats it (B is small next to N),
 // which removes a launch and a grid-wide dependency.  Also validates cu.
-// Returns the status bits (0 = valid) and leaves s_off[0..B] filled.
+// Returns the status bits (0 = valid) and leaves s_off[0..B] filled, and
+// s_cu[0..B] = cu[0..B].
 __device__ int scan_kblocks(const int32_t* __restrict__ cu, int B, int64_t N, int Bc,
-                            int64_t cap, int32_t* s_off, long long* tmp) {
+                            int64_t cap, int32_t* s_off, int32_t* s_cu, long long* tmp) {
     __shared__ int s_bad;
     if (threadIdx.x == 0) s_bad = (cu[0] != 0 ? FM_STATUS_CU0 : 0) | (cu[B] != (int)N ? FM_STATUS_CUN : 0);
     __syncthreads();
@@ -26,9 +27,11 @@ __device__ int scan_kblocks(const int32_t* __restrict__ cu, int B, int64_t N, in
         const int b = base + threadIdx.x;
         long long tc = 0;
         if (b < B) {
-            const int L = cu[b + 1] - cu[b];
+            const int c = cu[b];
+            const int L = cu[b + 1] - c;
             if (L < 0) atomicOr(&s_bad, FM_STATUS_ORDER);
             tc = L > 0 ? ceil_div(L, Bc) : 0;
+            s_cu[b] = c;
         }
         long long tot;
         const long long ex = block_exclusive_scan(tc, tmp, &tot);
@@ -36,6 +39,7 @@ __device__ int scan_kblocks(const int32_t* __restrict__ cu, int B, int64_t N, in
         carry += tot;
     }
     if (threadIdx.x == 0) {
+        s_cu[B] = cu[B];
         s_off[B] = (int32_t)min(carry, (long long)INT_MAX);
         if (carry > cap) atomicOr(&s_bad, FM_STATUS_CAP);
     }
@@ -66,16 +70,18 @@ __device__ inline int block_extrema(const int32_t* __restrict__ sv, int n_vec, i
     return outv;
 }
 
-// N2: one wave per key block, grid-stride over the global key blocks.
-// Lanes read consecutive columns (coalesced 256 B per vector per wave) and
-// reduce min/max across the wave.
+// N2: grid-stride over the global key blocks.  For Bc <= 64 a wave takes
+// four blocks at a time (16 lanes each, four columns per lane: coalesced,
+// and the min / max reductions stay inside a row of 16 lanes); larger blocks
+// take one wave each.
 __global__ __launch_bounds__(256) void fm_extrema_kernel(
     const int32_t* __restrict__ sv, int n_vec, int causal, const int32_t* __restrict__ cu,
     int B, int64_t N, int Bc, int32_t* __restrict__ kb_off, int32_t* __restrict__ ext,
     int64_t ext_cap, int32_t* __restrict__ n_kblocks, int32_t* __restrict__ status) {
-    extern __shared__ int32_t s_off[];  // [B+1]
+    extern __shared__ int32_t s_off[];  // [B+1] key-block offsets, then [B+1] cu
+    int32_t* s_cu = s_off + B + 1;
     __shared__ long long tmp[17];
-    const int bad = scan_kblocks(cu, B, N, Bc, ext_cap, s_off, tmp);
+    const int bad = scan_kblocks(cu, B, N, Bc, ext_cap, s_off, s_cu, tmp);
     if (blockIdx.x == 0) {
         for (int b = threadIdx.x; b <= B; b += blockDim.x) kb_off[b] = bad ? 0 : s_off[b];
         if (threadIdx.x == 0) { *status = bad; *n_kblocks = bad ? 0 : s_off[B]; }
@@ -84,18 +90,74 @@ __global__ __launch_bounds__(256) void fm_extrema_kernel(
     const int total = s_off[B];
     const int lane = threadIdx.x & 63;
     const int waves = blockDim.x >> 6;
-    for (int g = blockIdx.x * waves + (threadIdx.x >> 6); g < total; g += gridDim.x * waves) {
-        // sequence owning global key block g: last b with s_off[b] <= g
+    const int stride = gridDim.x * waves;
+    // column range of global key block g: sequence = last b with s_off[b] <= g
+    auto block_cols = [&](int g, int64_t& c0, int64_t& c1) {
         int lo = 0, hi = B;  // s_off[lo] <= g < s_off[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (s_off[mid] <= g) lo = mid; else hi = mid;
         }
-        const int b = lo;
-        const int64_t c0 = (int64_t)cu[b] + (int64_t)(g - s_off[b]) * Bc;
-        const int64_t c1 = min(c0 + Bc, (int64_t)cu[b + 1]);
-        const int outv = block_extrema(sv, n_vec, causal, N, c0, c1, lane);
-        if (lane < 8) ext[(int64_t)g * 8 + lane] = outv;
+        c0 = (int64_t)s_cu[lo] + (int64_t)(g - s_off[lo]) * Bc;
+        c1 = min(c0 + Bc, (int64_t)s_cu[lo + 1]);
+    };
+    if (Bc <= 64) {
+        // four blocks per wave: lanes 16r .. 16r+15 take block g0 + r, lane q
+        // of the row its columns 4q .. 4q+3 (four loads of 4 B per vector, the
+        // 16 lanes of a row together contiguous); min / max of the four columns
+        // in the lane, then across the row with DPP (every lane of the row
+        // gets the block's value)
+        const int r = lane >> 4, q = lane & 15;
+        auto row_min = [](int v) {
+            v = min(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xf, 0xf, false));    // quad_perm [1,0,3,2]
+            v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xf, 0xf, false));    // quad_perm [2,3,0,1]
+            v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false));   // row_half_mirror
+            return min(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false)); // row_mirror
+        };
+        auto row_max = [](int v) {
+            v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xf, 0xf, false));
+            v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xf, 0xf, false));
+            v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false));
+            return max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false));
+        };
+        const int nwaves = gridDim.x * waves;
+        for (int g0 = 4 * (blockIdx.x * waves + (threadIdx.x >> 6)); g0 < total; g0 += 4 * nwaves) {
+            const int g = g0 + r;
+            int64_t c0 = 0, c1 = 0;
+            if (g < total) block_cols(g, c0, c1);
+            int mn[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX}, mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+            Vec4 f[4];
+            bool ok[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t col = c0 + 4 * q + k;
+                ok[k] = 4 * q + k < Bc && col < c1;
+                if (ok[k]) f[k] = fill_column(sv, n_vec, causal, N, col);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (ok[k]) {
+                    mn[0] = min(mn[0], f[k].lts); mx[0] = max(mx[0], f[k].lts);
+                    mn[1] = min(mn[1], f[k].lte); mx[1] = max(mx[1], f[k].lte);
+                    mn[2] = min(mn[2], f[k].uts); mx[2] = max(mx[2], f[k].uts);
+                    mn[3] = min(mn[3], f[k].ute); mx[3] = max(mx[3], f[k].ute);
+                }
+            int outv = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int a = row_min(mn[t]), z = row_max(mx[t]);
+                if (q == 2 * t) outv = a;
+                if (q == 2 * t + 1) outv = z;
+            }
+            if (g < total && q < 8) ext[(int64_t)g * 8 + q] = outv;
+        }
+    } else {
+        for (int g = blockIdx.x * waves + (threadIdx.x >> 6); g < total; g += stride) {
+            int64_t c0, c1;
+            block_cols(g, c0, c1);
+            const int outv = block_extrema(sv, n_vec, causal, N, c0, c1, lane);
+            if (lane < 8) ext[(int64_t)g * 8 + lane] = outv;
+        }
     }
 }
 
@@ -440,7 +502,7 @@ hipError_t launch_extrema(const int32_t* sv, int n_vec, int causal, const int32_
     const int64_t kb_bound = (N + Bc - 1) / Bc + B;
     int64_t grid = (kb_bound + 3) / 4;
     grid = std::max<int64_t>(1, std::min<int64_t>(grid, (int64_t)n_cu * 8));
-    const size_t lds = (size_t)(B + 1) * sizeof(int32_t);
+    const size_t lds = 2 * (size_t)(B + 1) * sizeof(int32_t);
     hipLaunchKernelGGL(fm_extrema_kernel, dim3((unsigned)grid), dim3(256), lds, s, sv, n_vec,
                        causal, cu, B, N, Bc, kb_off, extrema, extrema_cap, n_kblocks, status);
     return hipGetLastError();
