@@ -121,6 +121,8 @@ __global__ __launch_bounds__(256) void fm_extrema_kernel(
             return max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false));
         };
         const int nwaves = gridDim.x * waves;
+        // 16-byte loads need 16-byte aligned vector rows
+        const bool vec16 = ((uintptr_t)sv & 15) == 0 && (N & 3) == 0;
         for (int g0 = 4 * (blockIdx.x * waves + (threadIdx.x >> 6)); g0 < total; g0 += 4 * nwaves) {
             const int g = g0 + r;
             int64_t c0 = 0, c1 = 0;
@@ -128,11 +130,34 @@ __global__ __launch_bounds__(256) void fm_extrema_kernel(
             int mn[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX}, mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
             Vec4 f[4];
             bool ok[4];
+            const int64_t cq = c0 + 4 * q;   // first column of this lane
+            if (vec16 && (c0 & 3) == 0 && 4 * q + 3 < Bc && cq + 3 < c1) {
+                // the lane's four columns of each stored vector in one 16-byte load
+                int4 x[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int64_t col = c0 + 4 * q + k;
-                ok[k] = 4 * q + k < Bc && col < c1;
-                if (ok[k]) f[k] = fill_column(sv, n_vec, causal, N, col);
+                for (int v = 0; v < 4; ++v)
+                    if (v < n_vec) x[v] = *(const int4*)(sv + (int64_t)v * N + cq);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    auto at = [&](int v) { return k == 0 ? x[v].x : k == 1 ? x[v].y : k == 2 ? x[v].z : x[v].w; };
+                    ok[k] = true;
+                    f[k].lts = at(0);
+                    if (causal) {
+                        f[k].lte = n_vec == 2 ? at(1) : (int)N;
+                        f[k].uts = 0; f[k].ute = 0;
+                    } else if (n_vec == 2) {
+                        f[k].lte = (int)N; f[k].uts = 0; f[k].ute = at(1);
+                    } else {
+                        f[k].lte = at(1); f[k].uts = at(2); f[k].ute = at(3);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int64_t col = cq + k;
+                    ok[k] = 4 * q + k < Bc && col < c1;
+                    if (ok[k]) f[k] = fill_column(sv, n_vec, causal, N, col);
+                }
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k)
