@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on oracle CPU time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--seed", type=int, default=None, help="workload seed (default 1000 + config)")
+    ap.add_argument("--sparsity-sweep", action="store_true",
+                    help="instead of the step: step latency against the unmasked fraction on the varlen shape")
     ap.add_argument("--preprocess-sweep", action="store_true",
                     help="instead of the step: time the block-extrema pass alone for N = 2^16 .. 2^26 "
                          "(n_vec = 4, non-causal) and report its achieved HBM GB/s")
@@ -169,20 +172,11 @@ def preprocess_sweep(args):
                       "sweep": rows}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.preprocess_sweep:
-        preprocess_sweep(args)
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
-        sys.exit(2)
+def make_setup(w, args):
+    """Device inputs, the plan and the step function for workload w."""
     import torch
     import workloads as W
     import packed_varlen_masked_amd as pv
-
-    w = W.make_config(args.config)
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float32
     q = torch.from_numpy(w.q).to(dt).to(dev)
@@ -190,12 +184,6 @@ def main():
     v = torch.from_numpy(w.v).to(dt).to(dev)
     cu = torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(dev)
     sv = torch.from_numpy(np.ascontiguousarray(w.startend.astype(np.int32))).to(dev)
-
-    # algorithmic work: closed form for causal documents, else the oracle's count
-    import oracle as O
-    pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
-    flops = O.effective_flops(pairs, w.H, w.D)
-
     plan = pv.build_plan(cu, sv, w.n_vec, w.causal, w.N, w.H, w.D, dt, max_kb_per_item=args.split)
     out = torch.empty_like(q)
     lse = torch.empty(w.H, w.N, dtype=torch.float32, device=dev)
@@ -204,6 +192,9 @@ def main():
     # planning launches fill the workspace and the attention launch reads it
     fused = pv.fused_path(w.N, w.B, w.H, w.D, dt, w.n_vec, w.causal, S) and not args.planned
     ws = torch.zeros_like(plan.workspace)
+
+    def attn_with_plan():   # the attention launch(es) reading a built plan
+        pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), plan=plan, out=out, lse=lse)
 
     if fused:
         def step(ev_a=None, ev_b=None):
@@ -218,9 +209,97 @@ def main():
             pv.build_plan_into(plan, cu, sv)
             if ev_a is not None:
                 ev_a.record()
-            pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), plan=plan, out=out, lse=lse)
+            attn_with_plan()
             if ev_b is not None:
                 ev_b.record()
+    hdr = (plan if not fused else pv.Plan(ws, plan.layout, w.N, w.B, w.H, w.D, dt, w.causal, w.n_vec, S)).header
+    return dict(dt=dt, dev=dev, step=step, attn_with_plan=attn_with_plan, plan=plan, S=S, fused=fused, hdr=hdr)
+
+
+def spin():
+    """Queue a spin kernel so the host enqueues the timed launches ahead of the GPU."""
+    import torch
+    try:
+        torch.cuda._sleep(int(2e8))
+        return True
+    except Exception:
+        return False
+
+
+def time_calls(fn, K):
+    """Mean ms per call of K back-to-back calls between two HIP events."""
+    import torch
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ahead = spin()
+    th0 = time.perf_counter()
+    t0.record()
+    for _ in range(K):
+        fn()
+    t1.record()
+    host_ms = (time.perf_counter() - th0) * 1e3 / K
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / K, host_ms, ahead
+
+
+def sparsity_sweep(args):
+    """Step time against unmasked work on the shape of the varlen workload
+    (N = 4352, H = 2, D = 128, causal documents): the documents are resized
+    (k equal documents, k = 1 .. 34, plus the [128, 128, 4096] mix), which
+    moves the unmasked fraction 1 - rho of the N x N score matrix; the
+    pages expect latency linear in it."""
+    import workloads as W
+    import oracle as O
+    N = 4352
+    cases = [[N // k] * (k - 1) + [N - (N // k) * (k - 1)] for k in (1, 2, 4, 8, 17, 34)] + [[128, 128, 4096]]
+    rows = []
+    for lens in cases:
+        w = W.document_workload(lens, H=2, D=128, seed=1002)
+        st = make_setup(w, args)
+        for _ in range(args.warmup):
+            st["step"]()
+        ms, _, _ = time_calls(st["step"], args.steps)
+        pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
+        rows.append({"documents": len(lens), "lengths": lens[:4] + (["..."] if len(lens) > 4 else []),
+                     "unmasked_fraction": round(pairs / float(N * N), 5), "unmasked_pairs_per_head": int(pairs),
+                     "path": "fused" if st["fused"] else "planned", "max_kb_per_item": st["S"],
+                     "us_per_step": round(ms * 1e3, 2),
+                     "effective_TFLOP_s": round(O.effective_flops(pairs, w.H, w.D) / (ms * 1e-3) / 1e12, 2)})
+    x = np.array([r["unmasked_fraction"] for r in rows])
+    y = np.array([r["us_per_step"] for r in rows])
+    slope, icpt = np.polyfit(x, y, 1)
+    r2 = 1.0 - float(np.sum((y - (slope * x + icpt)) ** 2)) / float(np.sum((y - y.mean()) ** 2))
+    print(json.dumps({"metric": "step latency against unmasked fraction (varlen workload shape)", "unit": "us",
+                      "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+                      "fit": {"us_per_unit_fraction": round(float(slope), 2), "intercept_us": round(float(icpt), 2),
+                              "r2": round(r2, 4)},
+                      "data": "synthetic (seeded N(0,1) q/k/v)", "sweep": rows}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.preprocess_sweep:
+        preprocess_sweep(args)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.sparsity_sweep:
+        sparsity_sweep(args)
+        return
+    import torch
+    import workloads as W
+
+    w = W.make_config(args.config, seed=args.seed)
+    st = make_setup(w, args)
+    dt, dev, step, plan, S, fused = st["dt"], st["dev"], st["step"], st["plan"], st["S"], st["fused"]
+
+    # algorithmic work: closed form for causal documents, else the oracle's count
+    import oracle as O
+    pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
+    flops = O.effective_flops(pairs, w.H, w.D)
 
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
@@ -233,26 +312,8 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
 
-    def spin():
-        try:
-            torch.cuda._sleep(int(2e8))  # let the host queue all K steps ahead of the GPU
-            return True
-        except Exception:
-            return False
-
     # pass 1: the timed steps
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    host_ahead = spin()
-    th0 = time.perf_counter()
-    t0.record()
-    for i in range(K):
-        step()
-    t1.record()
-    host_ms = (time.perf_counter() - th0) * 1e3 / K
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / K
+    ms_step, host_ms, host_ahead = time_calls(step, K)
     # pass 2: the same steps, events around every attention launch
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -262,10 +323,14 @@ def main():
     torch.cuda.synchronize()
     attn_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
     attn_avg = float(attn_ms.mean())
+    # pass 3: attention alone with the plan already built (a plan reused
+    # across layers that share the mask)
+    st["attn_with_plan"]()
+    ms_reuse, _, _ = time_calls(st["attn_with_plan"], K)
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (attn_avg * 1e-3) / 1e12
 
-    hdr = (plan if not fused else pv.Plan(ws, plan.layout, w.N, w.B, w.H, w.D, dt, w.causal, w.n_vec, S)).header()
+    hdr = st["hdr"]()
     path = "fused" if fused else "planned"
     kernel = ("fm_fused_bf16_kernel" if fused else "fm_attn_bf16_kernel") + (" + fm_merge_bf16_kernel" if S > 0 else "")
     traffic = stored_traffic("%s:%s:S%d" % (w.name, path, S))
@@ -276,7 +341,7 @@ def main():
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if dt == torch.bfloat16 else "f32",
         "data": "synthetic (seeded N(0,1) q/k/v, page-derived lengths and masks)",
-        "config": {"workload": w.name, "N": w.N, "B": w.B, "H": w.H, "D": w.D,
+        "config": {"workload": w.name, "seed": w.meta["seed"], "N": w.N, "B": w.B, "H": w.H, "D": w.D,
                    "lengths": [int(x) for x in w.lengths][:16], "causal": bool(w.causal),
                    "n_vec": w.n_vec, "block_q": plan.layout.block_q, "block_k": plan.layout.block_k,
                    "max_kb_per_item": S, "n_items": hdr["n_items"],
@@ -292,6 +357,10 @@ def main():
                      "algorithmic_bytes": int(algo_bytes),
                      "avg_launch_ms": round(attn_avg, 6),
                      "p10_p50_p90_ms": [round(float(x), 6) for x in np.percentile(attn_ms, [10, 50, 90])]},
+        "reused_plan": {"what": "attention launches alone, plan built once (fm_attn_bf16_kernel%s)" % (
+                            " + fm_merge_bf16_kernel" if S > 0 else ""),
+                        "ms_per_call": round(ms_reuse, 6),
+                        "effective_TFLOP_s": round(flops / (ms_reuse * 1e-3) / 1e12, 3)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, flops, args.cpu_seconds)

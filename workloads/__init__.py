@@ -252,6 +252,22 @@ def make_config(k: int, seed: Optional[int] = None, with_qkv: bool = True,
     return w
 
 
+def document_workload(lengths: List[int], H: int = 2, D: int = 128, seed: int = 1002,
+                      with_qkv: bool = True) -> Workload:
+    """Causal documents of the given lengths, encoded as the varlen workload
+    encodes them (n_vec = 2: LTS = end of the key's document, LTE = N), bf16
+    q/k/v from `seed`: the varlen workload with its documents resized."""
+    lens = [int(x) for x in lengths]
+    N_ = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    w = Workload("docs_%dx_%d" % (len(lens), N_), N_, H, D, BF16, True, 2, cu,
+                 causal_document_vectors(cu, 2, N_), np.float32(1.0 / np.sqrt(np.float32(D))))
+    w.meta["seed"] = seed
+    if with_qkv:
+        w.q, w.k, w.v = draw_qkv(seed, w.N, w.H, w.D, w.dtype)
+    return w
+
+
 def random_case(seed: int, N_max: int = 64, H: int = 1, D: int = 16,
                 causal: Optional[bool] = None, n_vec: Optional[int] = None,
                 dtype: str = F32, with_qkv: bool = True, allow_empty: bool = True) -> Workload:
