@@ -314,3 +314,30 @@ def test_empty_input(pv):
     out, lse = pv.attn_fwd(q, q, q, cu, sv, 1, True)
     torch.cuda.synchronize()
     assert out.shape == (0, 2, 128) and lse.shape == (2, 0)
+
+
+# ------------------------------------------------- extrema at large N
+@pytest.mark.parametrize("n_vec,causal,aligned", [(4, False, True), (4, False, False), (2, True, False), (1, True, True)])
+def test_extrema_large(pv, n_vec, causal, aligned):
+    """The extrema pass over 2^22 tokens (65536 key blocks at Bc = 64: more
+    than one grid-stride round of the launch), bit-exact against the oracle.
+    Documents of random lengths, multiples of 64 when `aligned` (every block
+    starts on a 16-byte boundary of the vectors) and arbitrary otherwise;
+    uniform random int32 mask values."""
+    N = 1 << 22
+    rng = np.random.default_rng(4242 + n_vec + 2 * int(aligned))
+    lens = []
+    while sum(lens) < N:
+        L = int(rng.integers(1000, 400000))
+        if aligned:
+            L = max(64, L // 64 * 64)
+        lens.append(min(L, N - sum(lens)))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    sv = rng.integers(0, N, size=(n_vec, N), dtype=np.int64).astype(np.int32)
+    say("extrema large: N=%d B=%d n_vec=%d causal=%d aligned=%d" % (N, len(lens), n_vec, causal, aligned))
+    kb_off, ext, status = pv.preprocess_mask(torch.from_numpy(sv).cuda(), n_vec, causal,
+                                             torch.from_numpy(cu).cuda(), N, 64)
+    okb, oext = O.extrema(cu, sv, n_vec, causal, 64)
+    assert status == 0
+    assert np.array_equal(kb_off.cpu().numpy(), okb)
+    assert np.array_equal(ext.cpu().numpy().reshape(-1, 8), oext.reshape(-1, 8))
