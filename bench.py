@@ -54,6 +54,11 @@ def parse():
     ap.add_argument("--seed", type=int, default=None, help="workload seed (default 1000 + config)")
     ap.add_argument("--sparsity-sweep", action="store_true",
                     help="instead of the step: step latency against the unmasked fraction on the varlen shape")
+    ap.add_argument("--packing-sweep", action="store_true",
+                    help="instead of the step: the workload's documents in four packings (varlen, mask-only "
+                         "with cu = [0, N], zero-padded, zero-padded with the padding masked), step time each")
+    ap.add_argument("--packings", default=",".join(("varlen", "mask_only", "padded", "padded_masked")),
+                    help="comma-separated packings the packing sweep runs")
     ap.add_argument("--preprocess-sweep", action="store_true",
                     help="instead of the step: time the block-extrema pass alone for N = 2^16 .. 2^26 "
                          "(n_vec = 4, non-causal) and report its achieved HBM GB/s")
@@ -277,6 +282,47 @@ def sparsity_sweep(args):
                       "data": "synthetic (seeded N(0,1) q/k/v)", "sweep": rows}), flush=True)
 
 
+def packing_sweep(args):
+    """The documents of a causal document workload (default: the varlen
+    workload [128, 128, 4096]) packed four ways through the same library:
+    back to back with one sequence each (varlen), back to back with
+    cu = [0, N] and only the mask separating them (mask_only, the FlashMask
+    article's ZeroPadding packing), zero-padded to the longest document
+    with a plain causal mask (padded, the Varlen-Packing document's padded
+    baseline), and zero-padded with the padding masked by the interval
+    (padded_masked).  Useful work is the documents' own unmasked pairs in
+    every case; `computed_pairs_per_head` is what the layout leaves
+    unmasked."""
+    import workloads as W
+    import oracle as O
+    base = W.make_config(args.config, seed=args.seed)
+    useful = O.unmasked_pairs(base.cu_seqlens, base.startend, base.n_vec, base.causal)
+    flops = O.effective_flops(useful, base.H, base.D)
+    rows = []
+    for kind in [x for x in args.packings.split(",") if x]:
+        w = W.packed_as(base, kind)
+        st = make_setup(w, args)
+        for _ in range(args.warmup):
+            st["step"]()
+        ms, _, _ = time_calls(st["step"], args.steps)
+        st["attn_with_plan"]()
+        ms_r, _, _ = time_calls(st["attn_with_plan"], args.steps)
+        hdr = st["hdr"]()
+        pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
+        rows.append({"packing": kind, "tokens_stored": w.N, "sequences": w.B, "n_vec": w.n_vec,
+                     "path": "fused" if st["fused"] else "planned", "max_kb_per_item": st["S"],
+                     "n_items": hdr["n_items"], "class_counts": hdr["class_counts"],
+                     "computed_pairs_per_head": int(pairs),
+                     "us_per_step": round(ms * 1e3, 2), "us_attention_reused_plan": round(ms_r * 1e3, 2),
+                     "effective_TFLOP_s": round(flops / (ms * 1e-3) / 1e12, 2)})
+    print(json.dumps({"metric": "step time of the same documents in four packings", "unit": "us",
+                      "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+                      "workload": base.name, "lengths": [int(x) for x in base.lengths][:16],
+                      "H": base.H, "D": base.D, "useful_pairs_per_head": int(useful),
+                      "effective_gflop": round(flops / 1e9, 4),
+                      "data": "synthetic (seeded N(0,1) q/k/v, zero pad tokens)", "sweep": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.preprocess_sweep:
@@ -288,6 +334,9 @@ def main():
         sys.exit(2)
     if args.sparsity_sweep:
         sparsity_sweep(args)
+        return
+    if args.packing_sweep:
+        packing_sweep(args)
         return
     import torch
     import workloads as W

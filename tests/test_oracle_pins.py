@@ -374,6 +374,38 @@ def test_mask_only_packing(k, N):
     assert np.allclose(a[1], b[1], atol=1e-12, rtol=0)
 
 
+@pytest.mark.parametrize("lens", [[5, 9, 20], [1, 17, 3, 8], [12], [7, 0, 7]])
+def test_packings_agree(lens):
+    """Varlen-Packing document §3 (padded batch) and FlashMask article §6.7
+    (ZeroPadding): the same causal documents packed back to back, packed
+    with cu = [0, N] and a global mask, or zero-padded to the longest one
+    give the same out and lse on every real token.  With the padding
+    masked by the interval, pad rows are empty rows (out = 0, lse = -inf).
+    Pair counts: the masked layouts keep exactly the documents' pairs, the
+    plain padded one every causal pair of each padded sample."""
+    w = W.document_workload(lens, H=2, D=8, seed=7)
+    ref_o, ref_l = O.attention(w.q, w.k, w.v, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)
+    ref_pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
+    assert ref_pairs == sum(L * (L + 1) // 2 for L in lens)
+    Lmax = max(lens)
+    for kind in W.PACKINGS:
+        p = W.packed_as(w, kind)
+        real = p.meta["real_rows"]
+        assert np.array_equal(p.q[real], w.q) and np.array_equal(p.v[real], w.v)
+        o, l = O.attention(p.q, p.k, p.v, p.cu_seqlens, p.startend, p.n_vec, p.causal, p.scale)
+        assert np.allclose(o[real], ref_o, atol=1e-12, rtol=0), kind
+        assert np.allclose(l[:, real], ref_l, atol=1e-12, rtol=0), kind
+        pad = np.setdiff1d(np.arange(p.N), real)
+        pairs = O.unmasked_pairs(p.cu_seqlens, p.startend, p.n_vec, p.causal)
+        if kind == "padded":
+            assert np.all(np.isfinite(l[:, pad]))
+            assert pairs == len(lens) * Lmax * (Lmax + 1) // 2
+        else:
+            assert pairs == ref_pairs, kind
+        if kind == "padded_masked":
+            assert np.all(o[pad] == 0.0) and np.all(np.isneginf(l[:, pad]))
+
+
 # ------------------------------------------------------------- worklist
 @pytest.mark.parametrize("seed", range(8))
 @pytest.mark.parametrize("S", [0, 1, 2, 3, 5])

@@ -14,7 +14,8 @@ Sources for the shapes and structures (cited by page title and section):
       §6.7 ZeroPadding: stored row indices are global (a running offset is
            added per packed sample), so every index below is a global row.
   * Varlen-Packing technical document (www.gsyq.cn/news/432802), §2: the
-      worked batch of lengths [128, 128, 4096] with 2 heads and Br=128.
+      worked batch of lengths [128, 128, 4096] with 2 heads and Br=128;
+      §3: the padded-batch baseline (every sample zero-padded to the longest).
   * Unsloth packing blog (unsloth.ai, "3x faster training + packing"),
       padding-free packing section: the short/long length mix.
 
@@ -35,7 +36,7 @@ from typing import List, Optional
 import numpy as np
 
 __all__ = ["Workload", "make_config", "make_lengths", "PAGE_LTS", "PAGE_LTE",
-           "causal_document_vectors", "shared_question_vectors",
+           "causal_document_vectors", "shared_question_vectors", "PACKINGS", "packed_as",
            "prefix_window_vectors", "random_case", "CONFIG_IDS"]
 
 # The 16-column causal example of the FlashMask article, §2.2 (its table is
@@ -296,3 +297,65 @@ def random_case(seed: int, N_max: int = 64, H: int = 1, D: int = 16,
     if with_qkv:
         w.q, w.k, w.v = draw_qkv(seed, N, H, D, dtype)
     return w
+
+
+PACKINGS = ("varlen", "mask_only", "padded", "padded_masked")
+
+
+def packed_as(w: Workload, kind: str) -> Workload:
+    """The causal documents of `w` (one sequence per document, LTS = the
+    document's end) laid out as one of the packings the pages compare:
+
+      varlen         w itself: documents back to back, one sequence each
+                     (Varlen-Packing document, §2);
+      mask_only      the same tokens and vectors with cu = [0, N]: only the
+                     mask keeps documents apart (FlashMask article §6.7,
+                     ZeroPadding packing);
+      padded         each document right-padded with zero tokens to the
+                     longest one, one sequence per document, plain causal
+                     mask (Varlen-Packing document §3, the padded baseline):
+                     pad rows are attended like real ones;
+      padded_masked  the padded layout whose mask also removes the padding:
+                     every column of a sample gets LTS = the end of the
+                     sample's real tokens (LTE defaults to N), so pad rows
+                     attend nowhere (out = 0, lse = -inf) and no real row
+                     sees a pad key (they lie above its diagonal).
+
+    meta["real_rows"] holds, in w's token order, the rows of the new layout
+    that carry w's tokens; q, k, v of pad rows are zero."""
+    if kind not in PACKINGS:
+        raise ValueError("unknown packing %r" % (kind,))
+    if not w.causal:
+        raise ValueError("packings are defined for causal document workloads")
+    cu = w.cu_seqlens.astype(np.int64)
+    if kind == "varlen":
+        out = dataclasses.replace(w, meta=dict(w.meta))
+        out.meta.update(packing=kind, real_rows=np.arange(w.N, dtype=np.int64))
+        return out
+    if kind == "mask_only":
+        out = dataclasses.replace(w, name=w.name + "_mask_only", cu_seqlens=np.array([0, w.N], np.int32),
+                                  meta=dict(w.meta))
+        out.meta.update(packing=kind, real_rows=np.arange(w.N, dtype=np.int64))
+        return out
+    lens = np.diff(cu)
+    Lmax = int(lens.max()) if lens.size else 0
+    B = int(lens.size)
+    Np = B * Lmax
+    cu_p = (np.arange(B + 1, dtype=np.int64) * Lmax).astype(np.int32)
+    real = np.concatenate([b * Lmax + np.arange(int(lens[b]), dtype=np.int64) for b in range(B)]) \
+        if B else np.zeros(0, np.int64)
+    if kind == "padded":
+        sv = np.full((1, Np), Np, np.int32)     # [N, N): empty, a plain causal mask
+    else:
+        sv = np.repeat((np.arange(B, dtype=np.int64) * Lmax + lens).astype(np.int32), Lmax)[None, :]
+
+    def spread(a):
+        if a is None:
+            return None
+        z = np.zeros((Np,) + a.shape[1:], a.dtype)
+        z[real] = a
+        return z
+    out = Workload(w.name + "_" + kind, Np, w.H, w.D, w.dtype, True, 1, cu_p, sv, w.scale,
+                   spread(w.q), spread(w.k), spread(w.v), dict(w.meta))
+    out.meta.update(packing=kind, real_rows=real)
+    return out
