@@ -1,4 +1,5 @@
-"""CPU oracle for packed, variable-length, interval-masked attention (forward).
+"""CPU oracle for packed, variable-length, interval-masked attention (forward and
+gradients).
 
 TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py may import this package.  It shares no code
@@ -15,7 +16,7 @@ the docstring of each function; every function here is pinned.
 """
 from .flashmask import (  # noqa: F401
     FULL, PARTIAL, UNMASKED,
-    fill_vectors, element_mask, attention, attention_rows, extrema,
+    fill_vectors, element_mask, attention, attention_rows, attention_bwd, extrema,
     classify, class_counts, worklist, unmasked_pairs, effective_flops,
     fa_varlen_grid_blocks,
 )

@@ -173,6 +173,66 @@ def attention_rows(q, k, v, cu_seqlens, startend, n_vec: int, causal: bool,
     return outs, lses
 
 
+# --------------------------------------------------- backward (gradients)
+def attention_bwd(q, k, v, dout, cu_seqlens, startend, n_vec: int, causal: bool,
+                  scale, chunk: int = 512):
+    """Gradients of `attention`'s out with respect to q, k and v for the
+    upstream gradient dout, float64.  Returns dq, dk, dv [N, H, D].
+
+    [FM] §3.4: the backward op takes q, k, v, startend_row_indices, out,
+    softmax_lse and out_grad and returns the gradients of q, k and v; §4.2:
+    FlashMask is exact, so its gradients are those of the dense-mask
+    attention.  This is the chain rule through the forward's definition,
+    per (sequence, head), over the same allowed keys A_i:
+      P_ij   = exp(s_ij - lse_i) for j in A_i, 0 otherwise;
+      dv_j   = sum_i P_ij dout_i;
+      dP_ij  = <dout_i, v_j>;
+      dS_ij  = P_ij (dP_ij - sum_l P_il dP_il)     (softmax Jacobian);
+      dq_i   = scale * sum_j dS_ij k_j;   dk_j = scale * sum_i dS_ij q_i.
+    P is recomputed here from q and k (nothing is taken from a forward run).
+    Rows with no allowed key have constant out = 0: they contribute nothing.
+    Pinned by: central finite differences of `attention` on tiny random
+    cases (both modes, empty rows), the q = 0 closed form of dv, the
+    softmax shift invariance (sum_j dk_j = 0 per sequence and head) and
+    packed = separate.
+    """
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64); g = np.asarray(dout, np.float64)
+    N, H, D = q.shape
+    vecs = fill_vectors(startend, n_vec, causal, N)
+    cu = np.asarray(cu_seqlens, np.int64)
+    scale = float(np.float64(scale))
+    dq = np.zeros((N, H, D), np.float64)
+    dk = np.zeros((N, H, D), np.float64)
+    dv = np.zeros((N, H, D), np.float64)
+    for b in range(len(cu) - 1):
+        s, e = _seq_bounds(cu, b)
+        if e <= s:
+            continue
+        cols = np.arange(s, e)
+        for h in range(H):
+            kh = k[s:e, h, :]
+            vh = v[s:e, h, :]
+            for r0 in range(s, e, chunk):
+                r1 = min(r0 + chunk, e)
+                rows = np.arange(r0, r1)
+                sc = scale * (q[r0:r1, h, :] @ kh.T)
+                msk = element_mask(rows, cols, vecs, causal)
+                sc = np.where(msk, -np.inf, sc)
+                mx = sc.max(axis=1, keepdims=True)
+                mx = np.where(np.isfinite(mx), mx, 0.0)
+                p = np.exp(sc - mx)                       # 0 on masked pairs
+                ssum = p.sum(axis=1, keepdims=True)
+                p = np.divide(p, ssum, out=np.zeros_like(p), where=ssum > 0)
+                gh = g[r0:r1, h, :]
+                dv[s:e, h, :] += p.T @ gh
+                dp = gh @ vh.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[r0:r1, h, :] = scale * (ds @ kh)
+                dk[s:e, h, :] += scale * (ds.T @ q[r0:r1, h, :])
+    return dq, dk, dv
+
+
 # -------------------------------------------------------------- O4 extrema
 def extrema(cu_seqlens, startend, n_vec: int, causal: bool, block_k: int):
     """Per-key-block min/max of the four filled vectors.

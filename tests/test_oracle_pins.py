@@ -406,6 +406,80 @@ def test_packings_agree(lens):
             assert np.all(o[pad] == 0.0) and np.all(np.isneginf(l[:, pad]))
 
 
+# ------------------------------------------------------------- gradients
+@pytest.mark.parametrize("seed", range(6))
+def test_bwd_finite_differences(seed):
+    """FlashMask article §3.4 (the backward returns the gradients of q, k,
+    v) and §4.2 (exact: the dense-mask attention's gradients): central
+    differences of the forward oracle's L = sum(G * out) match the
+    backward for every element of q, k and v, masked pairs, empty rows and
+    zero-length sequences included."""
+    w = W.random_case(300 + seed, N_max=18, H=2, D=3, dtype=W.F32, allow_empty=True)
+    rng = np.random.default_rng(seed)
+    G = rng.standard_normal(w.q.shape)
+    q, k, v = (x.astype(np.float64) for x in (w.q, w.k, w.v))
+    dq, dk, dv = O.attention_bwd(q, k, v, G, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(G * O.attention(qq, kk, vv, w.cu_seqlens, w.startend, w.n_vec, w.causal,
+                                            w.scale)[0]))
+    eps = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert np.max(np.abs(num - grad)) < 1e-6, (which, np.max(np.abs(num - grad)))
+
+
+def test_bwd_q_zero_closed_form():
+    """q = 0 makes every allowed key equally likely (P_ij = 1 / |A_i|), so
+    dv_j = sum over the rows i that see j of G_i / |A_i|; with the same
+    mask written out here as the FlashMask article §2.2 intervals."""
+    w = W.make_config(1)
+    q = np.zeros_like(w.q)
+    G = np.random.default_rng(5).standard_normal(w.q.shape)
+    _, _, dv = O.attention_bwd(q, w.k, w.v, G, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)
+    lts, lte = W.PAGE_LTS, W.PAGE_LTE
+    allowed = [[j for j in range(16) if j <= i and not (lts[j] <= i < lte[j])] for i in range(16)]
+    ref = np.zeros_like(dv)
+    for i in range(16):
+        for j in allowed[i]:
+            ref[j] += G[i] / len(allowed[i])
+    assert sum(len(a) for a in allowed) == 71
+    assert np.allclose(dv, ref, atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_bwd_invariants(seed):
+    """Softmax is unchanged when one vector is added to every key of a
+    sequence (each score row moves by a constant), so the key gradients of
+    a sequence sum to zero per head; rows with no allowed key get dq = 0,
+    keys no row attends get dk = dv = 0; packed = separate ([US] packing
+    without contamination) holds for the gradients too."""
+    w = W.random_case(400 + seed, N_max=40, H=2, D=8, dtype=W.F32, allow_empty=True)
+    G = np.random.default_rng(seed).standard_normal(w.q.shape)
+    dq, dk, dv = O.attention_bwd(w.q, w.k, w.v, G, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)
+    vecs = O.fill_vectors(w.startend, w.n_vec, w.causal, w.N)
+    cu = [int(x) for x in w.cu_seqlens]
+    for b in range(len(cu) - 1):
+        s, e = cu[b], cu[b + 1]
+        if e == s:
+            continue
+        assert np.allclose(dk[s:e].sum(axis=0), 0.0, atol=1e-12)
+        m = O.element_mask(np.arange(s, e), np.arange(s, e), vecs, w.causal)
+        assert np.all(dq[s:e][m.all(axis=1)] == 0.0)
+        assert np.all(dk[s:e][m.all(axis=0)] == 0.0) and np.all(dv[s:e][m.all(axis=0)] == 0.0)
+        sv = w.startend[:, s:e].astype(np.int64) - s
+        one = O.attention_bwd(w.q[s:e], w.k[s:e], w.v[s:e], G[s:e], np.array([0, e - s]), sv, w.n_vec,
+                              w.causal, w.scale)
+        for a, bb in zip(one, (dq, dk, dv)):
+            assert np.allclose(a, bb[s:e], atol=1e-12, rtol=0)
+
+
 # ------------------------------------------------------------- worklist
 @pytest.mark.parametrize("seed", range(8))
 @pytest.mark.parametrize("S", [0, 1, 2, 3, 5])
