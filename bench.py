@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--packing-sweep", action="store_true",
                     help="instead of the step: the workload's documents in four packings (varlen, mask-only "
                          "with cu = [0, N], zero-padded, zero-padded with the padding masked), step time each")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward step: time the backward (dq, dk, dv) on the workload")
     ap.add_argument("--packings", default=",".join(("varlen", "mask_only", "padded", "padded_masked")),
                     help="comma-separated packings the packing sweep runs")
     ap.add_argument("--preprocess-sweep", action="store_true",
@@ -218,7 +220,8 @@ def make_setup(w, args):
             if ev_b is not None:
                 ev_b.record()
     hdr = (plan if not fused else pv.Plan(ws, plan.layout, w.N, w.B, w.H, w.D, dt, w.causal, w.n_vec, S)).header
-    return dict(dt=dt, dev=dev, step=step, attn_with_plan=attn_with_plan, plan=plan, S=S, fused=fused, hdr=hdr)
+    return dict(dt=dt, dev=dev, step=step, attn_with_plan=attn_with_plan, plan=plan, S=S, fused=fused, hdr=hdr,
+                tensors=(q, k, v, cu, sv))
 
 
 def spin():
@@ -323,6 +326,51 @@ def packing_sweep(args):
                       "data": "synthetic (seeded N(0,1) q/k/v, zero pad tokens)", "sweep": rows}), flush=True)
 
 
+def backward_bench(args):
+    """The backward on workload --config: dq, dk, dv from q, k, v, the
+    forward's out and lse, and a seeded N(0, 1) output gradient.  One step =
+    one fm_attn_bwd call (block extrema, Delta, dK/dV, dQ).  Useful work =
+    five products per attending pair (S recomputed, dP, dV, dK, dQ), i.e.
+    2.5 x the forward's effective FLOPs; the dQ launch recomputes S and dP,
+    which is not counted."""
+    import torch
+    import workloads as W
+    import oracle as O
+    import packed_varlen_masked_amd as pv
+    w = W.make_config(args.config, seed=args.seed)
+    if w.dtype != W.BF16:
+        raise SystemExit("the backward is built for the bf16 workloads (configs 2-5)")
+    st = make_setup(w, args)
+    dev = st["dev"]
+    q, k, v, cu, sv = st["tensors"]
+    out, lse = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale))
+    g = torch.from_numpy(np.random.default_rng(w.meta["seed"] + 2).standard_normal(
+        (w.N, w.H, w.D), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    ws = torch.zeros(pv.bwd_workspace_size(w.N, w.B, w.H, w.D, torch.bfloat16), dtype=torch.uint8, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def step():
+        pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale), workspace=ws,
+                    dq=dq, dk=dk, dv=dv)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms, host_ms, ahead = time_calls(step, args.steps)
+    pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
+    flops = 2.5 * O.effective_flops(pairs, w.H, w.D)
+    value = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({"metric": "backward effective TFLOP/s (5 products per unmasked pair) + % bf16 MFMA peak",
+                      "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+                      "dtype": "bf16", "data": "synthetic (seeded N(0,1) q/k/v/dout)",
+                      "config": {"workload": w.name, "N": w.N, "B": w.B, "H": w.H, "D": w.D,
+                                 "causal": bool(w.causal), "n_vec": w.n_vec,
+                                 "unmasked_pairs_per_head": int(pairs), "useful_gflop": round(flops / 1e9, 4)},
+                      "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+                      "timing": {"host_enqueue_ms_per_step": round(host_ms, 4), "host_ran_ahead": ahead}}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.preprocess_sweep:
@@ -337,6 +385,9 @@ def main():
         return
     if args.packing_sweep:
         packing_sweep(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
     import torch
     import workloads as W

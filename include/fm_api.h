@@ -1,6 +1,7 @@
 /*
- * fm_api.h — C ABI of libflashmask_mi355.so: FlashMask-style forward
- * attention over packed, variable-length sequences on MI355X (gfx950).
+ * fm_api.h — C ABI of libflashmask_mi355.so: FlashMask-style attention
+ * (forward and backward) over packed, variable-length sequences on MI355X
+ * (gfx950).
  *
  * What is computed (sources cited by page title and section):
  *   [FM] PaddleNLP FlashMask article (m.nxbn.cn/news/70198)
@@ -279,6 +280,41 @@ int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype,
  */
 int fm_fused_path(int64_t N, int B, int H, int head_dim, int dtype, int n_vec, int causal,
                   int max_kb_per_item, unsigned flags);
+
+/*
+ * Workspace bytes of fm_attn_bwd (0 on bad arguments): a status header,
+ * kb_off [B+1] and extrema [ceil(N/64)+B][8] of the mask at block_k = 64,
+ * and Delta fp32 [H][N].  Separate from the forward's workspace.
+ */
+size_t fm_bwd_workspace_size(int64_t N, int B, int H, int head_dim, int dtype);
+
+/*
+ * The backward ([FM] §3.4: the op takes q, k, v, the row intervals, out,
+ * softmax_lse and the output gradient, and returns the gradients of q, k
+ * and v; [FM] §4.2: exact, and deterministic because dq is not summed
+ * with atomics).  With P_ij = exp(scale <q_i, k_j> - lse_i) on the allowed
+ * pairs (0 elsewhere) and Delta_i = <dout_i, out_i>:
+ *   dv_j = sum_i P_ij dout_i
+ *   dS_ij = P_ij (<dout_i, v_j> - Delta_i)
+ *   dq_i = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i
+ * Fully masked tiles are skipped by the same block extrema and tile rules
+ * as the forward (preprocessing runs inside this call).
+ *
+ * q, k, v, out, dout, dq, dk, dv: contiguous [N, H, D] bf16; D = 128 only
+ *   (other dtypes / head_dims: FM_E_UNSUPPORTED).  out and softmax_lse
+ *   (fp32 [H, N]) are the forward's outputs for the same inputs; rows with
+ *   lse = -inf get dq = 0.  cu_seqlens, startend, n_vec, causal, scale as
+ *   for fm_attn_fwd.  dq, dk, dv are written completely (zeros where no
+ *   pair contributes) unless the device data is invalid (status word).
+ * workspace: device, >= fm_bwd_workspace_size(...) bytes.
+ * Launches: block extrema, Delta, dK/dV (one workgroup per 128-key tile
+ * and head), dQ (one per 128-query tile and head); same bits every run.
+ */
+int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                const float* softmax_lse, int dtype, int64_t N, int H, int D,
+                const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
+                float scale, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                hipStream_t stream);
 
 /* Test helper: synchronises `stream` and copies the workspace's status
  * word to *status (0 = the device data was valid). */

@@ -16,7 +16,8 @@ the docstring of each function; every function here is pinned.
 """
 from .flashmask import (  # noqa: F401
     FULL, PARTIAL, UNMASKED,
-    fill_vectors, element_mask, attention, attention_rows, attention_bwd, extrema,
+    fill_vectors, element_mask, attention, attention_rows, attention_bwd,
+    attention_bwd_rows, extrema,
     classify, class_counts, worklist, unmasked_pairs, effective_flops,
     fa_varlen_grid_blocks,
 )

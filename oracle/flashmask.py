@@ -233,6 +233,34 @@ def attention_bwd(q, k, v, dout, cu_seqlens, startend, n_vec: int, causal: bool,
     return dq, dk, dv
 
 
+def attention_bwd_rows(q, k, v, dout, cu_seqlens, startend, n_vec: int, causal: bool,
+                       scale, rows: Sequence[int], heads: Sequence[int]):
+    """dq of `attention_bwd` at the given (row, head) pairs only, one row at a
+    time from the same definition (for sampled checks at full size):
+    dq_i = scale * sum_j P_ij (<dout_i, v_j> - sum_l P_il <dout_i, v_l>) k_j
+    over the row's allowed keys.  Returns dq [len(rows), D] in fp64."""
+    N, H, D = np.asarray(q).shape
+    vecs = fill_vectors(startend, n_vec, causal, N)
+    cu = np.asarray(cu_seqlens, np.int64)
+    scale = float(np.float64(scale))
+    out = np.zeros((len(rows), D), np.float64)
+    for t, (i, h) in enumerate(zip(rows, heads)):
+        b = int(np.searchsorted(cu, i, side="right") - 1)
+        s, e = _seq_bounds(cu, b)
+        cols = np.arange(s, e)
+        allowed = cols[~element_mask(np.array([i]), cols, vecs, causal)[0]]
+        if allowed.size == 0:
+            continue
+        kk = np.asarray(k[allowed, h, :], np.float64)
+        vv = np.asarray(v[allowed, h, :], np.float64)
+        sc = scale * (kk @ np.asarray(q[i, h, :], np.float64))
+        p = np.exp(sc - sc.max())
+        p /= p.sum()
+        dp = vv @ np.asarray(dout[i, h, :], np.float64)
+        out[t] = scale * ((p * (dp - (p * dp).sum())) @ kk)
+    return out
+
+
 # -------------------------------------------------------------- O4 extrema
 def extrema(cu_seqlens, startend, n_vec: int, causal: bool, block_k: int):
     """Per-key-block min/max of the four filled vectors.

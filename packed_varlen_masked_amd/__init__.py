@@ -77,6 +77,8 @@ def _load():
         "fm_attn_fwd": (I, [P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, I, I, I, P, SZ, U, P]),
         "fm_read_status": (I, [P, P, P]),
         "fm_fused_path": (I, [I64, I, I, I, I, I, I, I, U]),
+        "fm_bwd_workspace_size": (SZ, [I64, I, I, I, I]),
+        "fm_attn_bwd": (I, [P, P, P, P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -89,7 +91,7 @@ _lib = _load()
 EXPORTED = ("fm_last_error", "fm_version", "fm_self_check", "fm_get_tile_config", "fm_auto_split",
             "fm_workspace_layout", "fm_workspace_size", "fm_worklist_scratch_size",
             "fm_preprocess_mask", "fm_build_worklist", "fm_build_plan", "fm_attn_fwd",
-            "fm_read_status", "fm_fused_path")
+            "fm_read_status", "fm_fused_path", "fm_bwd_workspace_size", "fm_attn_bwd")
 
 
 def _check(rc: int):
@@ -326,6 +328,55 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
                             _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
                             _ptr(out), _ptr(lse), bq, bk, S, _ptr(ws), ws.numel(), flags, _stream()))
     return out, lse
+
+
+def bwd_workspace_size(N: int, B: int, H: int, head_dim: int, dtype: torch.dtype) -> int:
+    n = _lib.fm_bwd_workspace_size(N, B, H, head_dim, _dtype_code(dtype))
+    if n == 0:
+        raise FMError(FM_E_INVAL, "bad sizes for the backward: %s" % _lib.fm_last_error().decode())
+    return n
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, cu_seqlens: torch.Tensor, startend: torch.Tensor, n_vec: int, causal: bool,
+             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None):
+    """FlashMask backward.  q, k, v, out, dout: [N, H, D] bf16 (contiguous,
+    same device); lse fp32 [H, N] from the forward; cu_seqlens and startend
+    as for attn_fwd.  Returns (dq, dk, dv) [N, H, D] bf16."""
+    ts = ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"))
+    for t, nm in ts:
+        if t.dim() != 3 or t.shape != q.shape:
+            raise FMError(FM_E_INVAL, "%s must have q's [N, H, D] shape" % nm)
+        if t.dtype != q.dtype:
+            raise FMError(FM_E_INVAL, "%s must have q's dtype" % nm)
+        if not t.is_contiguous() or not t.is_cuda:
+            raise FMError(FM_E_INVAL, "%s must be a contiguous CUDA tensor" % nm)
+    N, H, D = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, N) or not lse.is_contiguous():
+        raise FMError(FM_E_INVAL, "lse must be contiguous fp32 [H, N]")
+    cu = _i32(cu_seqlens, "cu_seqlens")
+    B = cu.numel() - 1
+    if N > 0:
+        _i32(startend, "startend")
+        if tuple(startend.shape) != (n_vec, N):
+            raise FMError(FM_E_INVAL, "startend must be [n_vec, N] = [%d, %d]" % (n_vec, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = torch.zeros(bwd_workspace_size(N, B, H, D, q.dtype), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise FMError(FM_E_INVAL, "%s must be contiguous with q's shape and dtype" % nm)
+    _check(_lib.fm_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                            _dtype_code(q.dtype), N, H, D, _ptr(cu), B,
+                            _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv
 
 
 def read_status(workspace: torch.Tensor) -> int:

@@ -201,6 +201,28 @@ int preprocess_impl(const int32_t* sv, int n_vec, int causal, const int32_t* cu,
                                         nkb, status, n_cu, s), "extrema launch");
 }
 
+// Backward workspace: header, kb_off, extrema at block_k = 64, Delta.
+struct BwdLayout { size_t off_hdr, off_kb_off, off_extrema, off_delta, bytes; int64_t kb_cap; };
+
+int bwd_layout(int64_t N, int B, int H, BwdLayout* L) {
+    L->kb_cap = cdiv(N, fm::bwd_block_k()) + B;
+    size_t off = 0;
+    L->off_hdr = off; off = align256(off + 256);
+    L->off_kb_off = off; off = align256(off + (size_t)(B + 1) * 4);
+    L->off_extrema = off; off = align256(off + (size_t)L->kb_cap * 32);
+    L->off_delta = off; off = align256(off + (size_t)H * (size_t)N * 4);
+    L->bytes = off;
+    if ((int64_t)off > kMaxBytes) return fail(FM_E_INVAL, "problem too large");
+    if (L->kb_cap > INT32_MAX / 2) return fail(FM_E_INVAL, "too many key blocks");
+    return FM_OK;
+}
+
+int bwd_supported(int dtype, int D) {
+    if (dtype != FM_BF16) return fail(FM_E_UNSUPPORTED, "the backward is built for bf16 only (dtype %d)", dtype);
+    if (D != 128) return fail(FM_E_UNSUPPORTED, "the backward is built for head_dim 128 (got %d)", D);
+    return FM_OK;
+}
+
 int worklist_impl(const int32_t* cu, int B, int64_t N, int H, int Br, int Bc, const int32_t* kb_off,
                   const int32_t* ext, const int32_t* status, int32_t* status_rw, int causal, int S,
                   int32_t* items, int64_t items_cap, int32_t* n_items, int64_t* counts,
@@ -473,6 +495,49 @@ int fm_fused_path(int64_t N, int B, int H, int head_dim, int dtype, int n_vec, i
     int n_cu = 0;
     if (device_cus(&n_cu)) return -1;
     return fused_eligible(N, B, H, dtype, head_dim, bq, bk, S, n_vec, flags, n_cu) ? 1 : 0;
+}
+
+size_t fm_bwd_workspace_size(int64_t N, int B, int H, int head_dim, int dtype) {
+    BwdLayout L;
+    if (check_sizes(N, B, H) || bwd_supported(dtype, head_dim) || bwd_layout(N, B, H, &L)) return 0;
+    return L.bytes;
+}
+
+int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                const float* softmax_lse, int dtype, int64_t N, int H, int D, const int32_t* cu_seqlens,
+                int B, const int32_t* startend, int n_vec, int causal, float scale, void* dq, void* dk,
+                void* dv, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_sizes(N, B, H);
+    if (rc) return rc;
+    if ((rc = bwd_supported(dtype, D))) return rc;
+    if (!mask_form_ok(n_vec, causal))
+        return fail(FM_E_INVAL, "unsupported (n_vec=%d, causal=%d)", n_vec, causal);
+    if (!(scale > 0.f) || !isfinite(scale)) return fail(FM_E_INVAL, "scale must be finite and > 0");
+    if (!cu_seqlens || !workspace) return fail(FM_E_INVAL, "null pointer argument");
+    if (N > 0 && (!q || !k || !v || !out || !dout || !softmax_lse || !startend || !dq || !dk || !dv))
+        return fail(FM_E_INVAL, "null pointer argument");
+    BwdLayout L;
+    if ((rc = bwd_layout(N, B, H, &L))) return rc;
+    if (ws_bytes < L.bytes) return fail(FM_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.bytes);
+    char* base = (char*)workspace;
+    int32_t* hdr = (int32_t*)(base + L.off_hdr);
+    int32_t* kb_off = (int32_t*)(base + L.off_kb_off);
+    int32_t* ext = (int32_t*)(base + L.off_extrema);
+    if ((rc = preprocess_impl(startend, n_vec, causal, cu_seqlens, B, N, fm::bwd_block_k(), kb_off, ext,
+                              L.kb_cap, hdr + fm::HDR_NKB, hdr + fm::HDR_STATUS, stream)))
+        return rc;
+    if (N == 0) return ok();
+    fm::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = softmax_lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.delta = (float*)(base + L.off_delta);
+    a.N = N; a.H = H; a.B = B;
+    a.cu = cu_seqlens; a.sv = startend; a.n_vec = n_vec; a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.kb_off = kb_off; a.extrema = ext; a.n_kb = hdr + fm::HDR_NKB; a.status = hdr + fm::HDR_STATUS;
+    if ((rc = hip_check(fm::launch_bwd_bf16(a, L.kb_cap, stream), "backward launch"))) return rc;
+    return ok();
 }
 
 int fm_read_status(const void* workspace, hipStream_t stream, int32_t* status) {

@@ -1,0 +1,576 @@
+// Backward of the FlashMask attention: dq, dk, dv from q, k, v, out, the
+// output gradient dout and softmax_lse; bf16 in and out, fp32 accumulation,
+// head_dim 128, on gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
+//
+// Method (PaddleNLP FlashMask article, m.nxbn.cn/news/70198): §3.4 names the
+// backward op (inputs q, k, v, the row intervals, out, softmax_lse and the
+// output gradient; outputs the gradients of q, k and v); the block extrema
+// and tile classes of §3.1/§3.2 decide which tiles are skipped, as in the
+// forward; §4.2: the result does not depend on the order of floating-point
+// accumulation (no atomics on dq).  The gradients are those of the
+// forward's softmax attention, with P = exp(scale S - lse) on the allowed
+// pairs:
+//   dV = P^T dO,  dP = dO V^T,  Delta_i = <dO_i, O_i>,
+//   dS = P o (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Layout and schedule (this file's own):
+//   * delta kernel: Delta[h, i] = <dO_i, O_i> in fp32, 16 lanes per row.
+//   * dK/dV kernel: one workgroup of 4 waves per (128-key tile, head);
+//     wave w owns keys 32w..32w+31 and holds their K and V fragments in
+//     registers.  It walks the sequence's 64-row q tiles that are not FULL
+//     against its key tile, stages Q, dO, lse and Delta of each in LDS (the
+//     next tile is loaded into registers while the current one is used),
+//     computes S = Q K^T and dP = dO V^T with one key per lane (so the
+//     key's mask intervals are lane constants), and accumulates
+//     dV^T = dO^T P and dK^T = Q^T dS with the LDS transpose read.
+//   * dQ kernel: one workgroup of 4 waves per (128-query tile, head); wave
+//     w owns queries 32w..32w+31 with their Q and dO fragments, lse and
+//     Delta in registers.  It walks the visited 64-key blocks, stages K and
+//     V in LDS, computes S^T = K Q^T and dP^T = V dO^T with one query per
+//     lane (as the forward does), and accumulates dQ^T = K^T dS^T.
+//   * every output element is written by exactly one workgroup: the same
+//     inputs give the same bits.
+#include "fm_common.hpp"
+#include "fm_internal.h"
+#include "fm_api.h"
+
+namespace fm {
+namespace bwd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int HD = 128;          // head_dim
+constexpr int BLK = 64;          // key block of the extrema; q rows per dK/dV step; keys per dQ step
+constexpr int NTH = 256;         // 4 waves
+constexpr int ROW_T = 320;       // LDS row stride (bytes) of tiles also read transposed
+constexpr int ROW_R = 272;       // LDS row stride of tiles read by rows only
+constexpr float LOG2E = 1.4426950408889634074f;
+
+__device__ __attribute__((always_inline)) inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __attribute__((always_inline)) inline uint32_t bf16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __attribute__((always_inline)) inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// A-operand fragment of the transpose of a row-major LDS tile (rows are the
+// MFMA's k index, channels its m index): channel block dt (32 channels),
+// k group kg (16 rows).  Within a group, lane half hh takes rows
+// 4hh + {0..3, 8..11}: the order in which an MFMA result holds its rows
+// (register e of a 32x32 result is row 8(e>>2) + 4hh + (e&3)), so the B
+// operand can be packed straight from such a result.
+template <int RS>
+__device__ __attribute__((always_inline)) inline bf16x8 tr_frag(const char* tile, int kg, int dt, int lane) {
+    const int hh = lane >> 5, grp = lane >> 4, gi = lane & 15;
+    const char* p = tile + (4 * hh + (gi >> 2)) * RS + 16 * (2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1) +
+                    16 * kg * RS + 64 * dt;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)p);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)(p + 8 * RS));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Rows [s, e) of 32 as a bit mask (s, e relative, clamped; empty if e <= s).
+__device__ __attribute__((always_inline)) inline uint32_t row_bits(int s, int e) {
+    s = min(max(s, 0), 32);
+    e = min(max(e, s), 32);
+    const int w = e - s;
+    return w >= 32 ? 0xffffffffu : ((1u << w) - 1u) << (s & 31);
+}
+// x, or y where the lane's bit of {lo: lanes 0-31, hi: lanes 32-63} is set.
+__device__ __attribute__((always_inline)) inline float select_lanes(float x, float y, uint32_t lo, uint32_t hi) {
+    const uint64_t m = ((uint64_t)hi << 32) | lo;
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "s"(m));
+    return r;
+}
+
+// Sequence of global key block x (kb_off[0] <= x < kb_off[B]).
+__device__ inline int seq_of_block(const int32_t* kb_off, int B, int x) {
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (kb_off[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// The 128-row (or 128-key) span of a workgroup: global block x and, when it
+// lies in the same sequence, block x + 1.  Workgroups of odd local blocks
+// have no span (their block belongs to the workgroup before).
+struct Span {
+    bool ok;
+    int b, s_b, e_b, lo, hi, x;
+    bool two;
+};
+__device__ inline Span span_of(const BwdArgs& a, int x) {
+    Span sp;
+    sp.ok = false;
+    if (__builtin_amdgcn_readfirstlane(*a.status) != 0) return sp;
+    const int n_kb = __builtin_amdgcn_readfirstlane(*a.n_kb);
+    if (x >= n_kb) return sp;
+    sp.b = seq_of_block(a.kb_off, a.B, x);
+    const int kb0 = a.kb_off[sp.b], kb1 = a.kb_off[sp.b + 1];
+    if ((x - kb0) & 1) return sp;
+    sp.x = x;
+    sp.two = x + 1 < kb1;
+    sp.s_b = a.cu[sp.b];
+    sp.e_b = a.cu[sp.b + 1];
+    sp.lo = sp.s_b + (x - kb0) * BLK;
+    sp.hi = min(sp.lo + 2 * BLK, sp.e_b);
+    sp.ok = true;
+    return sp;
+}
+
+// ---- Delta ---------------------------------------------------------------
+// Delta[h, i] = sum_d dO[i, h, d] O[i, h, d]: 16 lanes per (row, head), 8
+// channels each, summed over the 16 lanes with DPP (quad swaps, then the
+// half-row and row mirrors leave the sum in every lane of the row).
+__device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+template <int CTRL>
+__device__ inline float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+__global__ __launch_bounds__(NTH) void fm_bwd_delta_kernel(BwdArgs a) {
+    const int64_t p = ((int64_t)blockIdx.x * NTH + threadIdx.x) >> 4;   // (row, head) = row * H + head
+    const int sub = threadIdx.x & 15;
+    const int64_t NH = a.N * a.H;
+    float acc = 0.f;
+    if (p < NH) {
+        const u32x4 o = *(const u32x4*)((const char*)a.out + p * (2 * HD) + 16 * sub);
+        const u32x4 g = *(const u32x4*)((const char*)a.dout + p * (2 * HD) + 16 * sub);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc += bf_lo(o[i]) * bf_lo(g[i]) + bf_hi(o[i]) * bf_hi(g[i]);
+    }
+    acc = dpp_add<0xB1>(acc);    // quad_perm [1,0,3,2]
+    acc = dpp_add<0x4E>(acc);    // quad_perm [2,3,0,1]
+    acc = dpp_add<0x141>(acc);   // row_half_mirror
+    acc = dpp_add<0x140>(acc);   // row_mirror
+    if (p < NH && sub == 0) {
+        const int64_t i = p / a.H;
+        const int h = (int)(p - i * a.H);
+        a.delta[(int64_t)h * a.N + i] = acc;
+    }
+}
+
+// ---- dK / dV ---------------------------------------------------------------
+__shared__ __attribute__((aligned(16))) char s_q[BLK * ROW_T];
+__shared__ __attribute__((aligned(16))) char s_g[BLK * ROW_T];
+__shared__ __attribute__((aligned(16))) float s_l2[BLK];
+__shared__ __attribute__((aligned(16))) float s_dl[BLK];
+
+// One q tile's staging data in registers: 4 chunks of Q and of dO per
+// thread (row c >> 4, chunk c & 15 of c = tid + 256 u), and threads 0..63
+// the lse (log2 units; +inf for rows that attend nothing or lie past the
+// sequence, so that P = 0 there) and Delta of row tid.
+struct QStage {
+    u32x4 q[4], g[4];
+    float l2, dl;
+};
+__device__ inline void load_qstage(const BwdArgs& a, int h, int r0, int r1, int tid, QStage& st) {
+    const int64_t rsb = (int64_t)a.H * 2 * HD;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int c = tid + NTH * u, row = c >> 4, ch = c & 15;
+        st.q[u] = u32x4{0, 0, 0, 0};
+        st.g[u] = u32x4{0, 0, 0, 0};
+        if (r0 + row < r1) {
+            const int64_t off = (int64_t)(r0 + row) * rsb + (int64_t)h * 2 * HD + 16 * ch;
+            st.q[u] = *(const u32x4*)((const char*)a.q + off);
+            st.g[u] = *(const u32x4*)((const char*)a.dout + off);
+        }
+    }
+    st.l2 = INFINITY;
+    st.dl = 0.f;
+    if (tid < BLK && r0 + tid < r1) {
+        const float l = a.lse[(int64_t)h * a.N + r0 + tid];
+        st.l2 = l == -INFINITY ? INFINITY : l * LOG2E;
+        st.dl = a.delta[(int64_t)h * a.N + r0 + tid];
+    }
+}
+__device__ inline void store_qstage(const QStage& st, int tid) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int c = tid + NTH * u, row = c >> 4, ch = c & 15;
+        *(u32x4*)(s_q + row * ROW_T + 16 * ch) = st.q[u];
+        *(u32x4*)(s_g + row * ROW_T + 16 * ch) = st.g[u];
+    }
+    if (tid < BLK) {
+        s_l2[tid] = st.l2;
+        s_dl[tid] = st.dl;
+    }
+}
+
+__global__ __launch_bounds__(NTH, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
+    const int h = blockIdx.y;
+    const Span sp = span_of(a, blockIdx.x);
+    if (!sp.ok) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, hh = lane >> 5;
+    const int c0 = sp.lo, c1 = sp.hi;
+
+    // extrema of the key tile: its one or two blocks combined
+    int xe[8];
+    {
+        const int4 e0 = *(const int4*)(a.extrema + (int64_t)sp.x * 8);
+        const int4 e1 = *(const int4*)(a.extrema + (int64_t)sp.x * 8 + 4);
+        xe[0] = e0.x; xe[1] = e0.y; xe[2] = e0.z; xe[3] = e0.w;
+        xe[4] = e1.x; xe[5] = e1.y; xe[6] = e1.z; xe[7] = e1.w;
+        if (sp.two) {
+            const int4 f0 = *(const int4*)(a.extrema + (int64_t)(sp.x + 1) * 8);
+            const int4 f1 = *(const int4*)(a.extrema + (int64_t)(sp.x + 1) * 8 + 4);
+            const int y[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xe[i] = (i & 1) ? max(xe[i], y[i]) : min(xe[i], y[i]);
+        }
+    }
+
+    // this lane's key: K and V fragments (B operands: column = key n,
+    // channels 16s + 8hh .. +7) and its mask intervals
+    const int kj = c0 + 32 * w + n;
+    const bool kvalid = kj < c1;
+    bf16x8 kf[8], vf[8];
+    {
+        const int64_t off = ((int64_t)kj * a.H + h) * 2 * HD + 16 * hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            kf[s] = as_bf16x8(kvalid ? *(const u32x4*)((const char*)a.k + off + 32 * s) : u32x4{0, 0, 0, 0});
+            vf[s] = as_bf16x8(kvalid ? *(const u32x4*)((const char*)a.v + off + 32 * s) : u32x4{0, 0, 0, 0});
+        }
+    }
+    Vec4 mv{0, 0, 0, 0};
+    if (kvalid) mv = fill_column(a.sv, a.n_vec, a.causal, a.N, kj);
+
+    f32x16 dk[4], dv[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { dk[dt][e] = 0.f; dv[dt][e] = 0.f; }
+
+    // q tiles of 64 rows from the sequence start; causal rows before c0 see
+    // none of the tile's keys
+    const int Tq = ceil_div(sp.e_b - sp.s_b, BLK);
+    const int i_first = a.causal ? (c0 - sp.s_b) / BLK : 0;
+    // next q tile at or after `from` whose class is not FULL (Tq if none)
+    auto next_visit = [&](int from, bool& part) -> int {
+        for (int w0 = from; w0 < Tq; w0 += 64) {
+            const int i = w0 + lane;
+            bool v = false, p = false;
+            if (i < Tq) {
+                const int r0 = sp.s_b + i * BLK, r1 = min(r0 + BLK, sp.e_b);
+                const TileInfo ti = classify_tile(r0, r1, c0, c1, xe, a.causal);
+                v = ti.cls != CLS_FULL;
+                p = ti.cls == CLS_PARTIAL;
+            }
+            const uint64_t vm = __ballot(v);
+            if (vm) {
+                const int bit = __builtin_ctzll(vm);
+                part = ((__ballot(p) >> bit) & 1ull) != 0;
+                return w0 + bit;
+            }
+        }
+        return Tq;
+    };
+
+    QStage st;
+    bool part = false;
+    int i = next_visit(i_first, part);
+    if (i < Tq) load_qstage(a, h, sp.s_b + i * BLK, min(sp.s_b + (i + 1) * BLK, sp.e_b), tid, st);
+    const float sl2 = a.scale_log2;
+    while (i < Tq) {
+        const int r0 = sp.s_b + i * BLK;
+        __syncthreads();   // every wave is done with the previous tile
+        store_qstage(st, tid);
+        __syncthreads();
+        bool npart = false;
+        const int ni = next_visit(i + 1, npart);
+        if (ni < Tq) load_qstage(a, h, sp.s_b + ni * BLK, min(sp.s_b + (ni + 1) * BLK, sp.e_b), tid, st);
+
+        // S = Q K^T and dP = dO V^T: register e of result t is row
+        // 32t + 8(e>>2) + 4hh + (e&3) of the tile, column = this lane's key
+        f32x16 sc[2], dp[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) { sc[t][e] = 0.f; dp[t][e] = 0.f; }
+        const char* qa = s_q + n * ROW_T + 16 * hh;
+        const char* ga = s_g + n * ROW_T + 16 * hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sc[t] = mfma(as_bf16x8(*(const u32x4*)(qa + 32 * t * ROW_T + 32 * s)), kf[s], sc[t]);
+                dp[t] = mfma(as_bf16x8(*(const u32x4*)(ga + 32 * t * ROW_T + 32 * s)), vf[s], dp[t]);
+            }
+        // P = exp2(S scale log2e - lse2), masked pairs 0; dS = P (dP - Delta)
+        bf16x8 pb[2][2], db[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 l4 = *(const float4*)(s_l2 + 32 * t + 8 * j + 4 * hh);
+                const float4 d4 = *(const float4*)(s_dl + 32 * t + 8 * j + 4 * hh);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int e = 4 * j + c;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][e], sl2, -lv[c]));
+                    if (part) {
+                        const int row = r0 + 32 * t + 8 * j + 4 * hh + c;
+                        const bool m = (a.causal && kj > row) || (mv.lts <= row && row < mv.lte) ||
+                                       (mv.uts <= row && row < mv.ute);
+                        p = m ? 0.f : p;
+                    }
+                    const float ds = p * (dp[t][e] - dv4[c]);
+                    pb[t][e >> 3][e & 7] = (__bf16)p;
+                    db[t][e >> 3][e & 7] = (__bf16)ds;
+                }
+            }
+        // dV^T += dO^T P, dK^T += Q^T dS: 16-row groups kg of the tile
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                dv[dt] = mfma(tr_frag<ROW_T>(s_g, kg, dt, lane), pb[kg >> 1][kg & 1], dv[dt]);
+                dk[dt] = mfma(tr_frag<ROW_T>(s_q, kg, dt, lane), db[kg >> 1][kg & 1], dk[dt]);
+            }
+        i = ni;
+        part = npart;
+    }
+
+    // dK = scale dK^T, dV = dV^T: lane = key kj, channels 32dt + 8g + 4hh + 0..3
+    if (kvalid) {
+        const int64_t off = ((int64_t)kj * a.H + h) * HD;
+        uint16_t* dkp = (uint16_t*)a.dk + off;
+        uint16_t* dvp = (uint16_t*)a.dv + off;
+        const float sc = a.scale;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = 32 * dt + 8 * g + 4 * hh;
+                u32x2 x, y;
+                x.x = bf16_bits(dk[dt][4 * g] * sc) | (bf16_bits(dk[dt][4 * g + 1] * sc) << 16);
+                x.y = bf16_bits(dk[dt][4 * g + 2] * sc) | (bf16_bits(dk[dt][4 * g + 3] * sc) << 16);
+                y.x = bf16_bits(dv[dt][4 * g]) | (bf16_bits(dv[dt][4 * g + 1]) << 16);
+                y.y = bf16_bits(dv[dt][4 * g + 2]) | (bf16_bits(dv[dt][4 * g + 3]) << 16);
+                *(u32x2*)(dkp + c) = x;
+                *(u32x2*)(dvp + c) = y;
+            }
+    }
+}
+
+// ---- dQ --------------------------------------------------------------------
+__shared__ __attribute__((aligned(16))) char s_k[BLK * ROW_T];
+__shared__ __attribute__((aligned(16))) char s_v[BLK * ROW_R];
+
+// One key block's staging data in registers: 4 chunks of K and of V per
+// thread (rows past the sequence are zero), and for partial blocks the
+// mask intervals of key c0 + lane (every wave loads its own copy).
+struct KStage {
+    u32x4 k[4], v[4];
+    Vec4 mv;
+};
+__device__ inline void load_kstage(const BwdArgs& a, int h, int c0, int c1, bool part, int tid, KStage& st) {
+    const int64_t rsb = (int64_t)a.H * 2 * HD;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int c = tid + NTH * u, row = c >> 4, ch = c & 15;
+        st.k[u] = u32x4{0, 0, 0, 0};
+        st.v[u] = u32x4{0, 0, 0, 0};
+        if (c0 + row < c1) {
+            const int64_t off = (int64_t)(c0 + row) * rsb + (int64_t)h * 2 * HD + 16 * ch;
+            st.k[u] = *(const u32x4*)((const char*)a.k + off);
+            st.v[u] = *(const u32x4*)((const char*)a.v + off);
+        }
+    }
+    st.mv = Vec4{0, 0, 0, 0};
+    const int key = c0 + (tid & 63);
+    if (part && key < c1) st.mv = fill_column(a.sv, a.n_vec, a.causal, a.N, key);
+}
+__device__ inline void store_kstage(const KStage& st, int tid) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int c = tid + NTH * u, row = c >> 4, ch = c & 15;
+        *(u32x4*)(s_k + row * ROW_T + 16 * ch) = st.k[u];
+        *(u32x4*)(s_v + row * ROW_R + 16 * ch) = st.v[u];
+    }
+}
+
+__global__ __launch_bounds__(NTH, 1) void fm_bwd_dq_kernel(BwdArgs a) {
+    const int h = blockIdx.y;
+    const Span sp = span_of(a, blockIdx.x);
+    if (!sp.ok) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, hh = lane >> 5;
+    const int r0 = sp.lo, r1 = sp.hi;
+    const int q0 = r0 + 32 * w;          // the wave's first row
+    const int qr = q0 + n;               // this lane's query
+    const bool qvalid = qr < r1;
+
+    // Q and dO fragments (B operands: column = query n, channels 16s + 8hh),
+    // lse in log2 units (+inf: no allowed key or no row, so P = 0) and Delta
+    bf16x8 qf[8], gf[8];
+    float l2 = INFINITY, dl = 0.f;
+    {
+        const int64_t off = ((int64_t)qr * a.H + h) * 2 * HD + 16 * hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            qf[s] = as_bf16x8(qvalid ? *(const u32x4*)((const char*)a.q + off + 32 * s) : u32x4{0, 0, 0, 0});
+            gf[s] = as_bf16x8(qvalid ? *(const u32x4*)((const char*)a.dout + off + 32 * s) : u32x4{0, 0, 0, 0});
+        }
+        if (qvalid) {
+            const float l = a.lse[(int64_t)h * a.N + qr];
+            l2 = l == -INFINITY ? INFINITY : l * LOG2E;
+            dl = a.delta[(int64_t)h * a.N + qr];
+        }
+    }
+    f32x16 dq[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dq[dt][e] = 0.f;
+
+    const int Tc = ceil_div(sp.e_b - sp.s_b, BLK);
+    const int kb_end = a.causal ? min(Tc, (r1 - 1 - sp.s_b) / BLK + 1) : Tc;
+    const int32_t* xb = a.extrema + (int64_t)a.kb_off[sp.b] * 8;
+    auto next_visit = [&](int from, bool& part) -> int {
+        for (int w0 = from; w0 < kb_end; w0 += 64) {
+            const int kb = w0 + lane;
+            bool v = false, p = false;
+            if (kb < kb_end) {
+                const int4 e0 = *(const int4*)(xb + (int64_t)kb * 8);
+                const int4 e1 = *(const int4*)(xb + (int64_t)kb * 8 + 4);
+                const int x[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+                const int c0 = sp.s_b + kb * BLK, c1 = min(c0 + BLK, sp.e_b);
+                const TileInfo ti = classify_tile(r0, r1, c0, c1, x, a.causal);
+                v = ti.cls != CLS_FULL;
+                p = ti.cls == CLS_PARTIAL;
+            }
+            const uint64_t vm = __ballot(v);
+            if (vm) {
+                const int bit = __builtin_ctzll(vm);
+                part = ((__ballot(p) >> bit) & 1ull) != 0;
+                return w0 + bit;
+            }
+        }
+        return kb_end;
+    };
+
+    KStage st;
+    bool part = false;
+    int kb = next_visit(0, part);
+    if (kb < kb_end) {
+        const int c0 = sp.s_b + kb * BLK;
+        load_kstage(a, h, c0, min(c0 + BLK, sp.e_b), part, tid, st);
+    }
+    const float sl2 = a.scale_log2;
+    while (kb < kb_end) {
+        const int c0 = sp.s_b + kb * BLK, c1 = min(c0 + BLK, sp.e_b);
+        __syncthreads();   // every wave is done with the previous block
+        store_kstage(st, tid);
+        // 32-row mask of key c0 + lane for this wave's rows (partial blocks)
+        uint32_t mk = 0;
+        if (part) {
+            const int key = c0 + lane;
+            mk = a.causal ? row_bits(0, key - q0) : 0u;
+            if (key >= c1) mk = 0xffffffffu;
+            mk |= row_bits(st.mv.lts - q0, st.mv.lte - q0) | row_bits(st.mv.uts - q0, st.mv.ute - q0);
+        }
+        __syncthreads();
+        bool npart = false;
+        const int nkb = next_visit(kb + 1, npart);
+        if (nkb < kb_end) {
+            const int nc0 = sp.s_b + nkb * BLK;
+            load_kstage(a, h, nc0, min(nc0 + BLK, sp.e_b), npart, tid, st);
+        }
+
+        // S^T = K Q^T and dP^T = V dO^T: register e of result t is key
+        // 32t + 8(e>>2) + 4hh + (e&3) of the block, column = this lane's query
+        f32x16 sc[2], dp[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) { sc[t][e] = 0.f; dp[t][e] = 0.f; }
+        const char* ka = s_k + n * ROW_T + 16 * hh;
+        const char* va = s_v + n * ROW_R + 16 * hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sc[t] = mfma(as_bf16x8(*(const u32x4*)(ka + 32 * t * ROW_T + 32 * s)), qf[s], sc[t]);
+                dp[t] = mfma(as_bf16x8(*(const u32x4*)(va + 32 * t * ROW_R + 32 * s)), gf[s], dp[t]);
+            }
+        if (part) {   // keys k and k + 4 of register e: the masks built by lanes k and k + 4
+            const int mki = (int)mk;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int k0 = 32 * t + 8 * (e >> 2) + (e & 3);
+                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(mki, k0);
+                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(mki, k0 + 4);
+                    sc[t][e] = select_lanes(sc[t][e], -INFINITY, lo, hi);
+                }
+        }
+        bf16x8 db[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][e], sl2, -l2));
+                db[t][e >> 3][e & 7] = (__bf16)(p * (dp[t][e] - dl));
+            }
+        // dQ^T += K^T dS^T: 16-key groups kg of the block
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                dq[dt] = mfma(tr_frag<ROW_T>(s_k, kg, dt, lane), db[kg >> 1][kg & 1], dq[dt]);
+        kb = nkb;
+        part = npart;
+    }
+
+    // dQ = scale dQ^T: lane = query qr, channels 32dt + 8g + 4hh + 0..3
+    if (qvalid) {
+        uint16_t* dqp = (uint16_t*)a.dq + ((int64_t)qr * a.H + h) * HD;
+        const float sc = a.scale;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 x;
+                x.x = bf16_bits(dq[dt][4 * g] * sc) | (bf16_bits(dq[dt][4 * g + 1] * sc) << 16);
+                x.y = bf16_bits(dq[dt][4 * g + 2] * sc) | (bf16_bits(dq[dt][4 * g + 3] * sc) << 16);
+                *(u32x2*)(dqp + 32 * dt + 8 * g + 4 * hh) = x;
+            }
+    }
+}
+
+}  // namespace bwd
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s) {
+    const int64_t nh = a.N * a.H;
+    if (nh > 0) {
+        const int64_t grid = (nh * 16 + bwd::NTH - 1) / bwd::NTH;
+        hipLaunchKernelGGL(bwd::fm_bwd_delta_kernel, dim3((unsigned)grid), dim3(bwd::NTH), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (kb_cap <= 0 || a.N == 0) return hipSuccess;
+    const dim3 grid((unsigned)kb_cap, (unsigned)a.H);
+    hipLaunchKernelGGL(bwd::fm_bwd_dkdv_kernel, grid, dim3(bwd::NTH), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd::fm_bwd_dq_kernel, grid, dim3(bwd::NTH), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace fm

@@ -90,4 +90,20 @@ hipError_t launch_fused_bf16(const AttnArgs& a, int n_cu, hipStream_t s);
 int fused_grid(int n_cu);
 hipError_t launch_attn_f32(const AttnArgs& a, int n_cu, hipStream_t s);
 
+// Backward launch arguments (bf16, head_dim 128).
+struct BwdArgs {
+    const void* q; const void* k; const void* v; const void* out; const void* dout; const float* lse;
+    void* dq; void* dk; void* dv;
+    float* delta;              // workspace: fp32 [H][N]
+    int64_t N; int H, B;
+    const int32_t* cu; const int32_t* sv; int n_vec; int causal;
+    float scale, scale_log2;   // scale, scale * log2(e)
+    const int32_t* kb_off; const int32_t* extrema; const int32_t* n_kb; const int32_t* status;
+};
+
+// Key block (columns per extrema row) of the backward's plan.
+constexpr int bwd_block_k() { return 64; }
+// Delta, then dK/dV, then dQ; kb_cap bounds the number of 64-key blocks.
+hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s);
+
 }  // namespace fm

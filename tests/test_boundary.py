@@ -125,3 +125,36 @@ def test_worklist_rejects_on_host(pv):
     assert L.fm_build_worklist(*args(S=-1)) == pv.FM_E_INVAL
     assert L.fm_build_worklist(*args(cu=None)) == pv.FM_E_INVAL
     assert L.fm_worklist_scratch_size(1000, 2, 3, 16, 16, 0) == lay.scratch_bytes
+
+
+def _bwd(pv, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dtype=pv.FM_BF16, N=256, H=2, D=128,
+             cu=FAKE, B=1, sv=FAKE, n_vec=1, causal=1, scale=0.1, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    rc = pv._lib.fm_attn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dtype"], a["N"], a["H"],
+                             a["D"], a["cu"], a["B"], a["sv"], a["n_vec"], a["causal"], ctypes.c_float(a["scale"]),
+                             a["dq"], a["dk"], a["dv"], a["ws"], a["ws_bytes"], None)
+    return rc, pv._lib.fm_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_vec=4), 1), (dict(n_vec=1, causal=0), 1), (dict(D=64), 2), (dict(dtype=1, D=32), 2),
+    (dict(dtype=9), 2), (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(cu=None), 1),
+    (dict(dout=None), 1), (dict(lse=None), 1), (dict(dk=None), 1), (dict(ws=None), 1),
+    (dict(ws_bytes=1024), 3), (dict(B=0), 1), (dict(H=0), 1), (dict(N=-1), 1),
+])
+def test_bwd_rejects_on_host(pv, kw, code):
+    rc, msg = _bwd(pv, **kw)
+    assert rc == code, msg
+    assert msg
+
+
+def test_bwd_workspace_size(pv):
+    """Header, kb_off, extrema at 64-key blocks, Delta fp32 [H][N]."""
+    L = pv._lib
+    n = L.fm_bwd_workspace_size(4352, 3, 2, 128, pv.FM_BF16)
+    assert n >= 256 + 4 * 4 + (4352 // 64 + 3) * 32 + 2 * 4352 * 4 and n % 256 == 0
+    assert L.fm_bwd_workspace_size(4352, 3, 2, 64, pv.FM_BF16) == 0
+    assert L.fm_bwd_workspace_size(4352, 0, 2, 128, pv.FM_BF16) == 0
+    assert L.fm_bwd_workspace_size(16, 1, 1, 32, pv.FM_F32) == 0

@@ -1,0 +1,175 @@
+"""GPU parity of the backward (dq, dk, dv) through the C ABI against the fp64
+oracle's gradients, on the same bf16 inputs and output gradient.
+
+The forward's out and lse come from the library (the backward's inputs);
+the oracle recomputes everything from q, k, v and dout.  Bar: max |err| <=
+ATOL + RTOL * max |ref| per tensor (bf16 outputs and bf16 P, dS operands
+of the products), and exact zeros where no pair contributes.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-2
+RTOL = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def pv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import packed_varlen_masked_amd as pv
+    return pv
+
+
+def bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def run_bwd(pv, w, seed=0):
+    dt = torch.bfloat16
+    q, k, v = (bf16(x).cuda() for x in (w.q, w.k, w.v))
+    g = bf16(np.random.default_rng(seed + 77).standard_normal(w.q.shape, dtype=np.float32))
+    cu = torch.from_numpy(w.cu_seqlens.astype(np.int32)).cuda()
+    sv = torch.from_numpy(np.ascontiguousarray(w.startend.astype(np.int32))).cuda()
+    out, lse = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale))
+    dq, dk, dv = pv.attn_bwd(q, k, v, out, lse, g.cuda(), cu, sv, w.n_vec, w.causal, float(w.scale))
+    torch.cuda.synchronize()
+    return (dq.float().cpu().numpy(), dk.float().cpu().numpy(), dv.float().cpu().numpy()), g.float().numpy()
+
+
+def no_pairs(w):
+    """Rows that attend no key and keys no row attends (their gradients are
+    exactly zero: no pair contributes)."""
+    vecs = O.fill_vectors(w.startend, w.n_vec, w.causal, w.N)
+    cu = w.cu_seqlens.astype(np.int64)
+    row_empty = np.ones(w.N, bool)
+    col_empty = np.ones(w.N, bool)
+    for b in range(w.B):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if e > s:
+            ok = ~O.element_mask(np.arange(s, e), np.arange(s, e), vecs, w.causal)
+            row_empty[s:e] = ~ok.any(axis=1)
+            col_empty[s:e] = ~ok.any(axis=0)
+    return row_empty, col_empty
+
+
+def compare(w, got, g, tag=""):
+    ref = O.attention_bwd(w.q, w.k, w.v, g, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)
+    row_empty, col_empty = no_pairs(w)
+    for nm, a, r, z in zip(("dq", "dk", "dv"), got, ref, (row_empty, col_empty, col_empty)):
+        err = float(np.max(np.abs(a - r))) if a.size else 0.0
+        mx = float(np.max(np.abs(r))) if r.size else 0.0
+        say("  %s %s: max|err|=%.3e max|ref|=%.3e" % (tag, nm, err, mx))
+        assert np.all(np.isfinite(a))
+        assert err <= ATOL + RTOL * mx, (nm, err, mx)
+        assert np.all(a[z] == 0.0), nm
+    return ref
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_bwd_random(pv, seed):
+    w = W.random_case(700 + seed, N_max=300, H=2, D=128, dtype=W.BF16, allow_empty=True)
+    say("bwd random", seed, "N=%d B=%d causal=%d n_vec=%d" % (w.N, w.B, w.causal, w.n_vec))
+    got, g = run_bwd(pv, w, seed)
+    compare(w, got, g, "random %d" % seed)
+
+
+@pytest.mark.parametrize("lens", [[100, 37, 300, 1], [64, 128, 65]])
+def test_bwd_documents(pv, lens):
+    w = W.document_workload(lens, H=2, seed=21)
+    say("bwd documents", lens)
+    got, g = run_bwd(pv, w)
+    compare(w, got, g, "docs")
+
+
+def test_bwd_varlen_workload(pv):
+    w = W.make_config(2)
+    say("bwd varlen workload N=%d" % w.N)
+    got, g = run_bwd(pv, w)
+    compare(w, got, g, "cfg2")
+
+
+@pytest.mark.parametrize("k,N,H", [(3, 3000, 2), (4, 3000, 1), (5, 9000, 1)])
+def test_bwd_reduced_configs(pv, k, N, H):
+    w = W.make_config(k, N=N, H=H)
+    say("bwd config", k, "N=%d H=%d" % (w.N, w.H))
+    got, g = run_bwd(pv, w)
+    compare(w, got, g, "cfg%d" % k)
+
+
+def test_bwd_deterministic(pv):
+    w = W.document_workload([300, 700], H=2, seed=5)
+    a, _ = run_bwd(pv, w)
+    b, _ = run_bwd(pv, w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_bwd_sft_full_one_head(pv):
+    """SFT packing workload at full size (16384 tokens, 32 heads): head 0's
+    dq, dk, dv against the full oracle (heads are independent)."""
+    w = W.make_config(3)
+    say("bwd SFT full N=%d H=%d" % (w.N, w.H))
+    got, g = run_bwd(pv, w)
+    h = 0
+    w1 = W.Workload(w.name + "_h0", w.N, 1, w.D, w.dtype, w.causal, w.n_vec, w.cu_seqlens, w.startend, w.scale,
+                    w.q[:, h:h + 1], w.k[:, h:h + 1], w.v[:, h:h + 1])
+    compare(w1, tuple(x[:, h:h + 1] for x in got), g[:, h:h + 1], "cfg3 head 0")
+
+
+def test_bwd_prefix_window_full_sampled(pv):
+    """Prefix-LM + window workload at full size (131072 tokens, 8 heads):
+    sampled dq rows against the oracle one by one, and for every sequence and
+    head two identities of the exact gradients: sum_j dk_j = 0 (softmax is
+    unchanged when all keys move by one vector) and sum_j dv_j = sum of dout
+    over the rows that attend (each row's P sums to 1)."""
+    w = W.make_config(5)
+    say("bwd prefix-window full N=%d H=%d" % (w.N, w.H))
+    (dq, dk, dv), g = run_bwd(pv, w)
+    rng = np.random.default_rng(3)
+    cu = w.cu_seqlens.astype(np.int64)
+    rows = sorted(set(int(x) for x in rng.integers(0, w.N, 48)) | {int(cu[b]) for b in range(w.B)} |
+                  {int(cu[b + 1]) - 1 for b in range(w.B)})
+    heads = [int(x) for x in rng.integers(0, w.H, len(rows))]
+    ref = O.attention_bwd_rows(w.q, w.k, w.v, g, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale, rows, heads)
+    got = np.stack([dq[r, h] for r, h in zip(rows, heads)])
+    err, mx = float(np.max(np.abs(got - ref))), float(np.max(np.abs(ref)))
+    say("  sampled dq rows: %d, max|err|=%.3e max|ref|=%.3e" % (len(rows), err, mx))
+    assert err <= ATOL + RTOL * mx
+    row_empty, _ = no_pairs_rows(w)
+    for b in range(w.B):
+        s, e = int(cu[b]), int(cu[b + 1])
+        sk = dk[s:e].astype(np.float64).sum(axis=0)
+        sv_ = dv[s:e].astype(np.float64).sum(axis=0)
+        gs = g[s:e][~row_empty[s:e]].astype(np.float64).sum(axis=0)
+        ek = float(np.max(np.abs(sk)) / max(1.0, float(np.abs(dk[s:e]).sum(axis=0).max())))
+        ev = float(np.max(np.abs(sv_ - gs)) / max(1.0, float(np.abs(dv[s:e]).sum(axis=0).max())))
+        say("  seq %d (L=%d): |sum dk| / sum|dk| = %.2e, |sum dv - sum dout| / sum|dv| = %.2e" % (b, e - s, ek, ev))
+        assert ek <= 1e-2 and ev <= 1e-2
+
+
+def no_pairs_rows(w):
+    """Rows with no allowed key, per token (any size: one pass per row block)."""
+    vecs = O.fill_vectors(w.startend, w.n_vec, w.causal, w.N)
+    cu = w.cu_seqlens.astype(np.int64)
+    empty = np.ones(w.N, bool)
+    for b in range(w.B):
+        s, e = int(cu[b]), int(cu[b + 1])
+        cols = np.arange(s, e)
+        for r0 in range(s, e, 1024):
+            rr = np.arange(r0, min(r0 + 1024, e))
+            empty[rr] = O.element_mask(rr, cols, vecs, w.causal).all(axis=1)
+    return empty, None

@@ -453,6 +453,19 @@ def test_bwd_q_zero_closed_form():
     assert np.allclose(dv, ref, atol=1e-13, rtol=0)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_bwd_rows_match_full(seed):
+    """The one-row-at-a-time dq equals the full backward's rows (the same
+    definition evaluated two ways), empty rows included."""
+    w = W.random_case(500 + seed, N_max=60, H=2, D=8, dtype=W.F32, allow_empty=True)
+    G = np.random.default_rng(seed).standard_normal(w.q.shape)
+    dq, _, _ = O.attention_bwd(w.q, w.k, w.v, G, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)
+    rows = list(range(w.N)) * 2
+    heads = [0] * w.N + [1] * w.N
+    r = O.attention_bwd_rows(w.q, w.k, w.v, G, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale, rows, heads)
+    assert np.allclose(r, np.stack([dq[i, h] for i, h in zip(rows, heads)]), atol=1e-12, rtol=0)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_bwd_invariants(seed):
     """Softmax is unchanged when one vector is added to every key of a
