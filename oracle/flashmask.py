@@ -440,3 +440,41 @@ def effective_flops(pairs_per_head: int, H: int, D: int) -> int:
     The FlashMask article reports TFLOPs/s (§4.4) without defining the
     count; masked pairs and softmax work are not counted."""
     return 4 * D * H * int(pairs_per_head)
+
+
+# ------------------------------------------------------ rotary embedding
+def rope(x, cu_seqlens, cos, sin, inverse: bool = False):
+    """Rotary position embedding of packed rows, float64.
+
+    x: [N, H, D] (D even); cos, sin: [max_pos, D/2] tables (any float
+    dtype, widened exactly).  Unsloth packing blog, fused QK RoPE section:
+    out = x cos + rotate_half(x) sin, where rotate_half(x) = x R with
+    R = [[0, I], [-I, 0]] (halves x1 = x[:D/2], x2 = x[D/2:] give
+    [-x2, x1]); the tables repeat over the two halves.  Positions restart
+    at 0 in every packed sample (the blog's packing section: the kernel
+    resets position ids): row i of sequence b has position i - cu[b].
+    The backward of the rotation is the same map with sin negated (the
+    blog: R^T replaces R), `inverse=True`.
+    Pinned by: the 2-D rotation matrix (D = 2), norm preservation of
+    every (j, j + D/2) pair, inverse after forward = identity, relative
+    positions (<rope(q, m), rope(k, n)> depends only on m - n) and packed =
+    separate sequences.
+    """
+    x = np.asarray(x, np.float64)
+    N, H, D = x.shape
+    if D % 2:
+        raise ValueError("D must be even")
+    cu = np.asarray(cu_seqlens, np.int64)
+    c = np.asarray(cos, np.float64)
+    s = np.asarray(sin, np.float64)
+    if inverse:
+        s = -s
+    pos = np.zeros(N, np.int64)
+    for b in range(len(cu) - 1):
+        pos[cu[b]:cu[b + 1]] = np.arange(cu[b + 1] - cu[b])
+    if N and pos.max() >= c.shape[0]:
+        raise ValueError("position beyond the tables")
+    cc = np.concatenate([c[pos], c[pos]], axis=1)[:, None, :]
+    ss = np.concatenate([s[pos], s[pos]], axis=1)[:, None, :]
+    rot = np.concatenate([-x[..., D // 2:], x[..., :D // 2]], axis=-1)
+    return x * cc + rot * ss

@@ -493,6 +493,58 @@ def test_bwd_invariants(seed):
             assert np.allclose(a, bb[s:e], atol=1e-12, rtol=0)
 
 
+# --------------------------------------------------------------- rotary
+def test_rope_2d_rotation():
+    """D = 2: each (x0, x1) pair turns by the table's angle, as the 2-D
+    rotation matrix [[c, s], [-s, c]] acting on the row vector."""
+    rng = np.random.default_rng(0)
+    ang = rng.uniform(-np.pi, np.pi, 9)
+    cos, sin = np.cos(ang)[:, None], np.sin(ang)[:, None]
+    x = rng.standard_normal((9, 3, 2))
+    got = O.rope(x, [0, 9], cos, sin)
+    for i in range(9):
+        M = np.array([[np.cos(ang[i]), np.sin(ang[i])], [-np.sin(ang[i]), np.cos(ang[i])]])
+        assert np.allclose(got[i], x[i] @ M, atol=1e-14)
+
+
+def test_rope_norms_inverse_reset():
+    """Every (j, j + D/2) pair keeps its length; the map with sin negated
+    (the packing blog's backward) undoes it; positions restart per packed
+    sample, so packed = each sample alone."""
+    rng = np.random.default_rng(1)
+    D, H = 16, 3
+    lens = [5, 0, 11, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = rng.standard_normal((int(cu[-1]), H, D))
+    cos, sin = W.rope_tables(16, D)
+    y = O.rope(x, cu, cos, sin)
+    n0 = x[..., :D // 2] ** 2 + x[..., D // 2:] ** 2
+    n1 = y[..., :D // 2] ** 2 + y[..., D // 2:] ** 2
+    assert np.allclose(n0, n1, rtol=1e-6)     # tables are float32: cos^2 + sin^2 = 1 to ~1e-7
+    assert np.allclose(O.rope(y, cu, cos, sin, inverse=True), x, atol=1e-6)
+    for b in range(len(lens)):
+        s, e = int(cu[b]), int(cu[b + 1])
+        assert np.array_equal(O.rope(x[s:e], [0, e - s], cos, sin), y[s:e])
+
+
+def test_rope_relative_positions():
+    """With the usual angle tables <rope(q, m), rope(k, n)> depends only on
+    m - n: scores see relative positions."""
+    rng = np.random.default_rng(2)
+    D = 32
+    cos, sin = W.rope_tables(64, D)
+    q, k = rng.standard_normal((1, 1, D)), rng.standard_normal((1, 1, D))
+
+    def at(x, p):   # x placed at position p of a sequence of length p + 1
+        z = np.zeros((p + 1, 1, D))
+        z[p] = x[0]
+        return O.rope(z, [0, p + 1], cos, sin)[p, 0]
+    for m, n, c in [(10, 3, 0), (40, 33, 7), (5, 5, 20)]:
+        a = at(q, m) @ at(k, n)
+        b = at(q, m - n + c) @ at(k, c)
+        assert abs(a - b) < 1e-4 * (1 + abs(a))
+
+
 # ------------------------------------------------------------- worklist
 @pytest.mark.parametrize("seed", range(8))
 @pytest.mark.parametrize("S", [0, 1, 2, 3, 5])

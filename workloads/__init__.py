@@ -36,7 +36,7 @@ from typing import List, Optional
 import numpy as np
 
 __all__ = ["Workload", "make_config", "make_lengths", "PAGE_LTS", "PAGE_LTE",
-           "causal_document_vectors", "shared_question_vectors", "PACKINGS", "packed_as",
+           "causal_document_vectors", "shared_question_vectors", "PACKINGS", "packed_as", "rope_tables",
            "prefix_window_vectors", "random_case", "CONFIG_IDS"]
 
 # The 16-column causal example of the FlashMask article, §2.2 (its table is
@@ -359,3 +359,12 @@ def packed_as(w: Workload, kind: str) -> Workload:
                    spread(w.q), spread(w.k), spread(w.v), dict(w.meta))
     out.meta.update(packing=kind, real_rows=real)
     return out
+
+
+def rope_tables(max_pos: int, D: int, base: float = 10000.0):
+    """cos / sin tables [max_pos, D/2] (float32) of the usual rotary angles
+    p * base^(-2j / D): the input the rotary kernel reads (the pages leave
+    the angles to the model; this is the common choice)."""
+    j = np.arange(D // 2, dtype=np.float64)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * base ** (-2.0 * j / D)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
