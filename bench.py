@@ -59,6 +59,8 @@ def parse():
                          "with cu = [0, N], zero-padded, zero-padded with the padding masked), step time each")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward step: time the backward (dq, dk, dv) on the workload")
+    ap.add_argument("--rope", action="store_true",
+                    help="instead of the forward step: time the fused q/k rotary embedding on the workload")
     ap.add_argument("--packings", default=",".join(("varlen", "mask_only", "padded", "padded_masked")),
                     help="comma-separated packings the packing sweep runs")
     ap.add_argument("--preprocess-sweep", action="store_true",
@@ -371,6 +373,44 @@ def backward_bench(args):
           flush=True)
 
 
+def rope_bench(args):
+    """The fused rotary embedding of the workload's q and k in place (one
+    launch for both, positions restarting per document).  HBM-bound:
+    algorithmic bytes = q and k read and written once, plus one cos and one
+    sin row (D/2 fp32 each) per token."""
+    import torch
+    import workloads as W
+    import packed_varlen_masked_amd as pv
+    w = W.make_config(args.config, seed=args.seed)
+    dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float32
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(w.q).to(dt).to(dev)
+    k = torch.from_numpy(w.k).to(dt).to(dev)
+    cu = torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(dev)
+    cos, sin = (torch.from_numpy(t).to(dev) for t in W.rope_tables(int(w.lengths.max()), w.D))
+
+    def step():   # forward then inverse, so the data stays bounded over many steps
+        pv.rope_qk_(q, k, cu, cos, sin)
+        pv.rope_qk_(q, k, cu, cos, sin, inverse=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms2, host_ms, ahead = time_calls(step, args.steps)
+    ms = ms2 / 2
+    esz = 2 if dt == torch.bfloat16 else 4
+    nbytes = 2 * 2 * w.N * w.H * w.D * esz + w.N * w.D * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "fused q/k rotary embedding, achieved HBM GB/s (algorithmic bytes)",
+                      "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_call": round(ms, 6), "higher_is_better": True,
+                      "dtype": "bf16" if dt == torch.bfloat16 else "f32", "data": "synthetic (seeded N(0,1) q/k)",
+                      "config": {"workload": w.name, "N": w.N, "B": w.B, "Hq": w.H, "Hk": w.H, "D": w.D},
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                                   "frac": round(gbs / 8000.0, 4), "algorithmic_bytes": int(nbytes)},
+                      "timing": {"host_enqueue_ms_per_step": round(host_ms / 2, 4), "host_ran_ahead": ahead,
+                                 "what": "mean of a forward and an inverse call"}}), flush=True)
+
+
 def main():
     args = parse()
     if args.preprocess_sweep:
@@ -388,6 +428,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.rope:
+        rope_bench(args)
         return
     import torch
     import workloads as W

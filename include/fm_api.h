@@ -85,6 +85,7 @@ extern "C" {
 #define FM_STATUS_ORDER    0x2    /* cu_seqlens decreases somewhere         */
 #define FM_STATUS_CUN      0x4    /* cu_seqlens[B] != N                     */
 #define FM_STATUS_CAP      0x8    /* more key blocks than extrema_cap       */
+#define FM_STATUS_POS      0x10   /* fm_rope_qk: a position outside the tables */
 
 /* Returns the message of the last failing call on this thread ("" if none). */
 const char* fm_last_error(void);
@@ -315,6 +316,29 @@ int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, co
                 const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
                 float scale, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                 hipStream_t stream);
+
+/*
+ * Rotary position embedding of packed q and k, in place, one launch for
+ * both (Unsloth packing blog, fused QK RoPE section: one kernel for Q and
+ * K, positions that restart in every packed sample, in place).  Row i of
+ * sample b (cu_seqlens[b] <= i < cu_seqlens[b+1]) has position
+ * p = i - cu_seqlens[b]; with x1 = x[:D/2], x2 = x[D/2:] of every head,
+ *   x1 <- x1 cos[p] - x2 sin[p],   x2 <- x2 cos[p] + x1 sin[p]
+ * i.e. x cos + rotate_half(x) sin; inverse != 0 negates sin (the
+ * backward: the gradient rows go through the same call).
+ *
+ * q: [N, Hq, head_dim], k: [N, Hk, head_dim], contiguous, of dtype FM_BF16
+ *   (fp32 arithmetic, rounded to bf16 once) or FM_F32; Hq or Hk may be 0
+ *   (the pointer is then unused); base pointers 16-byte aligned.
+ * head_dim: even, <= 512, and a multiple of 16 (bf16) or 8 (fp32).
+ * cos_table, sin_table: fp32 [max_pos][head_dim / 2], 16-byte aligned.
+ * cu_seqlens: int32 [B+1] device, valid as for fm_attn_fwd.
+ * status: nullable int32 device word; rows whose position falls outside
+ *   [0, max_pos) are left unchanged and FM_STATUS_POS is OR-ed into it.
+ */
+int fm_rope_qk(void* q, void* k, int dtype, int64_t N, int Hq, int Hk, int head_dim,
+               const int32_t* cu_seqlens, int B, const float* cos_table, const float* sin_table,
+               int64_t max_pos, int inverse, int32_t* status, hipStream_t stream);
 
 /* Test helper: synchronises `stream` and copies the workspace's status
  * word to *status (0 = the device data was valid). */

@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(HERE, "libflashmask_mi355.so")
 FM_OK, FM_E_INVAL, FM_E_UNSUPPORTED, FM_E_WORKSPACE, FM_E_HIP = 0, 1, 2, 3, 4
 FM_BF16, FM_F32 = 0, 1
 FM_FLAG_NO_SKIP, FM_FLAG_PLAN_READY = 0x1, 0x2
+FM_STATUS_CU0, FM_STATUS_ORDER, FM_STATUS_CUN, FM_STATUS_CAP, FM_STATUS_POS = 0x1, 0x2, 0x4, 0x8, 0x10
 FULL, PARTIAL, UNMASKED = 0, 1, 2
 ITEM_FIELDS = ("seq", "head", "q_tile", "kb_begin", "kb_end", "split_idx", "n_splits", "cost",
                "seq_start", "seq_end", "kb_base", "split0_slot", "zero0", "zero1", "zero2", "zero3")
@@ -79,6 +80,7 @@ def _load():
         "fm_fused_path": (I, [I64, I, I, I, I, I, I, I, U]),
         "fm_bwd_workspace_size": (SZ, [I64, I, I, I, I]),
         "fm_attn_bwd": (I, [P, P, P, P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, P, P, SZ, P]),
+        "fm_rope_qk": (I, [P, P, I, I64, I, I, I, P, I, P, P, I64, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -91,7 +93,7 @@ _lib = _load()
 EXPORTED = ("fm_last_error", "fm_version", "fm_self_check", "fm_get_tile_config", "fm_auto_split",
             "fm_workspace_layout", "fm_workspace_size", "fm_worklist_scratch_size",
             "fm_preprocess_mask", "fm_build_worklist", "fm_build_plan", "fm_attn_fwd",
-            "fm_read_status", "fm_fused_path", "fm_bwd_workspace_size", "fm_attn_bwd")
+            "fm_read_status", "fm_fused_path", "fm_bwd_workspace_size", "fm_attn_bwd", "fm_rope_qk")
 
 
 def _check(rc: int):
@@ -377,6 +379,36 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
                             _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream()))
     return dq, dk, dv
+
+
+def rope_qk_(q: Optional[torch.Tensor], k: Optional[torch.Tensor], cu_seqlens: torch.Tensor,
+             cos: torch.Tensor, sin: torch.Tensor, inverse: bool = False,
+             status: Optional[torch.Tensor] = None):
+    """Rotary embedding of packed q [N, Hq, D] and k [N, Hk, D] in place
+    (bf16 or fp32, contiguous; either may be None), positions restarting in
+    every sample of cu_seqlens; cos, sin: fp32 [max_pos, D/2].  inverse=True
+    negates sin (the backward).  status: optional int32 [1] device tensor
+    that receives FM_STATUS_POS for positions outside the tables."""
+    ref = q if q is not None else k
+    if ref is None:
+        raise FMError(FM_E_INVAL, "q and k are both None")
+    N, _, D = ref.shape
+    for t, nm in ((q, "q"), (k, "k")):
+        if t is not None and (t.dim() != 3 or t.shape[0] != N or t.shape[2] != D or t.dtype != ref.dtype
+                              or not t.is_contiguous() or not t.is_cuda):
+            raise FMError(FM_E_INVAL, "%s must be a contiguous CUDA [N, H, D] tensor like the other" % nm)
+    for t, nm in ((cos, "cos"), (sin, "sin")):
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != D // 2 or not t.is_contiguous():
+            raise FMError(FM_E_INVAL, "%s must be contiguous fp32 [max_pos, D/2]" % nm)
+    if cos.shape != sin.shape:
+        raise FMError(FM_E_INVAL, "cos and sin must have one shape")
+    cu = _i32(cu_seqlens, "cu_seqlens")
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 1 or not status.is_cuda):
+        raise FMError(FM_E_INVAL, "status must be an int32 CUDA tensor")
+    _check(_lib.fm_rope_qk(_ptr(q), _ptr(k), _dtype_code(ref.dtype), N, 0 if q is None else q.shape[1],
+                           0 if k is None else k.shape[1], D, _ptr(cu), cu.numel() - 1, _ptr(cos), _ptr(sin),
+                           cos.shape[0], int(bool(inverse)), _ptr(status), _stream()))
+    return q, k
 
 
 def read_status(workspace: torch.Tensor) -> int:

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libflashmask_mi355.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["fm_api.cpp", "fm_plan.hip", "fm_attn_bf16.hip", "fm_attn_f32.hip", "fm_bwd_bf16.hip"]
+SOURCES = ["fm_api.cpp", "fm_plan.hip", "fm_attn_bf16.hip", "fm_attn_f32.hip", "fm_bwd_bf16.hip", "fm_rope.hip"]
 ARCH = "gfx950"
 
 

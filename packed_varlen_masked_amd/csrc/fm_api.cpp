@@ -540,6 +540,33 @@ int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, co
     return ok();
 }
 
+int fm_rope_qk(void* q, void* k, int dtype, int64_t N, int Hq, int Hk, int head_dim, const int32_t* cu_seqlens,
+               int B, const float* cos_table, const float* sin_table, int64_t max_pos, int inverse,
+               int32_t* status, hipStream_t stream) {
+    if (B < 1 || B > FM_MAX_SEQS) return fail(FM_E_INVAL, "B=%d outside [1, %d]", B, FM_MAX_SEQS);
+    if (N < 0 || N >= INT32_MAX) return fail(FM_E_INVAL, "N=%lld outside [0, 2^31-1)", (long long)N);
+    if (Hq < 0 || Hk < 0 || Hq + Hk < 1) return fail(FM_E_INVAL, "need Hq, Hk >= 0 and Hq + Hk >= 1");
+    if (dtype != FM_BF16 && dtype != FM_F32) return fail(FM_E_UNSUPPORTED, "unknown dtype %d", dtype);
+    const int mult = dtype == FM_BF16 ? 16 : 8;
+    if (head_dim < mult || head_dim > 512 || head_dim % mult)
+        return fail(FM_E_UNSUPPORTED, "head_dim %d: must be a multiple of %d in [%d, 512]", head_dim, mult, mult);
+    if (max_pos < 1) return fail(FM_E_INVAL, "max_pos must be >= 1");
+    if ((int64_t)N * (Hq + Hk) * (head_dim / 2) > ((int64_t)1 << 40)) return fail(FM_E_INVAL, "problem too large");
+    if (!cu_seqlens) return fail(FM_E_INVAL, "null pointer argument");
+    if (N > 0 && (!cos_table || !sin_table || (Hq > 0 && !q) || (Hk > 0 && !k)))
+        return fail(FM_E_INVAL, "null pointer argument");
+    auto misaligned = [](const void* p) { return p && ((uintptr_t)p & 15); };
+    if (misaligned(q) || misaligned(k) || misaligned(cos_table) || misaligned(sin_table))
+        return fail(FM_E_INVAL, "q, k and the tables must be 16-byte aligned");
+    if (N == 0) return ok();
+    fm::RopeArgs a;
+    a.q = q; a.k = k; a.dtype = dtype; a.N = N; a.Hq = Hq; a.Hk = Hk; a.D = head_dim; a.B = B;
+    a.cu = cu_seqlens; a.cos_t = cos_table; a.sin_t = sin_table; a.max_pos = max_pos;
+    a.inverse = inverse ? 1 : 0; a.status = status;
+    int rc = hip_check(fm::launch_rope(a, stream), "rope launch");
+    return rc ? rc : ok();
+}
+
 int fm_read_status(const void* workspace, hipStream_t stream, int32_t* status) {
     if (!workspace || !status) return fail(FM_E_INVAL, "null pointer argument");
     int rc;

@@ -101,6 +101,15 @@ struct BwdArgs {
     const int32_t* kb_off; const int32_t* extrema; const int32_t* n_kb; const int32_t* status;
 };
 
+// Rotary embedding of q and k rows in place (bf16 or fp32).
+struct RopeArgs {
+    void* q; void* k; int dtype;
+    int64_t N; int Hq, Hk, D, B;
+    const int32_t* cu; const float* cos_t; const float* sin_t; int64_t max_pos;
+    int inverse; int32_t* status;
+};
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
+
 // Key block (columns per extrema row) of the backward's plan.
 constexpr int bwd_block_k() { return 64; }
 // Delta, then dK/dV, then dQ; kb_cap bounds the number of 64-key blocks.

@@ -158,3 +158,24 @@ def test_bwd_workspace_size(pv):
     assert L.fm_bwd_workspace_size(4352, 3, 2, 64, pv.FM_BF16) == 0
     assert L.fm_bwd_workspace_size(4352, 0, 2, 128, pv.FM_BF16) == 0
     assert L.fm_bwd_workspace_size(16, 1, 1, 32, pv.FM_F32) == 0
+
+
+def _rope(pv, **kw):
+    a = dict(q=FAKE, k=FAKE, dtype=pv.FM_BF16, N=64, Hq=2, Hk=1, D=128, cu=FAKE, B=1, cos=FAKE, sin=FAKE,
+             max_pos=64, inverse=0, status=None)
+    a.update(kw)
+    rc = pv._lib.fm_rope_qk(a["q"], a["k"], a["dtype"], a["N"], a["Hq"], a["Hk"], a["D"], a["cu"], a["B"],
+                            a["cos"], a["sin"], a["max_pos"], a["inverse"], a["status"], None)
+    return rc, pv._lib.fm_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=120), 2), (dict(D=8), 2), (dict(dtype=1, D=12), 2), (dict(D=1024), 2), (dict(dtype=5), 2),
+    (dict(Hq=0, Hk=0), 1), (dict(Hq=-1), 1), (dict(B=0), 1), (dict(N=-1), 1), (dict(max_pos=0), 1),
+    (dict(cu=None), 1), (dict(cos=None), 1), (dict(q=None), 1), (dict(q=ctypes.c_void_p(4104)), 1),
+    (dict(sin=ctypes.c_void_p(4100)), 1),
+])
+def test_rope_rejects_on_host(pv, kw, code):
+    rc, msg = _rope(pv, **kw)
+    assert rc == code, msg
+    assert msg
