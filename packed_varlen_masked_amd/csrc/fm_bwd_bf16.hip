@@ -15,15 +15,16 @@
 //
 // Layout and schedule (this file's own):
 //   * delta kernel: Delta[h, i] = <dO_i, O_i> in fp32, 16 lanes per row.
-//   * dK/dV kernel: one workgroup of 4 waves per (128-key tile, head);
-//     wave w owns keys 32w..32w+31 and holds their K and V fragments in
-//     registers.  It walks the sequence's 64-row q tiles that are not FULL
-//     against its key tile, stages Q, dO, lse and Delta of each in LDS (the
-//     next tile is loaded into registers while the current one is used),
-//     computes S = Q K^T and dP = dO V^T with one key per lane (so the
-//     key's mask intervals are lane constants), and accumulates
-//     dV^T = dO^T P and dK^T = Q^T dS with the LDS transpose read.
-//   * dQ kernel: one workgroup of 4 waves per (128-query tile, head); wave
+//   * dK/dV kernel: one workgroup of 8 waves per (128-key tile, head);
+//     wave 4g + t owns keys 32t..32t+31 (K and V fragments in registers)
+//     and query rows 32g..32g+31 of each staged tile.  It walks the
+//     sequence's 64-row q tiles that are not FULL against its key tile,
+//     stages Q, dO, lse and Delta of each in LDS (the next tile is loaded
+//     into registers while the current one is used), computes S = Q K^T
+//     and dP = dO V^T with one key per lane (so the key's mask intervals
+//     are lane constants), and accumulates dV^T = dO^T P and dK^T = Q^T dS
+//     with the LDS transpose read; the two row halves are summed in LDS.
+//   * dQ kernel: one workgroup of 8 waves per (256-query tile, head); wave
 //     w owns queries 32w..32w+31 with their Q and dO fragments, lse and
 //     Delta in registers.  It walks the visited 64-key blocks, stages K and
 //     V in LDS, computes S^T = K Q^T and dP^T = V dO^T with one query per
@@ -100,14 +101,15 @@ __device__ inline int seq_of_block(const int32_t* kb_off, int B, int x) {
     return lo;
 }
 
-// The 128-row (or 128-key) span of a workgroup: global block x and, when it
-// lies in the same sequence, block x + 1.  Workgroups of odd local blocks
-// have no span (their block belongs to the workgroup before).
+// The span of a workgroup: NB consecutive 64-row (or 64-key) blocks of one
+// sequence starting at global block x (fewer at the sequence end).  Only
+// workgroups whose local block index is a multiple of NB have a span.
 struct Span {
     bool ok;
     int b, s_b, e_b, lo, hi, x;
-    bool two;
+    bool two;   // block x + 1 lies in the sequence
 };
+template <int NB>
 __device__ inline Span span_of(const BwdArgs& a, int x) {
     Span sp;
     sp.ok = false;
@@ -116,13 +118,13 @@ __device__ inline Span span_of(const BwdArgs& a, int x) {
     if (x >= n_kb) return sp;
     sp.b = seq_of_block(a.kb_off, a.B, x);
     const int kb0 = a.kb_off[sp.b], kb1 = a.kb_off[sp.b + 1];
-    if ((x - kb0) & 1) return sp;
+    if ((x - kb0) % NB) return sp;
     sp.x = x;
     sp.two = x + 1 < kb1;
     sp.s_b = a.cu[sp.b];
     sp.e_b = a.cu[sp.b + 1];
     sp.lo = sp.s_b + (x - kb0) * BLK;
-    sp.hi = min(sp.lo + 2 * BLK, sp.e_b);
+    sp.hi = min(sp.lo + NB * BLK, sp.e_b);
     sp.ok = true;
     return sp;
 }
@@ -161,24 +163,33 @@ __global__ __launch_bounds__(NTH) void fm_bwd_delta_kernel(BwdArgs a) {
 }
 
 // ---- dK / dV ---------------------------------------------------------------
-__shared__ __attribute__((aligned(16))) char s_q[BLK * ROW_T];
-__shared__ __attribute__((aligned(16))) char s_g[BLK * ROW_T];
-__shared__ __attribute__((aligned(16))) float s_l2[BLK];
-__shared__ __attribute__((aligned(16))) float s_dl[BLK];
+// 8 waves: wave w = 4g + t owns keys 32t..32t+31 of the 128-key span and
+// query rows 32g..32g+31 of every staged 64-row q tile (two waves per
+// SIMD).  The two groups' dK^T and dV^T are summed through LDS at the end.
+constexpr int NTK = 512;
+constexpr int QU = BLK * 16 / NTK;   // 16-byte chunks of Q (and of dO) per thread
+constexpr int KV_COMB = 4 * 64 * 16 * 16;   // bytes: one accumulator set of a group (16 x 16 B per lane)
+constexpr int OFF_G = BLK * ROW_T, OFF_L2 = 2 * BLK * ROW_T, OFF_DL = OFF_L2 + 4 * BLK;
+constexpr int DKV_LDS = KV_COMB > OFF_DL + 4 * BLK ? KV_COMB : OFF_DL + 4 * BLK;
+// staging (Q tile, dO tile, lse, Delta) during the loop, the group sums after it
+__shared__ __attribute__((aligned(16))) char s_dkv[DKV_LDS];
+// the span's K and V rows (128 keys), staged once
+__shared__ __attribute__((aligned(16))) char s_kt[2 * BLK * ROW_R];
+__shared__ __attribute__((aligned(16))) char s_vt[2 * BLK * ROW_R];
 
-// One q tile's staging data in registers: 4 chunks of Q and of dO per
-// thread (row c >> 4, chunk c & 15 of c = tid + 256 u), and threads 0..63
+// One q tile's staging data in registers: QU chunks of Q and of dO per
+// thread (row c >> 4, chunk c & 15 of c = tid + 512 u), and threads 0..63
 // the lse (log2 units; +inf for rows that attend nothing or lie past the
 // sequence, so that P = 0 there) and Delta of row tid.
 struct QStage {
-    u32x4 q[4], g[4];
+    u32x4 q[QU], g[QU];
     float l2, dl;
 };
 __device__ inline void load_qstage(const BwdArgs& a, int h, int r0, int r1, int tid, QStage& st) {
     const int64_t rsb = (int64_t)a.H * 2 * HD;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int c = tid + NTH * u, row = c >> 4, ch = c & 15;
+    for (int u = 0; u < QU; ++u) {
+        const int c = tid + NTK * u, row = c >> 4, ch = c & 15;
         st.q[u] = u32x4{0, 0, 0, 0};
         st.g[u] = u32x4{0, 0, 0, 0};
         if (r0 + row < r1) {
@@ -197,22 +208,51 @@ __device__ inline void load_qstage(const BwdArgs& a, int h, int r0, int r1, int 
 }
 __device__ inline void store_qstage(const QStage& st, int tid) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int c = tid + NTH * u, row = c >> 4, ch = c & 15;
-        *(u32x4*)(s_q + row * ROW_T + 16 * ch) = st.q[u];
-        *(u32x4*)(s_g + row * ROW_T + 16 * ch) = st.g[u];
+    for (int u = 0; u < QU; ++u) {
+        const int c = tid + NTK * u, row = c >> 4, ch = c & 15;
+        *(u32x4*)(s_dkv + row * ROW_T + 16 * ch) = st.q[u];
+        *(u32x4*)(s_dkv + OFF_G + row * ROW_T + 16 * ch) = st.g[u];
     }
     if (tid < BLK) {
-        s_l2[tid] = st.l2;
-        s_dl[tid] = st.dl;
+        ((float*)(s_dkv + OFF_L2))[tid] = st.l2;
+        ((float*)(s_dkv + OFF_DL))[tid] = st.dl;
     }
 }
 
-__global__ __launch_bounds__(NTH, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
+// Group sums: group `from` writes its 4 accumulators, the other group adds
+// them to its own (float addition commutes: the result does not depend on
+// which group adds).  Lane L of wave slot t, accumulator dt, quad q at
+// float4 ((4 dt + q) * 256 + 64 t + L).
+__device__ __attribute__((always_inline)) inline void group_sum(f32x16 (&acc)[4], int g, int from, int t, int lane) {
+    float4* buf = (float4*)s_dkv;
+    __syncthreads();
+    if (g == from) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                buf[(4 * dt + q) * 256 + 64 * t + lane] =
+                    float4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]};
+    }
+    __syncthreads();
+    if (g != from) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 o = buf[(4 * dt + q) * 256 + 64 * t + lane];
+                acc[dt][4 * q] += o.x; acc[dt][4 * q + 1] += o.y;
+                acc[dt][4 * q + 2] += o.z; acc[dt][4 * q + 3] += o.w;
+            }
+    }
+}
+
+__global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
     const int h = blockIdx.y;
-    const Span sp = span_of(a, blockIdx.x);
+    const Span sp = span_of<2>(a, blockIdx.x);
     if (!sp.ok) return;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = w >> 2, t = w & 3;     // query-row half, key slot
     const int n = lane & 31, hh = lane >> 5;
     const int c0 = sp.lo, c1 = sp.hi;
 
@@ -232,19 +272,25 @@ __global__ __launch_bounds__(NTH, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
         }
     }
 
-    // this lane's key: K and V fragments (B operands: column = key n,
-    // channels 16s + 8hh .. +7) and its mask intervals
-    const int kj = c0 + 32 * w + n;
-    const bool kvalid = kj < c1;
-    bf16x8 kf[8], vf[8];
-    {
-        const int64_t off = ((int64_t)kj * a.H + h) * 2 * HD + 16 * hh;
+    // the span's K and V rows into LDS (rows past the sequence: zeros);
+    // this lane's key and its mask intervals
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            kf[s] = as_bf16x8(kvalid ? *(const u32x4*)((const char*)a.k + off + 32 * s) : u32x4{0, 0, 0, 0});
-            vf[s] = as_bf16x8(kvalid ? *(const u32x4*)((const char*)a.v + off + 32 * s) : u32x4{0, 0, 0, 0});
+    for (int u = 0; u < 2 * BLK * 16 / NTK; ++u) {
+        const int c = tid + NTK * u, row = c >> 4, ch = c & 15;
+        u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
+        if (c0 + row < c1) {
+            const int64_t off = ((int64_t)(c0 + row) * a.H + h) * 2 * HD + 16 * ch;
+            kv = *(const u32x4*)((const char*)a.k + off);
+            vv = *(const u32x4*)((const char*)a.v + off);
         }
+        *(u32x4*)(s_kt + row * ROW_R + 16 * ch) = kv;
+        *(u32x4*)(s_vt + row * ROW_R + 16 * ch) = vv;
     }
+    const int kj = c0 + 32 * t + n;
+    const bool kvalid = kj < c1;
+    // B-operand fragments of this lane's key (column n, channels 16s + 8hh)
+    const char* kb_l = s_kt + (32 * t + n) * ROW_R + 16 * hh;
+    const char* vb_l = s_vt + (32 * t + n) * ROW_R + 16 * hh;
     Vec4 mv{0, 0, 0, 0};
     if (kvalid) mv = fill_column(a.sv, a.n_vec, a.causal, a.N, kj);
 
@@ -284,6 +330,10 @@ __global__ __launch_bounds__(NTH, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
     int i = next_visit(i_first, part);
     if (i < Tq) load_qstage(a, h, sp.s_b + i * BLK, min(sp.s_b + (i + 1) * BLK, sp.e_b), tid, st);
     const float sl2 = a.scale_log2;
+    const char* s_q = s_dkv;
+    const char* s_g = s_dkv + OFF_G;
+    const float* s_l2 = (const float*)(s_dkv + OFF_L2);
+    const float* s_dl = (const float*)(s_dkv + OFF_DL);
     while (i < Tq) {
         const int r0 = sp.s_b + i * BLK;
         __syncthreads();   // every wave is done with the previous tile
@@ -293,81 +343,76 @@ __global__ __launch_bounds__(NTH, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
         const int ni = next_visit(i + 1, npart);
         if (ni < Tq) load_qstage(a, h, sp.s_b + ni * BLK, min(sp.s_b + (ni + 1) * BLK, sp.e_b), tid, st);
 
-        // S = Q K^T and dP = dO V^T: register e of result t is row
-        // 32t + 8(e>>2) + 4hh + (e&3) of the tile, column = this lane's key
-        f32x16 sc[2], dp[2];
+        // S = Q K^T and dP = dO V^T for rows 32g..32g+31 of the tile:
+        // register e is row 32g + 8(e>>2) + 4hh + (e&3), column = this lane's key
+        f32x16 sc, dp;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
+        const char* qa = s_q + (32 * g + n) * ROW_T + 16 * hh;
+        const char* ga = s_g + (32 * g + n) * ROW_T + 16 * hh;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) { sc[t][e] = 0.f; dp[t][e] = 0.f; }
-        const char* qa = s_q + n * ROW_T + 16 * hh;
-        const char* ga = s_g + n * ROW_T + 16 * hh;
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                sc[t] = mfma(as_bf16x8(*(const u32x4*)(qa + 32 * t * ROW_T + 32 * s)), kf[s], sc[t]);
-                dp[t] = mfma(as_bf16x8(*(const u32x4*)(ga + 32 * t * ROW_T + 32 * s)), vf[s], dp[t]);
-            }
+        for (int s = 0; s < 8; ++s) {
+            sc = mfma(as_bf16x8(*(const u32x4*)(qa + 32 * s)), as_bf16x8(*(const u32x4*)(kb_l + 32 * s)), sc);
+            dp = mfma(as_bf16x8(*(const u32x4*)(ga + 32 * s)), as_bf16x8(*(const u32x4*)(vb_l + 32 * s)), dp);
+        }
         // P = exp2(S scale log2e - lse2), masked pairs 0; dS = P (dP - Delta)
-        bf16x8 pb[2][2], db[2][2];
+        bf16x8 pb[2], db[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int j = 0; j < 4; ++j) {
+            const float4 l4 = *(const float4*)(s_l2 + 32 * g + 8 * j + 4 * hh);
+            const float4 d4 = *(const float4*)(s_dl + 32 * g + 8 * j + 4 * hh);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 l4 = *(const float4*)(s_l2 + 32 * t + 8 * j + 4 * hh);
-                const float4 d4 = *(const float4*)(s_dl + 32 * t + 8 * j + 4 * hh);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int e = 4 * j + c;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][e], sl2, -lv[c]));
-                    if (part) {
-                        const int row = r0 + 32 * t + 8 * j + 4 * hh + c;
-                        const bool m = (a.causal && kj > row) || (mv.lts <= row && row < mv.lte) ||
-                                       (mv.uts <= row && row < mv.ute);
-                        p = m ? 0.f : p;
-                    }
-                    const float ds = p * (dp[t][e] - dv4[c]);
-                    pb[t][e >> 3][e & 7] = (__bf16)p;
-                    db[t][e >> 3][e & 7] = (__bf16)ds;
+            for (int c = 0; c < 4; ++c) {
+                const int e = 4 * j + c;
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], sl2, -lv[c]));
+                if (part) {
+                    const int row = r0 + 32 * g + 8 * j + 4 * hh + c;
+                    const bool m = (a.causal && kj > row) || (mv.lts <= row && row < mv.lte) ||
+                                   (mv.uts <= row && row < mv.ute);
+                    p = m ? 0.f : p;
                 }
+                const float ds = p * (dp[e] - dv4[c]);
+                pb[e >> 3][e & 7] = (__bf16)p;
+                db[e >> 3][e & 7] = (__bf16)ds;
             }
-        // dV^T += dO^T P, dK^T += Q^T dS: 16-row groups kg of the tile
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS over the 16-row groups 2g, 2g + 1
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg)
+        for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                dv[dt] = mfma(tr_frag<ROW_T>(s_g, kg, dt, lane), pb[kg >> 1][kg & 1], dv[dt]);
-                dk[dt] = mfma(tr_frag<ROW_T>(s_q, kg, dt, lane), db[kg >> 1][kg & 1], dk[dt]);
+                dv[dt] = mfma(tr_frag<ROW_T>(s_g, 2 * g + c2, dt, lane), pb[c2], dv[dt]);
+                dk[dt] = mfma(tr_frag<ROW_T>(s_q, 2 * g + c2, dt, lane), db[c2], dk[dt]);
             }
         i = ni;
         part = npart;
     }
 
-    // dK = scale dK^T, dV = dV^T: lane = key kj, channels 32dt + 8g + 4hh + 0..3
+    // dK summed into group 0, dV into group 1; then group 0 writes
+    // dK = scale dK^T and group 1 dV = dV^T (lane = key kj, channels
+    // 32dt + 8q + 4hh + 0..3)
+    group_sum(dk, g, 1, t, lane);
+    group_sum(dv, g, 0, t, lane);
     if (kvalid) {
-        const int64_t off = ((int64_t)kj * a.H + h) * HD;
-        uint16_t* dkp = (uint16_t*)a.dk + off;
-        uint16_t* dvp = (uint16_t*)a.dv + off;
-        const float sc = a.scale;
+        uint16_t* op = (uint16_t*)(g == 0 ? a.dk : a.dv) + ((int64_t)kj * a.H + h) * HD;
+        const float sc = g == 0 ? a.scale : 1.f;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c = 32 * dt + 8 * g + 4 * hh;
-                u32x2 x, y;
-                x.x = bf16_bits(dk[dt][4 * g] * sc) | (bf16_bits(dk[dt][4 * g + 1] * sc) << 16);
-                x.y = bf16_bits(dk[dt][4 * g + 2] * sc) | (bf16_bits(dk[dt][4 * g + 3] * sc) << 16);
-                y.x = bf16_bits(dv[dt][4 * g]) | (bf16_bits(dv[dt][4 * g + 1]) << 16);
-                y.y = bf16_bits(dv[dt][4 * g + 2]) | (bf16_bits(dv[dt][4 * g + 3]) << 16);
-                *(u32x2*)(dkp + c) = x;
-                *(u32x2*)(dvp + c) = y;
+            for (int q = 0; q < 4; ++q) {
+                const f32x16& x = g == 0 ? dk[dt] : dv[dt];
+                u32x2 v2;
+                v2.x = bf16_bits(x[4 * q] * sc) | (bf16_bits(x[4 * q + 1] * sc) << 16);
+                v2.y = bf16_bits(x[4 * q + 2] * sc) | (bf16_bits(x[4 * q + 3] * sc) << 16);
+                *(u32x2*)(op + 32 * dt + 8 * q + 4 * hh) = v2;
             }
     }
 }
 
 // ---- dQ --------------------------------------------------------------------
+constexpr int NTQ = 512;         // dQ workgroup: 8 waves, 256 queries (two waves per SIMD)
+constexpr int QBLK = NTQ / 128;  // 64-row blocks per dQ workgroup
 __shared__ __attribute__((aligned(16))) char s_k[BLK * ROW_T];
 __shared__ __attribute__((aligned(16))) char s_v[BLK * ROW_R];
 
@@ -375,14 +420,15 @@ __shared__ __attribute__((aligned(16))) char s_v[BLK * ROW_R];
 // thread (rows past the sequence are zero), and for partial blocks the
 // mask intervals of key c0 + lane (every wave loads its own copy).
 struct KStage {
-    u32x4 k[4], v[4];
+    u32x4 k[BLK * 16 / 512], v[BLK * 16 / 512];
     Vec4 mv;
 };
+constexpr int KU = BLK * 16 / NTQ;   // 16-byte chunks of K (and of V) per thread
 __device__ inline void load_kstage(const BwdArgs& a, int h, int c0, int c1, bool part, int tid, KStage& st) {
     const int64_t rsb = (int64_t)a.H * 2 * HD;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int c = tid + NTH * u, row = c >> 4, ch = c & 15;
+    for (int u = 0; u < KU; ++u) {
+        const int c = tid + NTQ * u, row = c >> 4, ch = c & 15;
         st.k[u] = u32x4{0, 0, 0, 0};
         st.v[u] = u32x4{0, 0, 0, 0};
         if (c0 + row < c1) {
@@ -397,16 +443,16 @@ __device__ inline void load_kstage(const BwdArgs& a, int h, int c0, int c1, bool
 }
 __device__ inline void store_kstage(const KStage& st, int tid) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int c = tid + NTH * u, row = c >> 4, ch = c & 15;
+    for (int u = 0; u < KU; ++u) {
+        const int c = tid + NTQ * u, row = c >> 4, ch = c & 15;
         *(u32x4*)(s_k + row * ROW_T + 16 * ch) = st.k[u];
         *(u32x4*)(s_v + row * ROW_R + 16 * ch) = st.v[u];
     }
 }
 
-__global__ __launch_bounds__(NTH, 1) void fm_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
     const int h = blockIdx.y;
-    const Span sp = span_of(a, blockIdx.x);
+    const Span sp = span_of<QBLK>(a, blockIdx.x);
     if (!sp.ok) return;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hh = lane >> 5;
@@ -566,10 +612,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s) {
     }
     if (kb_cap <= 0 || a.N == 0) return hipSuccess;
     const dim3 grid((unsigned)kb_cap, (unsigned)a.H);
-    hipLaunchKernelGGL(bwd::fm_bwd_dkdv_kernel, grid, dim3(bwd::NTH), 0, s, a);
+    hipLaunchKernelGGL(bwd::fm_bwd_dkdv_kernel, grid, dim3(bwd::NTK), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd::fm_bwd_dq_kernel, grid, dim3(bwd::NTH), 0, s, a);
+    hipLaunchKernelGGL(bwd::fm_bwd_dq_kernel, grid, dim3(bwd::NTQ), 0, s, a);
     return hipGetLastError();
 }
 
