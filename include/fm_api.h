@@ -285,7 +285,10 @@ int fm_fused_path(int64_t N, int B, int H, int head_dim, int dtype, int n_vec, i
 /*
  * Workspace bytes of fm_attn_bwd (0 on bad arguments): a status header,
  * kb_off [B+1] and extrema [ceil(N/64)+B][8] of the mask at block_k = 64,
- * and Delta fp32 [H][N].  Separate from the forward's workspace.
+ * Delta fp32 [H][N], and for small problems (fewer than 256 dK/dV
+ * workgroups, (ceil(N/128) + B) * H < 256) fp32 partials of up to 8 chunks
+ * per tile with their flags (any initial content; each call marks what it
+ * writes with a fresh value).  Separate from the forward's workspace.
  */
 size_t fm_bwd_workspace_size(int64_t N, int B, int H, int head_dim, int dtype);
 
@@ -309,7 +312,11 @@ size_t fm_bwd_workspace_size(int64_t N, int B, int H, int head_dim, int dtype);
  *   pair contributes) unless the device data is invalid (status word).
  * workspace: device, >= fm_bwd_workspace_size(...) bytes.
  * Launches: block extrema, Delta, dK/dV (one workgroup per 128-key tile
- * and head), dQ (one per 128-query tile and head); same bits every run.
+ * and head), dQ (one per 256-query tile and head); for small problems the
+ * q tiles of a key tile and the key blocks of a query tile are cut into
+ * chunks (separate workgroups, fp32 partials) and two more launches sum
+ * them in chunk order.  The chunking depends on the sizes only: the same
+ * inputs give the same bits on every run and device.
  */
 int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                 const float* softmax_lse, int dtype, int64_t N, int H, int D,

@@ -13,6 +13,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -176,6 +178,15 @@ int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_
     return FM_OK;
 }
 
+// Flag value of one call that marks the partials it wrote: a process-wide
+// counter, never 0, so flags need no clearing between calls.
+uint32_t next_call_id() {
+    static std::atomic<uint32_t> ctr{0};
+    uint32_t v;
+    do { v = ctr.fetch_add(1, std::memory_order_relaxed) + 1; } while (v == 0);
+    return v;
+}
+
 int hip_check(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(FM_E_HIP, "%s: %s", what, hipGetErrorString(e));
     return FM_OK;
@@ -201,16 +212,43 @@ int preprocess_impl(const int32_t* sv, int n_vec, int causal, const int32_t* cu,
                                         nkb, status, n_cu, s), "extrema launch");
 }
 
-// Backward workspace: header, kb_off, extrema at block_k = 64, Delta.
-struct BwdLayout { size_t off_hdr, off_kb_off, off_extrema, off_delta, bytes; int64_t kb_cap; };
+// Backward workspace: header, kb_off, extrema at block_k = 64, Delta, and
+// for small problems the chunk partials and their flags.
+struct BwdLayout {
+    size_t off_hdr, off_kb_off, off_extrema, off_delta, off_part_kv, off_flag_kv, off_part_q, off_flag_q, bytes;
+    int64_t kb_cap;
+    int nc, qc, kc;
+};
+
+// Chunks of the backward, from the sizes only (so the bits do not depend
+// on the device): when the dK/dV launch would have fewer than 256
+// workgroups, each key tile's q tiles and each query tile's key blocks are
+// cut into nc <= 8 chunks, about two workgroups per compute unit of a
+// 256-CU device (16 chunks measured slower: more partial traffic, and the
+// chunks' fixed start-up cost).
+constexpr int kBwdChunkWgs = 256, kBwdMaxChunks = fm::BWD_MAX_CHUNKS;
+constexpr size_t kBwdPartBytes = 8 * 64 * 64 * 4;   // one chunk partial: 8 waves x 64 lanes x 64 floats
 
 int bwd_layout(int64_t N, int B, int H, BwdLayout* L) {
-    L->kb_cap = cdiv(N, fm::bwd_block_k()) + B;
+    const int bk = fm::bwd_block_k();
+    L->kb_cap = cdiv(N, bk) + B;
+    const int64_t wgs = (cdiv(N, 2 * bk) + B) * (int64_t)H;
+    L->nc = wgs >= kBwdChunkWgs ? 1 : (int)std::min<int64_t>(kBwdMaxChunks, cdiv(2 * kBwdChunkWgs, std::max<int64_t>(wgs, 1)));
+    L->qc = L->kc = (int)std::max<int64_t>(1, cdiv(cdiv(N, bk), L->nc));
     size_t off = 0;
     L->off_hdr = off; off = align256(off + 256);
     L->off_kb_off = off; off = align256(off + (size_t)(B + 1) * 4);
     L->off_extrema = off; off = align256(off + (size_t)L->kb_cap * 32);
     L->off_delta = off; off = align256(off + (size_t)H * (size_t)N * 4);
+    L->off_part_kv = L->off_flag_kv = L->off_part_q = L->off_flag_q = 0;
+    if (L->nc > 1) {
+        const size_t skv = (size_t)((L->kb_cap + B) / 2 + 1) * H * L->nc;       // (x + b) / 2
+        const size_t sq = (size_t)((L->kb_cap + 3 * (int64_t)B) / 4 + 1) * H * L->nc;   // (x + 3b) / 4
+        L->off_part_kv = off; off = align256(off + skv * kBwdPartBytes);
+        L->off_flag_kv = off; off = align256(off + skv * 4);
+        L->off_part_q = off; off = align256(off + sq * kBwdPartBytes);
+        L->off_flag_q = off; off = align256(off + sq * 4);
+    }
     L->bytes = off;
     if ((int64_t)off > kMaxBytes) return fail(FM_E_INVAL, "problem too large");
     if (L->kb_cap > INT32_MAX / 2) return fail(FM_E_INVAL, "too many key blocks");
@@ -536,6 +574,12 @@ int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, co
     a.scale = scale;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
     a.kb_off = kb_off; a.extrema = ext; a.n_kb = hdr + fm::HDR_NKB; a.status = hdr + fm::HDR_STATUS;
+    a.nc = L.nc; a.qc = L.qc; a.kc = L.kc;
+    a.part_kv = L.nc > 1 ? (float*)(base + L.off_part_kv) : nullptr;
+    a.flag_kv = L.nc > 1 ? (int32_t*)(base + L.off_flag_kv) : nullptr;
+    a.part_q = L.nc > 1 ? (float*)(base + L.off_part_q) : nullptr;
+    a.flag_q = L.nc > 1 ? (int32_t*)(base + L.off_flag_q) : nullptr;
+    a.call_id = next_call_id();
     if ((rc = hip_check(fm::launch_bwd_bf16(a, L.kb_cap, stream), "backward launch"))) return rc;
     return ok();
 }

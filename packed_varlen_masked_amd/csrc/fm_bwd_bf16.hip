@@ -29,8 +29,12 @@
 //     Delta in registers.  It walks the visited 64-key blocks, stages K and
 //     V in LDS, computes S^T = K Q^T and dP^T = V dO^T with one query per
 //     lane (as the forward does), and accumulates dQ^T = K^T dS^T.
-//   * every output element is written by exactly one workgroup: the same
-//     inputs give the same bits.
+//   * small problems (fewer workgroups than compute units) cut each key
+//     tile's q tiles and each query tile's key blocks into chunks that run
+//     as separate workgroups and write fp32 partials; two reduce launches
+//     sum them in chunk order.
+//   * every output element is written by exactly one workgroup, and chunk
+//     sums run in a fixed order: the same inputs give the same bits.
 #include "fm_common.hpp"
 #include "fm_internal.h"
 #include "fm_api.h"
@@ -247,6 +251,75 @@ __device__ __attribute__((always_inline)) inline void group_sum(f32x16 (&acc)[4]
     }
 }
 
+// Chunk partials: 8 waves x 64 lanes x 4 accumulators of 16 floats
+// (128 KB), float4 ((16 w + 4 dt + q) * 64 + lane): every store and load
+// instruction of a wave covers 1 KB contiguously.
+constexpr int PART_FLOATS = 8 * 64 * 64;
+__device__ __attribute__((always_inline)) inline void store_acc(float* base, const f32x16 (&acc)[4], int w, int lane) {
+    float4* p = (float4*)base;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            p[(16 * w + 4 * dt + q) * 64 + lane] = float4{acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2],
+                                                         acc[dt][4 * q + 3]};
+}
+// The reduce launches: RZ workgroups per tile, workgroup z summing the
+// accumulator quads dt = z of every lane (4 float4 per thread per chunk).
+// Per batch of CB chunks the flags are read first, then every written
+// chunk's loads are issued before the sums, which run in chunk order.
+constexpr int RZ = 4, CB = 8;   // chunks loaded per batch
+__device__ __attribute__((always_inline)) inline void sum_chunks(const BwdArgs& a, const float* base,
+                                                                 const int32_t* flags, int64_t slot0, int dt,
+                                                                 float4 (&acc)[4], int w, int lane) {
+    for (int c0 = 0; c0 < a.nc; c0 += CB) {
+        bool wr[CB];
+#pragma unroll
+        for (int c = 0; c < CB; ++c) wr[c] = c0 + c < a.nc && flags[slot0 + c0 + c] == (int32_t)a.call_id;
+        float4 v[CB][4];
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+            if (wr[c]) {
+                const float4* p = (const float4*)(base + (slot0 + c0 + c) * PART_FLOATS);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[c][q] = p[(16 * w + 4 * dt + q) * 64 + lane];
+            }
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+            if (wr[c]) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[q].x += v[c][q].x; acc[q].y += v[c][q].y; acc[q].z += v[c][q].z; acc[q].w += v[c][q].w;
+                }
+            }
+    }
+}
+// bf16 channels 32dt + 8q + 4hh + 0..3 (q = 0..3) of a row, times sc.
+__device__ __attribute__((always_inline)) inline void store_quads_bf16(uint16_t* op, const float4 (&x)[4], float sc,
+                                                                       int dt, int hh) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        u32x2 v2;
+        v2.x = bf16_bits(x[q].x * sc) | (bf16_bits(x[q].y * sc) << 16);
+        v2.y = bf16_bits(x[q].z * sc) | (bf16_bits(x[q].w * sc) << 16);
+        *(u32x2*)(op + 32 * dt + 8 * q + 4 * hh) = v2;
+    }
+}
+// bf16 row of 128 channels from a lane's 4 accumulators (channels
+// 32dt + 8q + 4hh + 0..3), times sc.
+__device__ __attribute__((always_inline)) inline void store_row_bf16(uint16_t* op, const f32x16 (&x)[4], float sc,
+                                                                     int hh) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            u32x2 v2;
+            v2.x = bf16_bits(x[dt][4 * q] * sc) | (bf16_bits(x[dt][4 * q + 1] * sc) << 16);
+            v2.y = bf16_bits(x[dt][4 * q + 2] * sc) | (bf16_bits(x[dt][4 * q + 3] * sc) << 16);
+            *(u32x2*)(op + 32 * dt + 8 * q + 4 * hh) = v2;
+        }
+}
+
 __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
     const int h = blockIdx.y;
     const Span sp = span_of<2>(a, blockIdx.x);
@@ -301,9 +374,11 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
         for (int e = 0; e < 16; ++e) { dk[dt][e] = 0.f; dv[dt][e] = 0.f; }
 
     // q tiles of 64 rows from the sequence start; causal rows before c0 see
-    // none of the tile's keys
-    const int Tq = ceil_div(sp.e_b - sp.s_b, BLK);
-    const int i_first = a.causal ? (c0 - sp.s_b) / BLK : 0;
+    // none of the tile's keys; with chunks, this workgroup's share only
+    const int Tq_all = ceil_div(sp.e_b - sp.s_b, BLK);
+    const int ch = blockIdx.z;
+    const int Tq = a.nc > 1 ? min(Tq_all, (ch + 1) * a.qc) : Tq_all;
+    const int i_first = max(a.causal ? (c0 - sp.s_b) / BLK : 0, a.nc > 1 ? ch * a.qc : 0);
     // next q tile at or after `from` whose class is not FULL (Tq if none)
     auto next_visit = [&](int from, bool& part) -> int {
         for (int w0 = from; w0 < Tq; w0 += 64) {
@@ -328,6 +403,8 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
     QStage st;
     bool part = false;
     int i = next_visit(i_first, part);
+    const bool any = i < Tq;
+    if (a.nc > 1 && !any) return;   // empty chunk: no partial, its flag stays stale
     if (i < Tq) load_qstage(a, h, sp.s_b + i * BLK, min(sp.s_b + (i + 1) * BLK, sp.e_b), tid, st);
     const float sl2 = a.scale_log2;
     const char* s_q = s_dkv;
@@ -355,36 +432,40 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
             sc = mfma(as_bf16x8(*(const u32x4*)(qa + 32 * s)), as_bf16x8(*(const u32x4*)(kb_l + 32 * s)), sc);
             dp = mfma(as_bf16x8(*(const u32x4*)(ga + 32 * s)), as_bf16x8(*(const u32x4*)(vb_l + 32 * s)), dp);
         }
-        // P = exp2(S scale log2e - lse2), masked pairs 0; dS = P (dP - Delta)
-        bf16x8 pb[2], db[2];
+        // P = exp2(S scale log2e - lse2), masked pairs 0; dS = P (dP - Delta);
+        // then dV^T += dO^T P and dK^T += Q^T dS for the 16-row group
+        // 2g + c2.  Written per half so that the second half's vector work
+        // can issue while the first half's products run.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 l4 = *(const float4*)(s_l2 + 32 * g + 8 * j + 4 * hh);
-            const float4 d4 = *(const float4*)(s_dl + 32 * g + 8 * j + 4 * hh);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int c2 = 0; c2 < 2; ++c2) {
+            bf16x8 pb, db;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int e = 4 * j + c;
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], sl2, -lv[c]));
-                if (part) {
-                    const int row = r0 + 32 * g + 8 * j + 4 * hh + c;
-                    const bool m = (a.causal && kj > row) || (mv.lts <= row && row < mv.lte) ||
-                                   (mv.uts <= row && row < mv.ute);
-                    p = m ? 0.f : p;
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * c2 + jj;
+                const float4 l4 = *(const float4*)(s_l2 + 32 * g + 8 * j + 4 * hh);
+                const float4 d4 = *(const float4*)(s_dl + 32 * g + 8 * j + 4 * hh);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int e = 4 * j + c;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], sl2, -lv[c]));
+                    if (part) {
+                        const int row = r0 + 32 * g + 8 * j + 4 * hh + c;
+                        const bool m = (a.causal && kj > row) || (mv.lts <= row && row < mv.lte) ||
+                                       (mv.uts <= row && row < mv.ute);
+                        p = m ? 0.f : p;
+                    }
+                    const float ds = p * (dp[e] - dv4[c]);
+                    pb[e & 7] = (__bf16)p;
+                    db[e & 7] = (__bf16)ds;
                 }
-                const float ds = p * (dp[e] - dv4[c]);
-                pb[e >> 3][e & 7] = (__bf16)p;
-                db[e >> 3][e & 7] = (__bf16)ds;
             }
-        }
-        // dV^T += dO^T P, dK^T += Q^T dS over the 16-row groups 2g, 2g + 1
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                dv[dt] = mfma(tr_frag<ROW_T>(s_g, 2 * g + c2, dt, lane), pb[c2], dv[dt]);
-                dk[dt] = mfma(tr_frag<ROW_T>(s_q, 2 * g + c2, dt, lane), db[c2], dk[dt]);
+                dv[dt] = mfma(tr_frag<ROW_T>(s_g, 2 * g + c2, dt, lane), pb, dv[dt]);
+                dk[dt] = mfma(tr_frag<ROW_T>(s_q, 2 * g + c2, dt, lane), db, dk[dt]);
             }
+        }
         i = ni;
         part = npart;
     }
@@ -394,20 +475,32 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
     // 32dt + 8q + 4hh + 0..3)
     group_sum(dk, g, 1, t, lane);
     group_sum(dv, g, 0, t, lane);
-    if (kvalid) {
-        uint16_t* op = (uint16_t*)(g == 0 ? a.dk : a.dv) + ((int64_t)kj * a.H + h) * HD;
-        const float sc = g == 0 ? a.scale : 1.f;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x16& x = g == 0 ? dk[dt] : dv[dt];
-                u32x2 v2;
-                v2.x = bf16_bits(x[4 * q] * sc) | (bf16_bits(x[4 * q + 1] * sc) << 16);
-                v2.y = bf16_bits(x[4 * q + 2] * sc) | (bf16_bits(x[4 * q + 3] * sc) << 16);
-                *(u32x2*)(op + 32 * dt + 8 * q + 4 * hh) = v2;
-            }
+    if (a.nc > 1) {   // this chunk's dK^T (group 0) and dV^T (group 1), unscaled
+        const int64_t slot = ((int64_t)((sp.x + sp.b) >> 1) * a.H + h) * a.nc + ch;
+        store_acc(a.part_kv + slot * PART_FLOATS, g == 0 ? dk : dv, w, lane);
+        if (tid == 0) a.flag_kv[slot] = (int32_t)a.call_id;
+        return;
     }
+    if (kvalid)
+        store_row_bf16((uint16_t*)(g == 0 ? a.dk : a.dv) + ((int64_t)kj * a.H + h) * HD, g == 0 ? dk : dv,
+                       g == 0 ? a.scale : 1.f, hh);
+}
+
+// Sum of the dK/dV chunks of a key tile (chunk order), as the kernel above
+// would have written it: wave 4g + t, lane = key 32t + n; group 0 dK, 1 dV.
+__global__ __launch_bounds__(NTK) void fm_bwd_dkdv_reduce_kernel(BwdArgs a) {
+    const int h = blockIdx.y, dt = blockIdx.z;
+    const Span sp = span_of<2>(a, blockIdx.x);
+    if (!sp.ok) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = w >> 2, t = w & 3, n = lane & 31, hh = lane >> 5;
+    float4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const int64_t slot0 = ((int64_t)((sp.x + sp.b) >> 1) * a.H + h) * a.nc;
+    sum_chunks(a, a.part_kv, a.flag_kv, slot0, dt, acc, w, lane);
+    const int kj = sp.lo + 32 * t + n;
+    if (kj < sp.hi)
+        store_quads_bf16((uint16_t*)(g == 0 ? a.dk : a.dv) + ((int64_t)kj * a.H + h) * HD, acc,
+                         g == 0 ? a.scale : 1.f, dt, hh);
 }
 
 // ---- dQ --------------------------------------------------------------------
@@ -485,7 +578,10 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
         for (int e = 0; e < 16; ++e) dq[dt][e] = 0.f;
 
     const int Tc = ceil_div(sp.e_b - sp.s_b, BLK);
-    const int kb_end = a.causal ? min(Tc, (r1 - 1 - sp.s_b) / BLK + 1) : Tc;
+    const int ch = blockIdx.z;
+    const int kb_lim = a.causal ? min(Tc, (r1 - 1 - sp.s_b) / BLK + 1) : Tc;
+    const int kb_end = a.nc > 1 ? min(kb_lim, (ch + 1) * a.kc) : kb_lim;
+    const int kb_first = a.nc > 1 ? ch * a.kc : 0;
     const int32_t* xb = a.extrema + (int64_t)a.kb_off[sp.b] * 8;
     auto next_visit = [&](int from, bool& part) -> int {
         for (int w0 = from; w0 < kb_end; w0 += 64) {
@@ -512,7 +608,8 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
 
     KStage st;
     bool part = false;
-    int kb = next_visit(0, part);
+    int kb = next_visit(kb_first, part);
+    if (a.nc > 1 && kb >= kb_end) return;   // empty chunk: no partial, its flag stays stale
     if (kb < kb_end) {
         const int c0 = sp.s_b + kb * BLK;
         load_kstage(a, h, c0, min(c0 + BLK, sp.e_b), part, tid, st);
@@ -584,20 +681,29 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
         part = npart;
     }
 
-    // dQ = scale dQ^T: lane = query qr, channels 32dt + 8g + 4hh + 0..3
-    if (qvalid) {
-        uint16_t* dqp = (uint16_t*)a.dq + ((int64_t)qr * a.H + h) * HD;
-        const float sc = a.scale;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 x;
-                x.x = bf16_bits(dq[dt][4 * g] * sc) | (bf16_bits(dq[dt][4 * g + 1] * sc) << 16);
-                x.y = bf16_bits(dq[dt][4 * g + 2] * sc) | (bf16_bits(dq[dt][4 * g + 3] * sc) << 16);
-                *(u32x2*)(dqp + 32 * dt + 8 * g + 4 * hh) = x;
-            }
+    if (a.nc > 1) {   // this chunk's dQ^T, unscaled
+        const int64_t slot = ((int64_t)((sp.x + (QBLK - 1) * sp.b) / QBLK) * a.H + h) * a.nc + ch;
+        store_acc(a.part_q + slot * PART_FLOATS, dq, w, lane);
+        if (tid == 0) a.flag_q[slot] = (int32_t)a.call_id;
+        return;
     }
+    // dQ = scale dQ^T: lane = query qr, channels 32dt + 8g + 4hh + 0..3
+    if (qvalid) store_row_bf16((uint16_t*)a.dq + ((int64_t)qr * a.H + h) * HD, dq, a.scale, hh);
+}
+
+// Sum of the dQ chunks of a query tile (chunk order): wave w, lane = query
+// 32w + n.
+__global__ __launch_bounds__(NTQ) void fm_bwd_dq_reduce_kernel(BwdArgs a) {
+    const int h = blockIdx.y, dt = blockIdx.z;
+    const Span sp = span_of<QBLK>(a, blockIdx.x);
+    if (!sp.ok) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, hh = lane >> 5;
+    float4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const int64_t slot0 = ((int64_t)((sp.x + (QBLK - 1) * sp.b) / QBLK) * a.H + h) * a.nc;
+    sum_chunks(a, a.part_q, a.flag_q, slot0, dt, acc, w, lane);
+    const int qr = sp.lo + 32 * w + n;
+    if (qr < sp.hi) store_quads_bf16((uint16_t*)a.dq + ((int64_t)qr * a.H + h) * HD, acc, a.scale, dt, hh);
 }
 
 }  // namespace bwd
@@ -611,11 +717,16 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (kb_cap <= 0 || a.N == 0) return hipSuccess;
-    const dim3 grid((unsigned)kb_cap, (unsigned)a.H);
+    const dim3 grid((unsigned)kb_cap, (unsigned)a.H, (unsigned)a.nc);
     hipLaunchKernelGGL(bwd::fm_bwd_dkdv_kernel, grid, dim3(bwd::NTK), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd::fm_bwd_dq_kernel, grid, dim3(bwd::NTQ), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess || a.nc <= 1) return e;
+    const dim3 rgrid((unsigned)kb_cap, (unsigned)a.H, (unsigned)bwd::RZ);
+    hipLaunchKernelGGL(bwd::fm_bwd_dkdv_reduce_kernel, rgrid, dim3(bwd::NTK), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd::fm_bwd_dq_reduce_kernel, rgrid, dim3(bwd::NTQ), 0, s, a);
     return hipGetLastError();
 }
 

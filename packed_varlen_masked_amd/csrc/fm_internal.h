@@ -99,6 +99,14 @@ struct BwdArgs {
     const int32_t* cu; const int32_t* sv; int n_vec; int causal;
     float scale, scale_log2;   // scale, scale * log2(e)
     const int32_t* kb_off; const int32_t* extrema; const int32_t* n_kb; const int32_t* status;
+    // small problems: the q tiles of a key tile (dK/dV) and the key blocks of
+    // a query tile (dQ) are cut into nc chunks of qc / kc that run as
+    // separate workgroups writing fp32 partials; two reduce launches sum
+    // them in chunk order.  nc == 1: no chunks, no partials.
+    int nc, qc, kc;
+    float* part_kv; int32_t* flag_kv;   // [slot_kv][nc] partials (128 KB each) and their flags
+    float* part_q; int32_t* flag_q;     // [slot_q][nc]
+    uint32_t call_id;                   // flag value of this call (never 0)
 };
 
 // Rotary embedding of q and k rows in place (bf16 or fp32).
@@ -110,6 +118,8 @@ struct RopeArgs {
 };
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 
+// Most chunks a backward tile is cut into (small problems).
+constexpr int BWD_MAX_CHUNKS = 8;
 // Key block (columns per extrema row) of the backward's plan.
 constexpr int bwd_block_k() { return 64; }
 // Delta, then dK/dV, then dQ; kb_cap bounds the number of 64-key blocks.
