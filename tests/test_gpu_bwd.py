@@ -173,3 +173,26 @@ def no_pairs_rows(w):
             rr = np.arange(r0, min(r0 + 1024, e))
             empty[rr] = O.element_mask(rr, cols, vecs, w.causal).all(axis=1)
     return empty, None
+
+
+def test_bwd_bad_cu_and_empty(pv):
+    """Decreasing cu_seqlens: the preprocessing sets the status word and the
+    backward writes nothing (dq, dk, dv keep their contents).  N = 0: no
+    work, no error."""
+    w = W.document_workload([100, 100, 56], H=2, seed=8)
+    q, k, v = (bf16(x).cuda() for x in (w.q, w.k, w.v))
+    sv = torch.from_numpy(np.ascontiguousarray(w.startend.astype(np.int32))).cuda()
+    cu = torch.tensor([0, 150, 100, w.N], dtype=torch.int32, device="cuda")
+    lse = torch.zeros(w.H, w.N, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(pv.bwd_workspace_size(w.N, 3, w.H, w.D, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    grads = [torch.full_like(q, 7.0) for _ in range(3)]
+    pv.attn_bwd(q, k, v, q, lse, q, cu, sv, w.n_vec, w.causal, workspace=ws, dq=grads[0], dk=grads[1], dv=grads[2])
+    assert pv.read_status(ws) & pv.FM_STATUS_ORDER
+    for t in grads:
+        assert torch.all(t == 7.0).item()
+    e = torch.empty(0, 2, 128, dtype=torch.bfloat16, device="cuda")
+    z = torch.zeros(2, dtype=torch.int32, device="cuda")
+    dq, dk, dv = pv.attn_bwd(e, e, e, e, torch.empty(2, 0, device="cuda"), e, z,
+                             torch.empty(1, 0, dtype=torch.int32, device="cuda"), 1, True)
+    torch.cuda.synchronize()
+    assert dq.shape == (0, 2, 128)

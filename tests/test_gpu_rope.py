@@ -107,3 +107,10 @@ def test_rope_sft_full(pv):
     check(gk, O.rope(w.k, w.cu_seqlens, cos, sin), torch.bfloat16)
     bq, _, st = run(pv, gq, None, w.cu_seqlens, cos, sin, torch.bfloat16, inverse=True)
     check(bq, O.rope(gq, w.cu_seqlens, cos, sin, inverse=True), torch.bfloat16)
+
+
+def test_rope_empty(pv):
+    e = torch.empty(0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    cos, sin = (torch.from_numpy(t).cuda() for t in W.rope_tables(4, 64))
+    pv.rope_qk_(e, e, torch.zeros(2, dtype=torch.int32, device="cuda"), cos, sin)
+    torch.cuda.synchronize()
