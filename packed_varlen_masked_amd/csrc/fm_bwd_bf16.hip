@@ -52,7 +52,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 constexpr int HD = 128;          // head_dim
 constexpr int BLK = 64;          // key block of the extrema; q rows per dK/dV step; keys per dQ step
 constexpr int NTH = 256;         // 4 waves
-constexpr int ROW_T = 320;       // LDS row stride (bytes) of tiles also read transposed
 constexpr int ROW_R = 272;       // LDS row stride of tiles read by rows only
 constexpr float LOG2E = 1.4426950408889634074f;
 
@@ -64,19 +63,33 @@ __device__ __attribute__((always_inline)) inline f32x16 mfma(bf16x8 a, bf16x8 b,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// A-operand fragment of the transpose of a row-major LDS tile (rows are the
-// MFMA's k index, channels its m index): channel block dt (32 channels),
-// k group kg (16 rows).  Within a group, lane half hh takes rows
-// 4hh + {0..3, 8..11}: the order in which an MFMA result holds its rows
-// (register e of a 32x32 result is row 8(e>>2) + 4hh + (e&3)), so the B
-// operand can be packed straight from such a result.
-template <int RS>
-__device__ __attribute__((always_inline)) inline bf16x8 tr_frag(const char* tile, int kg, int dt, int lane) {
+// A-operand fragments of the transpose of a row-major LDS tile (rows are
+// the MFMA's k index, channels its m index) come from the gfx950 LDS
+// transpose read: channel block dt (32 channels), k group kg (16 rows);
+// within a group, lane half hh takes rows 4hh + {0..3, 8..11}, the order in
+// which an MFMA result holds its rows (register e of a 32x32 result is row
+// 8(e>>2) + 4hh + (e&3)), so the B operand can be packed straight from such
+// a result.
+// Tiles read both by rows (A operands of S, dP) and transposed (A operands
+// of dV, dK, dQ) are stored with 256-byte rows, chunk c (16 bytes) of row r
+// at chunk c ^ swz(r): 16 consecutive rows of one chunk, and the 4 rows x 4
+// chunks of a transposed read, then fall in 16 distinct 4-bank groups
+// (with padded rows only one of the two patterns can be conflict-free).
+constexpr int ROW_S = 256;
+__device__ __attribute__((always_inline)) inline int swz(int r) {
+    r &= 15;
+    return ((r & 3) << 2) | (r >> 2);
+}
+__device__ __attribute__((always_inline)) inline int soff(int r, int c) { return r * ROW_S + 16 * (c ^ swz(r)); }
+// The transposed fragment (rows 16kg + 4hh + (gi>>2), +8; chunks
+// 4dt + 2(grp&1) + ((gi&3)>>1); 8-byte half gi&1) of a swizzled tile.
+__device__ __attribute__((always_inline)) inline bf16x8 tr_frag_s(const char* tile, int kg, int dt, int lane) {
     const int hh = lane >> 5, grp = lane >> 4, gi = lane & 15;
-    const char* p = tile + (4 * hh + (gi >> 2)) * RS + 16 * (2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1) +
-                    16 * kg * RS + 64 * dt;
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)p);
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)(p + 8 * RS));
+    const int r = 16 * kg + 4 * hh + (gi >> 2), c = 4 * dt + 2 * (grp & 1) + ((gi & 3) >> 1);
+    const char* p0 = tile + soff(r, c) + 8 * (gi & 1);
+    const char* p1 = tile + soff(r + 8, c) + 8 * (gi & 1);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)p0);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(void*)p1);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -173,7 +186,7 @@ __global__ __launch_bounds__(NTH) void fm_bwd_delta_kernel(BwdArgs a) {
 constexpr int NTK = 512;
 constexpr int QU = BLK * 16 / NTK;   // 16-byte chunks of Q (and of dO) per thread
 constexpr int KV_COMB = 4 * 64 * 16 * 16;   // bytes: one accumulator set of a group (16 x 16 B per lane)
-constexpr int OFF_G = BLK * ROW_T, OFF_L2 = 2 * BLK * ROW_T, OFF_DL = OFF_L2 + 4 * BLK;
+constexpr int OFF_G = BLK * ROW_S, OFF_L2 = 2 * BLK * ROW_S, OFF_DL = OFF_L2 + 4 * BLK;
 constexpr int DKV_LDS = KV_COMB > OFF_DL + 4 * BLK ? KV_COMB : OFF_DL + 4 * BLK;
 // staging (Q tile, dO tile, lse, Delta) during the loop, the group sums after it
 __shared__ __attribute__((aligned(16))) char s_dkv[DKV_LDS];
@@ -214,8 +227,8 @@ __device__ inline void store_qstage(const QStage& st, int tid) {
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
         const int c = tid + NTK * u, row = c >> 4, ch = c & 15;
-        *(u32x4*)(s_dkv + row * ROW_T + 16 * ch) = st.q[u];
-        *(u32x4*)(s_dkv + OFF_G + row * ROW_T + 16 * ch) = st.g[u];
+        *(u32x4*)(s_dkv + soff(row, ch)) = st.q[u];
+        *(u32x4*)(s_dkv + OFF_G + soff(row, ch)) = st.g[u];
     }
     if (tid < BLK) {
         ((float*)(s_dkv + OFF_L2))[tid] = st.l2;
@@ -425,12 +438,12 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
         f32x16 sc, dp;
 #pragma unroll
         for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
-        const char* qa = s_q + (32 * g + n) * ROW_T + 16 * hh;
-        const char* ga = s_g + (32 * g + n) * ROW_T + 16 * hh;
+        const int qrow = 32 * g + n;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            sc = mfma(as_bf16x8(*(const u32x4*)(qa + 32 * s)), as_bf16x8(*(const u32x4*)(kb_l + 32 * s)), sc);
-            dp = mfma(as_bf16x8(*(const u32x4*)(ga + 32 * s)), as_bf16x8(*(const u32x4*)(vb_l + 32 * s)), dp);
+            const int o = soff(qrow, 2 * s + hh);
+            sc = mfma(as_bf16x8(*(const u32x4*)(s_q + o)), as_bf16x8(*(const u32x4*)(kb_l + 32 * s)), sc);
+            dp = mfma(as_bf16x8(*(const u32x4*)(s_g + o)), as_bf16x8(*(const u32x4*)(vb_l + 32 * s)), dp);
         }
         // P = exp2(S scale log2e - lse2), masked pairs 0; dS = P (dP - Delta);
         // then dV^T += dO^T P and dK^T += Q^T dS for the 16-row group
@@ -462,8 +475,8 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
             }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                dv[dt] = mfma(tr_frag<ROW_T>(s_g, 2 * g + c2, dt, lane), pb, dv[dt]);
-                dk[dt] = mfma(tr_frag<ROW_T>(s_q, 2 * g + c2, dt, lane), db, dk[dt]);
+                dv[dt] = mfma(tr_frag_s(s_g, 2 * g + c2, dt, lane), pb, dv[dt]);
+                dk[dt] = mfma(tr_frag_s(s_q, 2 * g + c2, dt, lane), db, dk[dt]);
             }
         }
         i = ni;
@@ -506,7 +519,7 @@ __global__ __launch_bounds__(NTK) void fm_bwd_dkdv_reduce_kernel(BwdArgs a) {
 // ---- dQ --------------------------------------------------------------------
 constexpr int NTQ = 512;         // dQ workgroup: 8 waves, 256 queries (two waves per SIMD)
 constexpr int QBLK = NTQ / 128;  // 64-row blocks per dQ workgroup
-__shared__ __attribute__((aligned(16))) char s_k[BLK * ROW_T];
+__shared__ __attribute__((aligned(16))) char s_k[BLK * ROW_S];
 __shared__ __attribute__((aligned(16))) char s_v[BLK * ROW_R];
 
 // One key block's staging data in registers: 4 chunks of K and of V per
@@ -538,7 +551,7 @@ __device__ inline void store_kstage(const KStage& st, int tid) {
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
         const int c = tid + NTQ * u, row = c >> 4, ch = c & 15;
-        *(u32x4*)(s_k + row * ROW_T + 16 * ch) = st.k[u];
+        *(u32x4*)(s_k + soff(row, ch)) = st.k[u];
         *(u32x4*)(s_v + row * ROW_R + 16 * ch) = st.v[u];
     }
 }
@@ -642,13 +655,12 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e) { sc[t][e] = 0.f; dp[t][e] = 0.f; }
-        const char* ka = s_k + n * ROW_T + 16 * hh;
         const char* va = s_v + n * ROW_R + 16 * hh;
 #pragma unroll
         for (int s = 0; s < 8; ++s)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                sc[t] = mfma(as_bf16x8(*(const u32x4*)(ka + 32 * t * ROW_T + 32 * s)), qf[s], sc[t]);
+                sc[t] = mfma(as_bf16x8(*(const u32x4*)(s_k + soff(32 * t + n, 2 * s + hh))), qf[s], sc[t]);
                 dp[t] = mfma(as_bf16x8(*(const u32x4*)(va + 32 * t * ROW_R + 32 * s)), gf[s], dp[t]);
             }
         if (part) {   // keys k and k + 4 of register e: the masks built by lanes k and k + 4
@@ -676,7 +688,7 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
         for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-                dq[dt] = mfma(tr_frag<ROW_T>(s_k, kg, dt, lane), db[kg >> 1][kg & 1], dq[dt]);
+                dq[dt] = mfma(tr_frag_s(s_k, kg, dt, lane), db[kg >> 1][kg & 1], dq[dt]);
         kb = nkb;
         part = npart;
     }
