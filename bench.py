@@ -16,7 +16,9 @@ events stay out of the first pass because an event recorded between two
 launches keeps the GPU from starting the next launch while the previous one
 drains (several microseconds per step at the small configurations).
 The oracle (fp64 NumPy, the parity reference) is timed on the host cores
-on a bounded sample of the same workload as the CPU baseline.
+on a bounded sample of the same workload as the CPU baseline.  For bf16
+workloads the line also reports, for information, the backward (dq, dk,
+dv) and the fused q/k rotary embedding on the same inputs.
 """
 from __future__ import annotations
 
@@ -411,6 +413,45 @@ def rope_bench(args):
                                  "what": "mean of a forward and an inverse call"}}), flush=True)
 
 
+def extra_legs(w, st, K, flops):
+    """Beside the headline (the forward step): the backward and the fused
+    q/k rotary embedding on the same workload and inputs, each timed over K
+    back-to-back calls (informational; the metric is the forward's)."""
+    import torch
+    import packed_varlen_masked_amd as pv
+    import workloads as W
+    q, k, v, cu, sv = st["tensors"]
+    out, lse = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale))
+    g = torch.from_numpy(np.random.default_rng(w.meta["seed"] + 2).standard_normal(
+        (w.N, w.H, w.D), dtype=np.float32)).to(torch.bfloat16).to(q.device)
+    ws = torch.zeros(pv.bwd_workspace_size(w.N, w.B, w.H, w.D, torch.bfloat16), dtype=torch.uint8, device=q.device)
+    grads = [torch.empty_like(q) for _ in range(3)]
+
+    def bwd():
+        pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale), workspace=ws,
+                    dq=grads[0], dk=grads[1], dv=grads[2])
+    for _ in range(5):
+        bwd()
+    ms_b, _, _ = time_calls(bwd, K)
+    qr, kr = q.clone(), k.clone()
+    cos, sin = (torch.from_numpy(t).to(q.device) for t in W.rope_tables(int(w.lengths.max()), w.D))
+
+    def rope():   # forward then inverse: the data stays bounded
+        pv.rope_qk_(qr, kr, cu, cos, sin)
+        pv.rope_qk_(qr, kr, cu, cos, sin, inverse=True)
+    for _ in range(5):
+        rope()
+    ms_r, _, _ = time_calls(rope, K)
+    rope_bytes = 2 * 2 * w.N * w.H * w.D * 2 + w.N * w.D * 4
+    return {"backward": {"what": "fm_attn_bwd (dq, dk, dv) on the same inputs; useful work = 5 products per "
+                                 "unmasked pair = 2.5 x the forward's effective FLOPs",
+                         "ms_per_call": round(ms_b, 6),
+                         "effective_TFLOP_s": round(2.5 * flops / (ms_b * 1e-3) / 1e12, 3)},
+            "rope": {"what": "fm_rope_qk on the workload's q and k in place (mean of a forward and an inverse call)",
+                     "ms_per_call": round(ms_r / 2, 6),
+                     "achieved_GB_s": round(rope_bytes / (ms_r / 2 * 1e-3) / 1e9, 1)}}
+
+
 def main():
     args = parse()
     if args.preprocess_sweep:
@@ -505,6 +546,8 @@ def main():
                         "ms_per_call": round(ms_reuse, 6),
                         "effective_TFLOP_s": round(flops / (ms_reuse * 1e-3) / 1e12, 3)},
     }
+    if dt == torch.bfloat16:
+        res.update(extra_legs(w, st, K, flops))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, flops, args.cpu_seconds)
     print(json.dumps(res), flush=True)
