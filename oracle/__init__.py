@@ -21,4 +21,5 @@ from .flashmask import (  # noqa: F401
     attention_bwd_rows, extrema,
     classify, class_counts, worklist, unmasked_pairs, effective_flops,
     fa_varlen_grid_blocks, rope,
+    philox4x32_10, dropout_threshold, dropout_keep, attention_dropout, attention_bwd_dropout,
 )

@@ -478,3 +478,141 @@ def rope(x, cu_seqlens, cos, sin, inverse: bool = False):
     ss = np.concatenate([s[pos], s[pos]], axis=1)[:, None, :]
     rot = np.concatenate([-x[..., D // 2:], x[..., :D // 2]], axis=-1)
     return x * cc + rot * ss
+
+
+# --------------------------------------------------------------- dropout
+_PH_M0, _PH_M1 = 0xD2511F53, 0xCD9E8D57      # Philox4x32 multipliers
+_PH_W0, _PH_W1 = 0x9E3779B9, 0xBB67AE85      # Weyl key increments
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
+    as easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64 products
+    and xors with the key, the key advancing by the Weyl constants between
+    rounds.  ctr: uint array [..., 4], key: uint array [..., 2] (broadcast);
+    returns uint32 [..., 4].  Arithmetic in uint64 (exact products)."""
+    c = [np.asarray(ctr[..., i], np.uint64) & np.uint64(0xFFFFFFFF) for i in range(4)]
+    k0 = np.asarray(key[..., 0], np.uint64) & np.uint64(0xFFFFFFFF)
+    k1 = np.asarray(key[..., 1], np.uint64) & np.uint64(0xFFFFFFFF)
+    mask = np.uint64(0xFFFFFFFF)
+    for r in range(10):
+        if r:
+            k0 = (k0 + np.uint64(_PH_W0)) & mask
+            k1 = (k1 + np.uint64(_PH_W1)) & mask
+        p0 = np.uint64(_PH_M0) * c[0]
+        p1 = np.uint64(_PH_M1) * c[2]
+        hi0, lo0 = p0 >> np.uint64(32), p0 & mask
+        hi1, lo1 = p1 >> np.uint64(32), p1 & mask
+        c = [hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0]
+    return np.stack(c, axis=-1).astype(np.uint32)
+
+
+def dropout_threshold(p: float) -> int:
+    """Dropout probability p in [0, 1) as the byte threshold t = round(256 p)
+    (a key is dropped when its byte is below t): the effective drop
+    probability is t / 256 and kept values are scaled by 256 / (256 - t)."""
+    if not (0.0 <= p < 1.0):
+        raise ValueError("dropout probability must be in [0, 1)")
+    return min(255, int(np.floor(p * 256.0 + 0.5)))
+
+
+def dropout_keep(rows, cols, seq_start, h: int, seed: int, offset: int, t: int):
+    """Keep mask [len(rows), len(cols)] of one head: the byte of pair (i, j)
+    is byte (j - s) & 15 (little-endian within the four words) of
+    Philox4x32-10 with key (seed mod 2^32, seed >> 32) and counter
+    (i, (j - s) >> 4, h, offset mod 2^32), s the start of the pair's
+    sequence; kept when the byte is >= t.  (The pages name the op's
+    dropout attribute and seed_offset input, FlashMask article §3.4; this
+    counter layout is this library's.)"""
+    i = np.asarray(rows, np.int64)[:, None]
+    jl = np.asarray(cols, np.int64)[None, :] - int(seq_start)
+    ctr = np.stack(np.broadcast_arrays(i, jl >> 4, np.int64(h), np.int64(offset & 0xFFFFFFFF)), axis=-1)
+    key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], np.uint64)
+    words = philox4x32_10(ctr.astype(np.uint64), key)
+    k = jl & 15
+    w = np.take_along_axis(words, np.broadcast_to(k >> 2, words.shape[:-1])[..., None], axis=-1)[..., 0]
+    byte = (w >> (8 * (k & 3)).astype(np.uint32)) & np.uint32(0xFF)
+    return byte >= np.uint32(t)
+
+
+def attention_dropout(q, k, v, cu_seqlens, startend, n_vec: int, causal: bool, scale, p: float,
+                      seed: int, offset: int, chunk: int = 512):
+    """Forward with attention dropout, float64: the forward's P (normalised
+    over the allowed keys, lse unchanged) times the keep mask and
+    256 / (256 - t); out = (P o keep * scale_keep) V.  p = 0 gives
+    `attention` exactly."""
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    N, H, D = q.shape
+    t = dropout_threshold(p)
+    ks = 256.0 / (256.0 - t)
+    vecs = fill_vectors(startend, n_vec, causal, N)
+    cu = np.asarray(cu_seqlens, np.int64)
+    scale = float(np.float64(scale))
+    out = np.zeros((N, H, D), np.float64)
+    lse = np.full((H, N), -np.inf, np.float64)
+    for b in range(len(cu) - 1):
+        s, e = _seq_bounds(cu, b)
+        if e <= s:
+            continue
+        cols = np.arange(s, e)
+        for h in range(H):
+            for r0 in range(s, e, chunk):
+                r1 = min(r0 + chunk, e)
+                rows = np.arange(r0, r1)
+                sc = scale * (q[r0:r1, h, :] @ k[s:e, h, :].T)
+                sc = np.where(element_mask(rows, cols, vecs, causal), -np.inf, sc)
+                mx = sc.max(axis=1, keepdims=True)
+                ok = np.isfinite(mx[:, 0])
+                mx = np.where(np.isfinite(mx), mx, 0.0)
+                pe = np.exp(sc - mx)
+                ssum = pe.sum(axis=1, keepdims=True)
+                pn = np.divide(pe, ssum, out=np.zeros_like(pe), where=ssum > 0)
+                keep = dropout_keep(rows, cols, s, h, seed, offset, t)
+                out[r0:r1, h, :] = (pn * keep * ks) @ v[s:e, h, :]
+                with np.errstate(divide="ignore"):
+                    lse[h, r0:r1] = np.where(ok, mx[:, 0] + np.log(np.where(ok, ssum[:, 0], 1.0)), -np.inf)
+    return out, lse
+
+
+def attention_bwd_dropout(q, k, v, dout, cu_seqlens, startend, n_vec: int, causal: bool, scale, p: float,
+                          seed: int, offset: int, chunk: int = 512):
+    """Gradients of `attention_dropout` (the keep mask is a constant of the
+    inputs): with Z = keep * 256 / (256 - t),
+      dv_j = sum_i P_ij Z_ij dout_i,   dP_ij = Z_ij <dout_i, v_j>,
+      dS_ij = P_ij (dP_ij - sum_l P_il dP_il),
+      dq_i = scale sum_j dS_ij k_j,    dk_j = scale sum_i dS_ij q_i.
+    Pinned by central finite differences of `attention_dropout`."""
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64); g = np.asarray(dout, np.float64)
+    N, H, D = q.shape
+    t = dropout_threshold(p)
+    ks = 256.0 / (256.0 - t)
+    vecs = fill_vectors(startend, n_vec, causal, N)
+    cu = np.asarray(cu_seqlens, np.int64)
+    scale = float(np.float64(scale))
+    dq = np.zeros((N, H, D)); dk = np.zeros((N, H, D)); dv = np.zeros((N, H, D))
+    for b in range(len(cu) - 1):
+        s, e = _seq_bounds(cu, b)
+        if e <= s:
+            continue
+        cols = np.arange(s, e)
+        for h in range(H):
+            kh, vh = k[s:e, h, :], v[s:e, h, :]
+            for r0 in range(s, e, chunk):
+                r1 = min(r0 + chunk, e)
+                rows = np.arange(r0, r1)
+                sc = scale * (q[r0:r1, h, :] @ kh.T)
+                sc = np.where(element_mask(rows, cols, vecs, causal), -np.inf, sc)
+                mx = sc.max(axis=1, keepdims=True)
+                mx = np.where(np.isfinite(mx), mx, 0.0)
+                pe = np.exp(sc - mx)
+                ssum = pe.sum(axis=1, keepdims=True)
+                pn = np.divide(pe, ssum, out=np.zeros_like(pe), where=ssum > 0)
+                z = dropout_keep(rows, cols, s, h, seed, offset, t) * ks
+                gh = g[r0:r1, h, :]
+                dv[s:e, h, :] += (pn * z).T @ gh
+                dp = (gh @ vh.T) * z
+                ds = pn * (dp - (pn * dp).sum(axis=1, keepdims=True))
+                dq[r0:r1, h, :] = scale * (ds @ kh)
+                dk[s:e, h, :] += scale * (ds.T @ q[r0:r1, h, :])
+    return dq, dk, dv

@@ -545,6 +545,84 @@ def test_rope_relative_positions():
         assert abs(a - b) < 1e-4 * (1 + abs(a))
 
 
+# --------------------------------------------------------------- dropout
+def test_philox_statistics():
+    """Philox4x32-10 as a counter-based generator: bytes uniform (chi-square
+    over 2^20 bytes), one counter bit flipped changes about half of the 128
+    output bits, different keys give unrelated streams, and the same
+    (counter, key) always gives the same words."""
+    ctr = np.zeros((65536, 4), np.uint64)
+    ctr[:, 0] = np.arange(65536)
+    ctr[:, 1] = 7
+    key = np.array([0x1234567, 0x89ABCDE], np.uint64)
+    w = O.philox4x32_10(ctr, key)
+    by = w.view(np.uint8).reshape(-1)
+    cnt = np.bincount(by, minlength=256)
+    chi2 = float(((cnt - by.size / 256) ** 2 / (by.size / 256)).sum())
+    assert chi2 < 255 + 6 * np.sqrt(2 * 255)
+    ctr2 = ctr.copy()
+    ctr2[:, 2] ^= np.uint64(1 << 13)
+    w2 = O.philox4x32_10(ctr2, key)
+    flips = np.unpackbits((w ^ w2).view(np.uint8)).reshape(65536, -1).sum(axis=1)
+    assert abs(flips.mean() - 64) < 0.5 and flips.min() > 20
+    w3 = O.philox4x32_10(ctr, key + np.uint64(1))
+    assert np.mean(w3 == w) < 1e-3
+    assert np.array_equal(O.philox4x32_10(ctr, key), w)
+
+
+def test_dropout_p0_and_keep_fraction():
+    """p = 0 is plain attention (to fp64 rounding: the normalisation is
+    applied before the product here); the kept fraction of pairs matches
+    1 - t/256 within five standard deviations."""
+    w = W.document_workload([40, 200, 300], H=2, D=16, seed=3)
+    a = O.attention(w.q, w.k, w.v, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)
+    b = O.attention_dropout(w.q, w.k, w.v, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale, 0.0, 9, 0)
+    assert np.allclose(a[0], b[0], atol=1e-12, rtol=0) and np.array_equal(a[1], b[1])
+    for p in (0.1, 0.5):
+        t = O.dropout_threshold(p)
+        kept = n = 0
+        for bb, (s_, e_) in enumerate(zip(w.cu_seqlens[:-1], w.cu_seqlens[1:])):
+            km = O.dropout_keep(np.arange(s_, e_), np.arange(s_, e_), s_, 1, 12345, 77, t)
+            kept += int(km.sum()); n += km.size
+        q = 1 - t / 256
+        assert abs(kept / n - q) < 5 * np.sqrt(q * (1 - q) / n)
+
+
+def test_dropout_expectation():
+    """Dropout scales kept values by 256 / (256 - t): averaged over seeds the
+    output approaches the output without dropout."""
+    w = W.document_workload([24, 40], H=1, D=8, seed=4)
+    ref = O.attention(w.q, w.k, w.v, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)[0]
+    n = 400
+    acc = sum(O.attention_dropout(w.q, w.k, w.v, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale, 0.25,
+                                  seed, 5)[0] for seed in range(n)) / n
+    assert np.max(np.abs(acc - ref)) < 0.15 and np.mean(np.abs(acc - ref)) < 0.03
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_dropout_bwd_finite_differences(seed):
+    """The dropout backward against central differences of the dropout
+    forward (the keep mask does not depend on q, k, v)."""
+    w = W.random_case(600 + seed, N_max=16, H=2, D=3, dtype=W.F32, allow_empty=True)
+    G = np.random.default_rng(seed).standard_normal(w.q.shape)
+    q, k, v = (x.astype(np.float64) for x in (w.q, w.k, w.v))
+    args = (w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale, 0.3, 1000 + seed, 3)
+    grads = O.attention_bwd_dropout(q, k, v, G, *args)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(G * O.attention_dropout(qq, kk, vv, *args)[0]))
+    eps = 1e-6
+    for which, grad in enumerate(grads):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            xp = [q.copy(), k.copy(), v.copy()]
+            xm = [q.copy(), k.copy(), v.copy()]
+            xp[which][idx] += eps
+            xm[which][idx] -= eps
+            num[idx] = (loss(*xp) - loss(*xm)) / (2 * eps)
+        assert np.max(np.abs(num - grad)) < 1e-6, (which, np.max(np.abs(num - grad)))
+
+
 # ------------------------------------------------------------- worklist
 @pytest.mark.parametrize("seed", range(8))
 @pytest.mark.parametrize("S", [0, 1, 2, 3, 5])
