@@ -61,6 +61,9 @@ def parse():
                          "with cu = [0, N], zero-padded, zero-padded with the padding masked), step time each")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward step: time the backward (dq, dk, dv) on the workload")
+    ap.add_argument("--dropout", type=float, default=None, metavar="P",
+                    help="time the forward and the backward with attention dropout P beside the plain ones "
+                         "on workload --config")
     ap.add_argument("--rope", action="store_true",
                     help="instead of the forward step: time the fused q/k rotary embedding on the workload")
     ap.add_argument("--packings", default=",".join(("varlen", "mask_only", "padded", "padded_masked")),
@@ -375,6 +378,65 @@ def backward_bench(args):
           flush=True)
 
 
+def dropout_bench(args):
+    """Forward and backward with attention dropout p (Philox4x32-10 keep
+    mask regenerated per element in both) beside the plain ones, on the same
+    inputs; the useful work is counted as without dropout."""
+    import torch
+    import workloads as W
+    import oracle as O
+    import packed_varlen_masked_amd as pv
+    w = W.make_config(args.config, seed=args.seed)
+    if w.dtype != W.BF16:
+        raise SystemExit("dropout is built for the bf16 workloads (configs 2-5)")
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in (w.q, w.k, w.v))
+    cu = torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(dev)
+    sv = torch.from_numpy(np.ascontiguousarray(w.startend.astype(np.int32))).to(dev)
+    g = torch.from_numpy(np.random.default_rng(w.meta["seed"] + 2).standard_normal(
+        (w.N, w.H, w.D), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    wsb = torch.zeros(pv.bwd_workspace_size(w.N, w.B, w.H, w.D, torch.bfloat16), dtype=torch.uint8, device=dev)
+    pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
+    flops = O.effective_flops(pairs, w.H, w.D)
+    res = {}
+    for p in (0.0, args.dropout):
+        kw = dict(dropout_p=p, seed=0x5EED, offset=1) if p > 0 else {}
+        plan = pv.build_plan(cu, sv, w.n_vec, w.causal, w.N, w.H, w.D, torch.bfloat16, max_kb_per_item=args.split)
+        out = torch.empty_like(q)
+        lse = torch.empty(w.H, w.N, dtype=torch.float32, device=dev)
+        wsf = torch.zeros_like(plan.workspace)
+        fused = pv.fused_path(w.N, w.B, w.H, w.D, torch.bfloat16, w.n_vec, w.causal, plan.max_kb_per_item) and p == 0
+
+        def fwd():
+            if fused:
+                pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), max_kb_per_item=plan.max_kb_per_item,
+                            out=out, lse=lse, workspace=wsf)
+            else:
+                pv.build_plan_into(plan, cu, sv)
+                pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), plan=plan, out=out, lse=lse, **kw)
+        grads = [torch.empty_like(q) for _ in range(3)]
+
+        def bwd():
+            pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale), workspace=wsb,
+                        dq=grads[0], dk=grads[1], dv=grads[2], **kw)
+        for _ in range(args.warmup):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        ms_f, _, _ = time_calls(fwd, args.steps)
+        ms_b, _, _ = time_calls(bwd, args.steps)
+        res["p=%g" % p] = {"forward_ms": round(ms_f, 6), "forward_TFLOP_s": round(flops / (ms_f * 1e-3) / 1e12, 3),
+                           "backward_ms": round(ms_b, 6),
+                           "backward_TFLOP_s": round(2.5 * flops / (ms_b * 1e-3) / 1e12, 3),
+                           "path": "fused" if fused else "planned"}
+    print(json.dumps({"metric": "forward and backward with attention dropout, effective TFLOP/s (work counted "
+                                "as without dropout)", "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "dtype": "bf16", "data": "synthetic (seeded N(0,1) q/k/v/dout)",
+                      "config": {"workload": w.name, "N": w.N, "B": w.B, "H": w.H, "D": w.D,
+                                 "causal": bool(w.causal), "n_vec": w.n_vec, "dropout_p": args.dropout},
+                      "results": res}), flush=True)
+
+
 def rope_bench(args):
     """The fused rotary embedding of the workload's q and k in place (one
     launch for both, positions restarting per document).  HBM-bound:
@@ -469,6 +531,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.dropout is not None:
+        dropout_bench(args)
         return
     if args.rope:
         rope_bench(args)

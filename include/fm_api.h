@@ -272,6 +272,27 @@ int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype,
                 unsigned flags, hipStream_t stream);
 
 /*
+ * fm_attn_fwd with attention dropout on the probabilities ([FM] §3.4: the
+ * op's dropout attribute and seed_offset input).  Pair (i, j) of head h in
+ * a sequence starting at s is dropped when byte (j - s) & 15 of
+ * Philox4x32-10 (Salmon et al., SC 2011) with key (seed mod 2^32,
+ * seed >> 32) and counter (i, (j - s) >> 4, h, offset mod 2^32) is below
+ * t = round(256 dropout_p) (little-endian bytes of the four words); kept
+ * probabilities are scaled by 256 / (256 - t), so the effective dropout
+ * probability is t / 256.  softmax_lse is the undropped normaliser.
+ * 0 <= dropout_p < 1 (t = 0: no dropout, the same call as fm_attn_fwd);
+ * bf16 only, not with FM_FLAG_NO_SKIP; always the planned path (never the
+ * fused one).  The same (seed, offset) give the same mask in the backward.
+ */
+int fm_attn_fwd_dropout(const void* q, const void* k, const void* v, int dtype,
+                        int64_t N, int H, int D, const int32_t* cu_seqlens, int B,
+                        const int32_t* startend, int n_vec, int causal, float scale,
+                        void* out, float* softmax_lse, int block_q, int block_k,
+                        int max_kb_per_item, void* workspace, size_t ws_bytes,
+                        unsigned flags, float dropout_p, uint64_t seed, uint64_t offset,
+                        hipStream_t stream);
+
+/*
  * 1 if fm_attn_fwd with these sizes and flags takes the fused one-launch
  * path (bf16, head_dim 128, default tiles, no FM_FLAG_NO_SKIP or
  * FM_FLAG_PLAN_READY, B <= 255, n_vec * N <= 16384, and the plan's bounds
@@ -323,6 +344,18 @@ int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, co
                 const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
                 float scale, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                 hipStream_t stream);
+
+/*
+ * fm_attn_bwd for a forward run with fm_attn_fwd_dropout: the same
+ * (dropout_p, seed, offset) regenerate the forward's mask; with Z = keep *
+ * 256 / (256 - t): dv = (P Z)^T dout, dS = P (Z (dout v^T) - Delta),
+ * Delta_i = <dout_i, out_i>.
+ */
+int fm_attn_bwd_dropout(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* softmax_lse, int dtype, int64_t N, int H, int D,
+                        const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
+                        float scale, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                        float dropout_p, uint64_t seed, uint64_t offset, hipStream_t stream);
 
 /*
  * Rotary position embedding of packed q and k, in place, one launch for

@@ -490,7 +490,12 @@ def philox4x32_10(ctr, key):
     as easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64 products
     and xors with the key, the key advancing by the Weyl constants between
     rounds.  ctr: uint array [..., 4], key: uint array [..., 2] (broadcast);
-    returns uint32 [..., 4].  Arithmetic in uint64 (exact products)."""
+    returns uint32 [..., 4].  Arithmetic in uint64 (exact products).
+
+    Pinned by statistics only (uniform bytes, avalanche on one counter bit,
+    unrelated streams for different keys, determinism).  That the stream
+    is bit for bit the published generator's is parity unpinned: no
+    known-answer vectors of the paper are stored here."""
     c = [np.asarray(ctr[..., i], np.uint64) & np.uint64(0xFFFFFFFF) for i in range(4)]
     k0 = np.asarray(key[..., 0], np.uint64) & np.uint64(0xFFFFFFFF)
     k1 = np.asarray(key[..., 1], np.uint64) & np.uint64(0xFFFFFFFF)

@@ -61,8 +61,8 @@ def _load():
         raise ImportError("%s is missing: build it with `python packed_varlen_masked_amd/build.py` "
                           "(or __graft_entry__.build())" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
-    P, I, I64, U, SZ, F = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint,
-                           ctypes.c_size_t, ctypes.c_float)
+    P, I, I64, U, SZ, F, U64 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint,
+                                ctypes.c_size_t, ctypes.c_float, ctypes.c_uint64)
     sig = {
         "fm_last_error": (ctypes.c_char_p, []),
         "fm_version": (I, []),
@@ -81,6 +81,8 @@ def _load():
         "fm_bwd_workspace_size": (SZ, [I64, I, I, I, I]),
         "fm_attn_bwd": (I, [P, P, P, P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, P, P, SZ, P]),
         "fm_rope_qk": (I, [P, P, I, I64, I, I, I, P, I, P, P, I64, I, P, P]),
+        "fm_attn_fwd_dropout": (I, [P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, I, I, I, P, SZ, U, F, U64, U64, P]),
+        "fm_attn_bwd_dropout": (I, [P, P, P, P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, P, P, SZ, F, U64, U64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -93,7 +95,8 @@ _lib = _load()
 EXPORTED = ("fm_last_error", "fm_version", "fm_self_check", "fm_get_tile_config", "fm_auto_split",
             "fm_workspace_layout", "fm_workspace_size", "fm_worklist_scratch_size",
             "fm_preprocess_mask", "fm_build_worklist", "fm_build_plan", "fm_attn_fwd",
-            "fm_read_status", "fm_fused_path", "fm_bwd_workspace_size", "fm_attn_bwd", "fm_rope_qk")
+            "fm_read_status", "fm_fused_path", "fm_bwd_workspace_size", "fm_attn_bwd", "fm_rope_qk",
+            "fm_attn_fwd_dropout", "fm_attn_bwd_dropout")
 
 
 def _check(rc: int):
@@ -291,10 +294,12 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
              startend: torch.Tensor, n_vec: int, causal: bool, scale: Optional[float] = None,
              plan: Optional[Plan] = None, max_kb_per_item: int = -1, block_q: int = 0,
              block_k: int = 0, flags: int = 0, out: Optional[torch.Tensor] = None,
-             lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+             lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
     """FlashMask forward.  q, k, v: [N, H, D] bf16 or fp32 (contiguous, same
     device); cu_seqlens int32 [B+1]; startend int32 [n_vec, N] (global row
-    indices).  Returns (out [N, H, D], softmax_lse fp32 [H, N])."""
+    indices).  dropout_p > 0 (bf16): attention dropout with the Philox mask
+    of (seed, offset).  Returns (out [N, H, D], softmax_lse fp32 [H, N])."""
     if q.shape != k.shape or q.shape != v.shape or q.dim() != 3:
         raise FMError(FM_E_INVAL, "q, k, v must share one [N, H, D] shape")
     if not (q.dtype == k.dtype == v.dtype):
@@ -326,9 +331,15 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(H, N, dtype=torch.float32, device=q.device)
-    _check(_lib.fm_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), N, H, D, _ptr(cu), B,
-                            _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
-                            _ptr(out), _ptr(lse), bq, bk, S, _ptr(ws), ws.numel(), flags, _stream()))
+    if dropout_p > 0.0:
+        _check(_lib.fm_attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), N, H, D, _ptr(cu), B,
+                                        _ptr(startend) if N > 0 else None, n_vec, int(causal),
+                                        ctypes.c_float(scale), _ptr(out), _ptr(lse), bq, bk, S, _ptr(ws),
+                                        ws.numel(), flags, ctypes.c_float(dropout_p), seed, offset, _stream()))
+    else:
+        _check(_lib.fm_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), N, H, D, _ptr(cu), B,
+                                _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
+                                _ptr(out), _ptr(lse), bq, bk, S, _ptr(ws), ws.numel(), flags, _stream()))
     return out, lse
 
 
@@ -343,7 +354,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
              dout: torch.Tensor, cu_seqlens: torch.Tensor, startend: torch.Tensor, n_vec: int, causal: bool,
              scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None):
+             dv: Optional[torch.Tensor] = None, dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
     """FlashMask backward.  q, k, v, out, dout: [N, H, D] bf16 (contiguous,
     same device); lse fp32 [H, N] from the forward; cu_seqlens and startend
     as for attn_fwd.  Returns (dq, dk, dv) [N, H, D] bf16."""
@@ -374,10 +385,13 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise FMError(FM_E_INVAL, "%s must be contiguous with q's shape and dtype" % nm)
-    _check(_lib.fm_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
-                            _dtype_code(q.dtype), N, H, D, _ptr(cu), B,
-                            _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
-                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream()))
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q.dtype), N, H, D,
+              _ptr(cu), B, _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
+              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel())
+    if dropout_p > 0.0:
+        _check(_lib.fm_attn_bwd_dropout(*common, ctypes.c_float(dropout_p), seed, offset, _stream()))
+    else:
+        _check(_lib.fm_attn_bwd(*common, _stream()))
     return dq, dk, dv
 
 

@@ -450,13 +450,27 @@ int fm_build_plan(const int32_t* cu_seqlens, int B, int64_t N, int H, int head_d
     return rc ? rc : ok();
 }
 
-int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t N, int H, int D,
-                const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
-                float scale, void* out, float* softmax_lse, int block_q, int block_k,
-                int max_kb_per_item, void* workspace, size_t ws_bytes, unsigned flags,
-                hipStream_t stream) {
+// Dropout probability -> byte threshold t = round(256 p) (0: no dropout) and
+// the scale 256 / (256 - t) of kept values.
+static int dropout_params(float p, int* t, float* ks) {
+    if (!(p >= 0.f && p < 1.f)) return fail(FM_E_INVAL, "dropout probability must be in [0, 1) (got %g)", (double)p);
+    *t = std::min(255, (int)floor((double)p * 256.0 + 0.5));
+    *ks = (float)(256.0 / (256.0 - *t));
+    return FM_OK;
+}
+
+static int attn_fwd_impl(const void* q, const void* k, const void* v, int dtype, int64_t N, int H, int D,
+                  const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
+                  float scale, void* out, float* softmax_lse, int block_q, int block_k,
+                  int max_kb_per_item, void* workspace, size_t ws_bytes, unsigned flags,
+                  float dropout_p, uint64_t seed, uint64_t offset, hipStream_t stream) {
     int rc = check_sizes(N, B, H);
     if (rc) return rc;
+    int drop_t = 0;
+    float drop_ks = 1.f;
+    if ((rc = dropout_params(dropout_p, &drop_t, &drop_ks))) return rc;
+    if (drop_t > 0 && (dtype != FM_BF16 || (flags & FM_FLAG_NO_SKIP)))
+        return fail(FM_E_UNSUPPORTED, "dropout is built for the bf16 path without FM_FLAG_NO_SKIP");
     int dq, dk;
     if ((rc = tile_config(dtype, D, &dq, &dk))) return rc;
     const int bq = block_q ? block_q : dq, bk = block_k ? block_k : dk;
@@ -484,7 +498,7 @@ int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t 
     w.base = (char*)workspace;
     int n_cu = 0;
     if ((rc = device_cus(&n_cu))) return rc;
-    const bool fused = fused_eligible(N, B, H, dtype, D, bq, bk, S, n_vec, flags, n_cu);
+    const bool fused = drop_t == 0 && fused_eligible(N, B, H, dtype, D, bq, bk, S, n_vec, flags, n_cu);
     if (!fused && !(flags & FM_FLAG_PLAN_READY)) {
         if ((rc = build_plan_impl(w, cu_seqlens, B, N, H, startend, n_vec, causal, stream))) return rc;
     }
@@ -518,11 +532,32 @@ int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t 
     a.w_items = (int32_t*)(w.base + w.L.off_items);
     a.w_counts = w.counts();
     a.w_merge = S > 0 ? (int32_t*)(w.base + w.L.off_merge) : nullptr;
+    a.drop_t = drop_t; a.drop_ks = drop_ks;
+    a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32); a.offset = (uint32_t)offset;
     const hipError_t e = fused ? fm::launch_fused_bf16(a, n_cu, stream)
                        : dtype == FM_BF16 ? fm::launch_attn_bf16(a, n_cu, stream)
                                           : fm::launch_attn_f32(a, n_cu, stream);
     if ((rc = hip_check(e, "attention launch"))) return rc;
     return ok();
+}
+
+int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t N, int H, int D,
+                const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
+                float scale, void* out, float* softmax_lse, int block_q, int block_k,
+                int max_kb_per_item, void* workspace, size_t ws_bytes, unsigned flags,
+                hipStream_t stream) {
+    return attn_fwd_impl(q, k, v, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal, scale, out, softmax_lse,
+                         block_q, block_k, max_kb_per_item, workspace, ws_bytes, flags, 0.f, 0, 0, stream);
+}
+
+int fm_attn_fwd_dropout(const void* q, const void* k, const void* v, int dtype, int64_t N, int H, int D,
+                        const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
+                        float scale, void* out, float* softmax_lse, int block_q, int block_k,
+                        int max_kb_per_item, void* workspace, size_t ws_bytes, unsigned flags,
+                        float dropout_p, uint64_t seed, uint64_t offset, hipStream_t stream) {
+    return attn_fwd_impl(q, k, v, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal, scale, out, softmax_lse,
+                         block_q, block_k, max_kb_per_item, workspace, ws_bytes, flags, dropout_p, seed, offset,
+                         stream);
 }
 
 int fm_fused_path(int64_t N, int B, int H, int head_dim, int dtype, int n_vec, int causal,
@@ -541,12 +576,16 @@ size_t fm_bwd_workspace_size(int64_t N, int B, int H, int head_dim, int dtype) {
     return L.bytes;
 }
 
-int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                const float* softmax_lse, int dtype, int64_t N, int H, int D, const int32_t* cu_seqlens,
-                int B, const int32_t* startend, int n_vec, int causal, float scale, void* dq, void* dk,
-                void* dv, void* workspace, size_t ws_bytes, hipStream_t stream) {
+static int attn_bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                  const float* softmax_lse, int dtype, int64_t N, int H, int D, const int32_t* cu_seqlens,
+                  int B, const int32_t* startend, int n_vec, int causal, float scale, void* dq, void* dk,
+                  void* dv, void* workspace, size_t ws_bytes, float dropout_p, uint64_t seed, uint64_t offset,
+                  hipStream_t stream) {
     int rc = check_sizes(N, B, H);
     if (rc) return rc;
+    int drop_t = 0;
+    float drop_ks = 1.f;
+    if ((rc = dropout_params(dropout_p, &drop_t, &drop_ks))) return rc;
     if ((rc = bwd_supported(dtype, D))) return rc;
     if (!mask_form_ok(n_vec, causal))
         return fail(FM_E_INVAL, "unsupported (n_vec=%d, causal=%d)", n_vec, causal);
@@ -580,8 +619,27 @@ int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, co
     a.part_q = L.nc > 1 ? (float*)(base + L.off_part_q) : nullptr;
     a.flag_q = L.nc > 1 ? (int32_t*)(base + L.off_flag_q) : nullptr;
     a.call_id = next_call_id();
+    a.drop_t = drop_t; a.drop_ks = drop_ks;
+    a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32); a.offset = (uint32_t)offset;
     if ((rc = hip_check(fm::launch_bwd_bf16(a, L.kb_cap, stream), "backward launch"))) return rc;
     return ok();
+}
+
+int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                const float* softmax_lse, int dtype, int64_t N, int H, int D, const int32_t* cu_seqlens,
+                int B, const int32_t* startend, int n_vec, int causal, float scale, void* dq, void* dk,
+                void* dv, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return attn_bwd_impl(q, k, v, out, dout, softmax_lse, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal,
+                         scale, dq, dk, dv, workspace, ws_bytes, 0.f, 0, 0, stream);
+}
+
+int fm_attn_bwd_dropout(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* softmax_lse, int dtype, int64_t N, int H, int D, const int32_t* cu_seqlens,
+                        int B, const int32_t* startend, int n_vec, int causal, float scale, void* dq, void* dk,
+                        void* dv, void* workspace, size_t ws_bytes, float dropout_p, uint64_t seed,
+                        uint64_t offset, hipStream_t stream) {
+    return attn_bwd_impl(q, k, v, out, dout, softmax_lse, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal,
+                         scale, dq, dk, dv, workspace, ws_bytes, dropout_p, seed, offset, stream);
 }
 
 int fm_rope_qk(void* q, void* k, int dtype, int64_t N, int Hq, int Hk, int head_dim, const int32_t* cu_seqlens,

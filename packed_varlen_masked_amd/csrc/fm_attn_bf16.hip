@@ -309,8 +309,10 @@ __device__ __attribute__((always_inline)) inline float mask_max(f32x16 (&sacc)[2
 // it by more than 2^RESCALE_LOG2 (p then stays <= 2^8).  Returns the factor
 // alpha by which O and l must be rescaled (1 when the max did not move);
 // the new row sum is added to l after that rescale by the caller.
+template <bool DROP>
 __device__ __attribute__((always_inline)) inline float exp_tile(const f32x16 (&sacc)[2], float mx, State& st,
-                                                                bf16x8 (&pb)[2][2], float sl2, float& rsum) {
+                                                                bf16x8 (&pb)[2][2], float sl2, float& rsum,
+                                                                const DropW& dw, int drop_t, float drop_ks) {
     float alpha = 1.f;
     if (__any(mx > st.m_run + RESCALE_LOG2)) {
         const float m_new = fmaxf(st.m_run, mx);
@@ -327,7 +329,12 @@ __device__ __attribute__((always_inline)) inline float exp_tile(const f32x16 (&s
             for (int e = 0; e < 8; ++e) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][8 * c + e], sl2, -m_use));
                 rs[e & 3] += p;
-                pb[t][c][e] = (__bf16)p;
+                if constexpr (DROP) {   // the row sum keeps every p; O gets the kept ones, scaled
+                    const uint32_t byte = (dw.w[2 * t + c][e >> 2] >> (8 * (e & 3))) & 0xffu;
+                    pb[t][c][e] = (__bf16)(byte >= (uint32_t)drop_t ? p * drop_ks : 0.f);
+                } else {
+                    pb[t][c][e] = (__bf16)p;
+                }
             }
         }
     }
@@ -435,6 +442,7 @@ struct Slots {
 // needs them, the row max, the lazy max update, P in bf16 and its row sum.
 // Returns alpha, the factor by which O and l (relative to the old max) must
 // be rescaled; the caller applies it and adds the row sum to l.
+template <bool DROP>
 __device__ __attribute__((always_inline)) inline float softmax_tile(const AttnArgs& a, const Item& I, const Wave& Wv,
                                                                     f32x16 (&sacc)[2], int kb, bool iv,
                                                                     const int32_t* cmv, State& st, bf16x8 (&pb)[2][2],
@@ -442,7 +450,9 @@ __device__ __attribute__((always_inline)) inline float softmax_tile(const AttnAr
     const int c0 = I.s_b + kb * BC, c1 = min(c0 + BC, I.e_b);
     const bool causal = a.causal && (c1 > I.r0 + 1);
     const float mx = mask_max(sacc, causal, (c1 - c0) < BC, iv, c0, c1, Wv.qrow - Wv.n, cmv, a.scale_log2, Wv.lane);
-    return exp_tile(sacc, mx, st, pb, a.scale_log2, rsum);
+    DropW dw;
+    if constexpr (DROP) dw = drop_words(a.seed_lo, a.seed_hi, a.offset, Wv.qrow, kb, I.h, Wv.hh);
+    return exp_tile<DROP>(sacc, mx, st, pb, a.scale_log2, rsum, dw, a.drop_t, a.drop_ks);
 }
 
 // Step j of the KV loop, j = 0..T-1 (all waves in step).  Both groups
@@ -462,7 +472,7 @@ __device__ __attribute__((always_inline)) inline float softmax_tile(const AttnAr
 // MFMAs of S_j, so that the CU's load path takes them while the matrix unit
 // works.  A step ends by waiting for the previous step's copies, then a
 // barrier.
-template <int G>
+template <int G, bool DROP>
 __device__ __attribute__((always_inline)) inline void kv_step(
     const AttnArgs& a, const Item& I, Queue& Qu, const Wave& Wv, Slots& sl, int j, int T, bool& rec_pending,
     int fv, int& nrec, int n_items, const bf16x8 (&qf)[8], f32x16 (&sacc)[2], bf16x8 (&pb)[2][2],
@@ -484,7 +494,8 @@ __device__ __attribute__((always_inline)) inline void kv_step(
         });
         pv_part(vbuf(sl.u2), pb, st, Wv.lane);
         float rsum;
-        const float alpha = softmax_tile(a, I, Wv, sacc, Qu.k0, (Qu.iv & 1u) != 0, s_mv + (j & 3) * MVW, st, pb, rsum);
+        const float alpha =
+            softmax_tile<DROP>(a, I, Wv, sacc, Qu.k0, (Qu.iv & 1u) != 0, s_mv + (j & 3) * MVW, st, pb, rsum);
         if (alpha != 1.f) {   // rare: the running max moved
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
@@ -499,7 +510,7 @@ __device__ __attribute__((always_inline)) inline void kv_step(
         if (j > 0) {
             float rsum;
             const float alpha =
-                softmax_tile(a, I, Wv, sacc, Qu.kp, (Qu.iv & 16u) != 0, s_mv + ((j - 1) & 3) * MVW, st, pb, rsum);
+                softmax_tile<DROP>(a, I, Wv, sacc, Qu.kp, (Qu.iv & 16u) != 0, s_mv + ((j - 1) & 3) * MVW, st, pb, rsum);
             if (alpha != 1.f) {
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
@@ -640,7 +651,7 @@ __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a
 // extrema in global memory (FlashMask article §3.2 rules) and the next
 // item's record is prefetched during the loop; otherwise the list is ready
 // in s_vis at `vis_off` (fused path).
-template <bool STD>
+template <bool STD, bool DROP>
 __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a, Wave& Wv, const Item& I,
                                                                int vis_off, bool& rec_pending, int fv, int& nrec,
                                                                int n_items) {
@@ -762,15 +773,15 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
         Qu.kp = Qu.k0;
         if (Wv.g == 0)
             for (int j = 0; j < T; ++j)
-                kv_step<0>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
+                kv_step<0, DROP>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
         else
             for (int j = 0; j < T; ++j)
-                kv_step<1>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
+                kv_step<1, DROP>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
         // the last tile (V_{T-1} sits in slot u2 now): group 1 still owes its
         // softmax; then O += V_{T-1} P_{T-1}
         if (Wv.g == 1) {
             float rsum;
-            const float alpha = softmax_tile(a, I, Wv, sacc, Qu.kp, (Qu.iv & 16u) != 0, s_mv + ((T - 1) & 3) * MVW,
+            const float alpha = softmax_tile<DROP>(a, I, Wv, sacc, Qu.kp, (Qu.iv & 16u) != 0, s_mv + ((T - 1) & 3) * MVW,
                                              st, pb, rsum);
             if (alpha != 1.f) {
 #pragma unroll
@@ -795,6 +806,7 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
 // workgroup that started an item fetches until it gets an index past the
 // list, so the fetches number exactly n_items and the one returning
 // n_items - 1 resets the counter for the next call.
+template <bool DROP>
 __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
     static_assert(NTH / 64 == NW && BR == 32 * NW && GW == 4, "one wave per 32 query rows, one per SIMD per group");
     __shared__ __attribute__((aligned(16))) int32_t s_rec[ITEM_WORDS];
@@ -816,7 +828,7 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
         if (tid == 0) fv = atomicAdd(a.sched_counter, 1);
         const Item I = item_of(a, s_rec);
         bool rec_pending = (w == 0);
-        run_item<true>(a, Wv, I, 0, rec_pending, fv, nrec, n_items);
+        run_item<true, DROP>(a, Wv, I, 0, rec_pending, fv, nrec, n_items);
         int nxt = G + __builtin_amdgcn_readfirstlane(fv);
         if (rec_pending) {
             if (nxt < n_items && lane < ITEM_WORDS) nrec = a.items[(int64_t)nxt * ITEM_WORDS + lane];
@@ -854,7 +866,7 @@ __global__ __launch_bounds__(NTH, 2) void fm_fused_bf16_kernel(AttnArgs a) {
     for (int k = 0; k < P.n_my; ++k) {
         const Item I = item_of(a, s_myrec[k]);
         const int vis_off = __builtin_amdgcn_readfirstlane(s_myrec[k][12]);
-        run_item<false>(a, Wv, I, vis_off, rec_pending, 0, nrec, P.n_items);
+        run_item<false, false>(a, Wv, I, vis_off, rec_pending, 0, nrec, P.n_items);
         item_barrier();   // the ring is free for the next item
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -947,9 +959,10 @@ int fused_grid(int n_cu) {
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int n_cu, hipStream_t s) {
-    static const int occ = occupancy((const void*)fm_attn_bf16_kernel);
+    static const int occ = occupancy((const void*)fm_attn_bf16_kernel<false>);
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.items_cap, (int64_t)n_cu * occ));
-    hipLaunchKernelGGL(fm_attn_bf16_kernel, dim3((unsigned)grid), dim3(NTH), 0, s, a);
+    if (a.drop_t > 0) hipLaunchKernelGGL(fm_attn_bf16_kernel<true>, dim3((unsigned)grid), dim3(NTH), 0, s, a);
+    else hipLaunchKernelGGL(fm_attn_bf16_kernel<false>, dim3((unsigned)grid), dim3(NTH), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : launch_merge(a, n_cu, s);
 }

@@ -333,6 +333,12 @@ __device__ __attribute__((always_inline)) inline void store_row_bf16(uint16_t* o
         }
 }
 
+// Dropout bytes of a wave's 32 rows x 32 keys (dK/dV): lane L writes the
+// four words of (row L & 31, 16-key block L >> 5), u32 index
+// ((row * 2 + block) * 4 + word).
+__shared__ __attribute__((aligned(16))) uint32_t s_drop[8][256];
+
+template <bool DROP>
 __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
     const int h = blockIdx.y;
     const Span sp = span_of<2>(a, blockIdx.x);
@@ -445,7 +451,14 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
             sc = mfma(as_bf16x8(*(const u32x4*)(s_q + o)), as_bf16x8(*(const u32x4*)(kb_l + 32 * s)), sc);
             dp = mfma(as_bf16x8(*(const u32x4*)(s_g + o)), as_bf16x8(*(const u32x4*)(vb_l + 32 * s)), dp);
         }
+        if constexpr (DROP) {   // this wave's dropout bytes for the tile
+            uint32_t w0 = (uint32_t)(r0 + 32 * g + (lane & 31));
+            uint32_t w1 = (uint32_t)(((c0 - sp.s_b) >> 4) + 2 * t + (lane >> 5)), w2 = (uint32_t)h, w3 = a.offset;
+            philox4x32_10(w0, w1, w2, w3, a.seed_lo, a.seed_hi);
+            *(u32x4*)&s_drop[w][((lane & 31) * 2 + (lane >> 5)) * 4] = u32x4{w0, w1, w2, w3};
+        }
         // P = exp2(S scale log2e - lse2), masked pairs 0; dS = P (dP - Delta);
+        // with dropout Z = keep * 256 / (256 - t): P Z for dV, dS = P (dP Z - Delta);
         // then dV^T += dO^T P and dK^T += Q^T dS for the 16-row group
         // 2g + c2.  Written per half so that the second half's vector work
         // can issue while the first half's products run.
@@ -468,8 +481,16 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
                                        (mv.uts <= row && row < mv.ute);
                         p = m ? 0.f : p;
                     }
-                    const float ds = p * (dp[e] - dv4[c]);
-                    pb[e & 7] = (__bf16)p;
+                    float pz = p, dpz = dp[e];
+                    if constexpr (DROP) {
+                        const int rw = 8 * j + 4 * hh + c;   // row within the wave's 32
+                        const uint32_t word = s_drop[w][(rw * 2 + (n >> 4)) * 4 + ((n & 15) >> 2)];
+                        const bool keep = ((word >> (8 * (n & 3))) & 0xffu) >= (uint32_t)a.drop_t;
+                        pz = keep ? p * a.drop_ks : 0.f;
+                        dpz = keep ? dpz * a.drop_ks : 0.f;
+                    }
+                    const float ds = p * (dpz - dv4[c]);
+                    pb[e & 7] = (__bf16)pz;
                     db[e & 7] = (__bf16)ds;
                 }
             }
@@ -556,6 +577,7 @@ __device__ inline void store_kstage(const KStage& st, int tid) {
     }
 }
 
+template <bool DROP>
 __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
     const int h = blockIdx.y;
     const Span sp = span_of<QBLK>(a, blockIdx.x);
@@ -676,12 +698,19 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
                 }
         }
         bf16x8 db[2][2];
+        DropW dw;
+        if constexpr (DROP) dw = drop_words(a.seed_lo, a.seed_hi, a.offset, qr, kb, h, hh);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][e], sl2, -l2));
-                db[t][e >> 3][e & 7] = (__bf16)(p * (dp[t][e] - dl));
+                float dpz = dp[t][e];
+                if constexpr (DROP) {   // register e of tile t: block 2t + (e >> 3), word 2((e >> 2) & 1) + hh
+                    const uint32_t byte = (dw.w[2 * t + (e >> 3)][(e >> 2) & 1] >> (8 * (e & 3))) & 0xffu;
+                    dpz = byte >= (uint32_t)a.drop_t ? dpz * a.drop_ks : 0.f;
+                }
+                db[t][e >> 3][e & 7] = (__bf16)(p * (dpz - dl));
             }
         // dQ^T += K^T dS^T: 16-key groups kg of the block
 #pragma unroll
@@ -730,10 +759,12 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s) {
     }
     if (kb_cap <= 0 || a.N == 0) return hipSuccess;
     const dim3 grid((unsigned)kb_cap, (unsigned)a.H, (unsigned)a.nc);
-    hipLaunchKernelGGL(bwd::fm_bwd_dkdv_kernel, grid, dim3(bwd::NTK), 0, s, a);
+    if (a.drop_t > 0) hipLaunchKernelGGL(bwd::fm_bwd_dkdv_kernel<true>, grid, dim3(bwd::NTK), 0, s, a);
+    else hipLaunchKernelGGL(bwd::fm_bwd_dkdv_kernel<false>, grid, dim3(bwd::NTK), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd::fm_bwd_dq_kernel, grid, dim3(bwd::NTQ), 0, s, a);
+    if (a.drop_t > 0) hipLaunchKernelGGL(bwd::fm_bwd_dq_kernel<true>, grid, dim3(bwd::NTQ), 0, s, a);
+    else hipLaunchKernelGGL(bwd::fm_bwd_dq_kernel<false>, grid, dim3(bwd::NTQ), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess || a.nc <= 1) return e;
     const dim3 rgrid((unsigned)kb_cap, (unsigned)a.H, (unsigned)bwd::RZ);
     hipLaunchKernelGGL(bwd::fm_bwd_dkdv_reduce_kernel, rgrid, dim3(bwd::NTK), 0, s, a);

@@ -63,6 +63,57 @@ __host__ __device__ inline TileInfo classify_tile(int r0, int r1, int c0, int c1
     return t;
 }
 
+// ---- dropout bits -------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64 products and
+// xors with the key, the key advancing by the Weyl constants between
+// rounds.  The dropout byte of a pair (query row i, key j of a sequence
+// starting at s) for head h is byte (j - s) & 15 of the four words for
+// counter (i, (j - s) >> 4, h, offset) and key (seed lo, seed hi).
+__device__ __attribute__((always_inline)) inline void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                                                    uint32_t& c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    }
+}
+
+// Dropout words of a 64-key block kb of a sequence for the query row of a
+// lane whose S^T registers hold one query (the forward, dQ): w[b][x] is
+// word 2x + hh of 16-key block 4kb + b, the words whose bytes are this
+// lane's keys (register 8c + e of S^T tile t is key 32t + 16c + 8(e>>2) +
+// 4hh + (e&3): block 2t + c, byte 8(e>>2) + 4hh + (e&3)).  Lane half hh
+// computes blocks 2hh, 2hh + 1 and the two halves swap the words the other
+// one needs.
+struct DropW { uint32_t w[4][2]; };
+__device__ __attribute__((always_inline)) inline DropW drop_words(uint32_t seed_lo, uint32_t seed_hi, uint32_t offset,
+                                                                  int row, int kb, int h, int hh) {
+    uint32_t own[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        uint32_t c0 = (uint32_t)row, c1 = (uint32_t)(4 * kb + 2 * hh + u), c2 = (uint32_t)h, c3 = offset;
+        philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
+        own[u][0] = c0; own[u][1] = c1; own[u][2] = c2; own[u][3] = c3;
+    }
+    DropW d;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const uint32_t mine = hh ? own[u][2 * x + 1] : own[u][2 * x];
+            const uint32_t send = hh ? own[u][2 * x] : own[u][2 * x + 1];
+            const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+            const uint32_t recv = hh ? r[0] : r[1];
+            d.w[u][x] = hh ? recv : mine;
+            d.w[2 + u][x] = hh ? mine : recv;
+        }
+    return d;
+}
+
 // ---- wave helpers (wave64) --------------------------------------------
 // min / max over the 64 lanes with DPP (no LDS traffic): quad swaps, the
 // half-row and row mirrors leave every lane of a row with its row's value;

@@ -82,6 +82,9 @@ struct AttnArgs {
     // fused path only: where the in-kernel planner writes the plan
     int32_t* w_hdr; int32_t* w_kb_off; int32_t* w_ext; int32_t* w_items; int64_t* w_counts;
     int32_t* w_merge;          // split-row list (S > 0), else null
+    // attention dropout (planned path): a pair is dropped when its byte is
+    // below drop_t (0 = no dropout); kept values are scaled by drop_ks
+    int drop_t; float drop_ks; uint32_t seed_lo, seed_hi, offset;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int n_cu, hipStream_t s);
@@ -107,6 +110,7 @@ struct BwdArgs {
     float* part_kv; int32_t* flag_kv;   // [slot_kv][nc] partials (128 KB each) and their flags
     float* part_q; int32_t* flag_q;     // [slot_q][nc]
     uint32_t call_id;                   // flag value of this call (never 0)
+    int drop_t; float drop_ks; uint32_t seed_lo, seed_hi, offset;   // dropout, as in AttnArgs
 };
 
 // Rotary embedding of q and k rows in place (bf16 or fp32).
