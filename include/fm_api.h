@@ -132,7 +132,9 @@ int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim);
  *   items:      int32 [item_cap][16] work items (see fm_build_worklist)
  *   tile_class: uint8 [map_cap]     per-tile classes (only if requested)
  *   scratch:    worklist scratch (fm_worklist_scratch_size bytes)
- *   partial:    fp32 split partials [slot_cap * H] x (Br*D + 2*Br) (S > 0)
+ *   partial:    split partials (S > 0), per (slot, head) Br*D fp16 values of
+ *               the split's O / l scaled by 2^-e (e per row), then Br each of
+ *               fp32 m, fp32 l and int32 e: Br*D*2 + 3*Br*4 bytes
  *   merge:      int32 [slot_cap * H / 2 + 1][8] (S > 0): the split rows,
  *               one entry per (split row, head): slot of split 0, head,
  *               first row, end row, number of splits, 3 zero words;
@@ -260,7 +262,7 @@ int fm_build_plan(const int32_t* cu_seqlens, int B, int64_t N, int H, int head_d
  * (see fm_fused_path) take the fused path: ONE attention launch in which
  * every workgroup rebuilds the plan in LDS and runs its share of the
  * items; the plan is still written to the workspace, identical to
- * fm_build_plan's.  Split rows (S > 0) write fp32 partials that a second
+ * fm_build_plan's.  Split rows (S > 0) write partials that a second
  * launch combines in split order.  Results are deterministic: the same
  * inputs give the same bits, on either path.
  */

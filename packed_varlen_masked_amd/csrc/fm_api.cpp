@@ -165,7 +165,8 @@ int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_
     L.off_items = off; off = align256(off + (size_t)c.item * fm::ITEM_WORDS * 4);
     L.off_tile_class = want_map ? off : 0; if (want_map) off = align256(off + (size_t)c.map);
     L.off_scratch = off; L.scratch_bytes = sl.bytes; off = align256(off + sl.bytes);
-    L.partial_bytes = S > 0 ? (size_t)c.slot * H * ((size_t)Br * D + 2 * (size_t)Br) * 4 : 0;
+    // per (slot, head): Br x D fp16 values of O / l, then m, l and the scale exponent per row
+    L.partial_bytes = S > 0 ? (size_t)c.slot * H * ((size_t)Br * D * 2 + 3 * (size_t)Br * 4) : 0;
     L.off_partial = S > 0 ? off : 0; off = align256(off + L.partial_bytes);
     // split-row list: a split row has >= 2 slots, so slot_cap * H / 2 + 1 entries suffice
     L.off_merge = S > 0 ? off : 0;

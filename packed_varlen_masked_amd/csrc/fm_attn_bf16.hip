@@ -62,7 +62,7 @@ constexpr int BR = 256, BC = 64, HD = 128;
 constexpr int NW = 8, NTH = 64 * NW;    // 8 waves, 32 query rows each
 constexpr int GW = NW / 2;              // waves per ping-pong group
 constexpr float LN2 = 0.69314718055994530942f;
-constexpr int PART = BR * HD + 2 * BR;  // floats per split partial: O row-major, then m, l
+constexpr int PART = BR * HD / 2 + 3 * BR;  // 4-byte words per split partial: O as fp16, then m, l, e per row
 // Lazy rescale: the running row max used for the exponentials moves only when
 // a new score exceeds it by more than 2^RESCALE_LOG2 (p then stays <= 2^8,
 // exact in the final normalisation, and O is rescaled rarely).
@@ -613,36 +613,63 @@ __device__ __attribute__((always_inline)) inline void write_lse(const AttnArgs& 
     if (Wv.hh == 0) a.lse[(int64_t)I.h * a.N + Wv.qrow] = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
 }
 
-// Split rows: every split writes its fp32 partial (O unnormalised, then m
-// and l per row); fm_merge_bf16_kernel combines them in split order after
-// the attention launch.  Partial of split s, head h at
-// ((slot0 + s) * H + h) * PART floats; its O part is lane-major: value e of
-// channel group (dt, g) of lane L of wave w at ((16 w + 4 dt + g) * 64 + L)
-// * 4 + e, so every store instruction of a wave writes 1 KB contiguously.
-__device__ __attribute__((always_inline)) inline int part_index(int w, int dt, int g, int lane) {
-    return ((16 * w + 4 * dt + g) * 64 + lane) * 4;
+// Split rows: every split writes its partial, combined by
+// fm_merge_bf16_kernel in split order after the attention launch.  Per row:
+// O / l of the split as fp16, scaled by 2^-e with e chosen per row so that
+// the row's largest magnitude lies below 2^15 (no overflow, 11 significant
+// bits however large or small V is), then m, l and e as 4-byte words.
+// Partial of split s, head h at ((slot0 + s) * H + h) * PART words; its O
+// part is lane-major: the 8 values of channel groups (dt, 2gp) and
+// (dt, 2gp + 1) of lane L of wave w are 16 bytes at word
+// ((8 w + 2 dt + gp) * 64 + L) * 4, so every store instruction of a wave
+// writes 1 KB contiguously.
+__device__ __attribute__((always_inline)) inline int part_index(int w, int dt, int gp, int lane) {
+    return ((8 * w + 2 * dt + gp) * 64 + lane) * 4;
+}
+__device__ inline uint32_t f16_pair(float x, float y) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y) << 16);
 }
 
 __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a, const Wave& Wv, const Item& I,
                                                                const State& st) {
+    const float l = st.l_run, inv = l > 0.f ? 1.f / l : 0.f;
     if (I.nsp <= 1) {
         // every wave is past its last ring read and its copies are drained:
         // the ring is free for the output staging
         phase_barrier();
-        const float l = st.l_run, inv = l > 0.f ? 1.f / l : 0.f;
         write_rows(a, Wv, I, st, inv);
         if (Wv.qrow < I.r1) write_lse(a, Wv, I, st.m_run, l);
         return;
     }
-    float* po = a.partial + ((int64_t)(I.slot0 + I.sidx) * a.H + I.h) * PART;
+    float mx = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-            *(float4*)(po + part_index(Wv.w, dt, g, Wv.lane)) =
-                float4{st.o[dt][4 * g], st.o[dt][4 * g + 1], st.o[dt][4 * g + 2], st.o[dt][4 * g + 3]};
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(st.o[dt][j]));
+    mx = halves_max(mx * inv);   // both lanes of the row take the same scale
+    // mx < 2^(u + 1) with u its binary exponent: e = u - 14 puts it below 2^15
+    const int u = (int)((__float_as_uint(mx) >> 23) & 0xff) - 127;
+    const int e = mx > 0.f ? min(max(u - 14, -100), 113) : 0;
+    const float sc = __uint_as_float((uint32_t)(127 - e) << 23) * inv;   // 2^-e / l
+    uint32_t* po = (uint32_t*)a.partial + ((int64_t)(I.slot0 + I.sidx) * a.H + I.h) * PART;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            const int j = 8 * gp;
+            *(u32x4*)(po + part_index(Wv.w, dt, gp, Wv.lane)) =
+                u32x4{f16_pair(st.o[dt][j] * sc, st.o[dt][j + 1] * sc),
+                      f16_pair(st.o[dt][j + 2] * sc, st.o[dt][j + 3] * sc),
+                      f16_pair(st.o[dt][j + 4] * sc, st.o[dt][j + 5] * sc),
+                      f16_pair(st.o[dt][j + 6] * sc, st.o[dt][j + 7] * sc)};
+        }
     const int lr = 32 * Wv.w + Wv.n;
-    if (Wv.hh == 0) { po[BR * HD + lr] = st.m_run; po[BR * HD + BR + lr] = st.l_run; }
+    if (Wv.hh == 0) {
+        po[BR * HD / 2 + lr] = __float_as_uint(st.m_run);
+        po[BR * HD / 2 + BR + lr] = __float_as_uint(l);
+        po[BR * HD / 2 + 2 * BR + lr] = (uint32_t)e;
+    }
 }
 
 // ---- one work item ----------------------------------------------------
@@ -874,13 +901,14 @@ __global__ __launch_bounds__(NTH, 2) void fm_fused_bf16_kernel(AttnArgs a) {
 
 // ---- merge of split rows ----------------------------------------------
 // Combines the partials of every split row in split order (deterministic,
-// one pass with the running max): with m = max so far,
+// one pass with the running max): with m = max so far and O_s = the stored
+// fp16 row times l_s 2^e_s,
 //   m' = max(m, m_s),  l = l 2^(m - m') + l_s 2^(m_s - m'),
 //   O = O 2^(m - m') + O_s 2^(m_s - m'),
 // then out = O / l and lse = (m + log2 l) ln 2.  Work comes from the list of
 // split rows the planner wrote (one entry per split row and head).  Task =
-// (entry, wave slot w of the partial layout, channel group g); thread =
-// (lane of that wave, dt): every read instruction of a wave is 1 KB
+// (entry, wave slot w of the partial layout, channel group pair gp); thread
+// = (lane of that wave, dt): every read instruction of a wave is 1 KB
 // contiguous, and a thread issues the reads of up to MSPL splits before
 // using any of them.
 constexpr int MNTH = 256, MSPL = 16;
@@ -888,30 +916,34 @@ constexpr int MNTH = 256, MSPL = 16;
 __global__ __launch_bounds__(MNTH) void fm_merge_bf16_kernel(AttnArgs a) {
     const int n_merge = *a.n_merge;
     const int lane = threadIdx.x & 63, dt = threadIdx.x >> 6, n = lane & 31, hh = lane >> 5;
-    const int64_t n_tasks = (int64_t)min((int64_t)n_merge, a.merge_cap) * NW * 4;
+    const int64_t n_tasks = (int64_t)min((int64_t)n_merge, a.merge_cap) * NW * 2;
     for (int64_t task = blockIdx.x; task < n_tasks; task += gridDim.x) {
-        const int64_t k = task / (NW * 4);
-        const int w = (int)((task / 4) % NW), g = (int)(task % 4);
+        const int64_t k = task / (NW * 2);
+        const int w = (int)((task / 2) % NW), gp = (int)(task % 2);
         const int4 e0 = *(const int4*)(a.merge_list + k * MERGE_WORDS);
         const int nsp = a.merge_list[k * MERGE_WORDS + 4];
         const int slot0 = e0.x, h = e0.y, lr = 32 * w + n;
         const int64_t qrow = (int64_t)e0.z + lr;
         if (qrow >= e0.w) continue;
-        const float* p0 = a.partial + ((int64_t)slot0 * a.H + h) * PART;
+        const uint32_t* p0 = (const uint32_t*)a.partial + ((int64_t)slot0 * a.H + h) * PART;
         const int64_t step = (int64_t)a.H * PART;
-        const int oi = part_index(w, dt, g, lane);
+        const int oi = part_index(w, dt, gp, lane);
         float m = -INFINITY, l = 0.f;
-        float4 acc = {0.f, 0.f, 0.f, 0.f};
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.f;
         for (int s0 = 0; s0 < nsp; s0 += MSPL) {
             float mv[MSPL], lv[MSPL];
-            float4 ov[MSPL];
+            int ev[MSPL];
+            u32x4 ov[MSPL];
 #pragma unroll
             for (int u = 0; u < MSPL; ++u)
                 if (s0 + u < nsp) {
-                    const float* ps = p0 + (s0 + u) * step;
-                    mv[u] = ps[BR * HD + lr];
-                    lv[u] = ps[BR * HD + BR + lr];
-                    ov[u] = *(const float4*)(ps + oi);
+                    const uint32_t* ps = p0 + (s0 + u) * step;
+                    mv[u] = __uint_as_float(ps[BR * HD / 2 + lr]);
+                    lv[u] = __uint_as_float(ps[BR * HD / 2 + BR + lr]);
+                    ev[u] = (int)ps[BR * HD / 2 + 2 * BR + lr];
+                    ov[u] = *(const u32x4*)(ps + oi);
                 }
 #pragma unroll
             for (int u = 0; u < MSPL; ++u)
@@ -920,20 +952,28 @@ __global__ __launch_bounds__(MNTH) void fm_merge_bf16_kernel(AttnArgs a) {
                     const float mu = mn == -INFINITY ? 0.f : mn;
                     const float ca = __builtin_amdgcn_exp2f(m - mu), cb = __builtin_amdgcn_exp2f(mv[u] - mu);
                     l = __builtin_fmaf(l, ca, lv[u] * cb);
-                    acc.x = __builtin_fmaf(acc.x, ca, ov[u].x * cb);
-                    acc.y = __builtin_fmaf(acc.y, ca, ov[u].y * cb);
-                    acc.z = __builtin_fmaf(acc.z, ca, ov[u].z * cb);
-                    acc.w = __builtin_fmaf(acc.w, ca, ov[u].w * cb);
+                    const float f = __builtin_amdgcn_ldexpf(lv[u] * cb, ev[u]);
+                    const uint32_t wd[4] = {ov[u].x, ov[u].y, ov[u].z, ov[u].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd[j] & 0xffff));
+                        const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd[j] >> 16));
+                        acc[2 * j] = __builtin_fmaf(acc[2 * j], ca, lo * f);
+                        acc[2 * j + 1] = __builtin_fmaf(acc[2 * j + 1], ca, hi * f);
+                    }
                     m = mn;
                 }
         }
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* op = (uint16_t*)a.out + qrow * ((int64_t)a.H * HD) + (int64_t)h * HD + 32 * dt + 8 * g + 4 * hh;
-        u32x2 wv;
-        wv.x = bf16_bits(acc.x * inv) | (bf16_bits(acc.y * inv) << 16);
-        wv.y = bf16_bits(acc.z * inv) | (bf16_bits(acc.w * inv) << 16);
-        *(u32x2*)op = wv;
-        if (dt == 0 && g == 0 && hh == 0)
+        uint16_t* op = (uint16_t*)a.out + qrow * ((int64_t)a.H * HD) + (int64_t)h * HD + 32 * dt + 16 * gp + 4 * hh;
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+            u32x2 wv;
+            wv.x = bf16_bits(acc[4 * g2] * inv) | (bf16_bits(acc[4 * g2 + 1] * inv) << 16);
+            wv.y = bf16_bits(acc[4 * g2 + 2] * inv) | (bf16_bits(acc[4 * g2 + 3] * inv) << 16);
+            *(u32x2*)(op + 8 * g2) = wv;
+        }
+        if (dt == 0 && gp == 0 && hh == 0)
             a.lse[(int64_t)h * a.N + qrow] = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
     }
 }
@@ -947,7 +987,7 @@ int occupancy(const void* fn) {
 
 hipError_t launch_merge(const AttnArgs& a, int n_cu, hipStream_t s) {
     if (a.S <= 0) return hipSuccess;
-    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.merge_cap * NW * 4, (int64_t)n_cu * 8));
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.merge_cap * NW * 2, (int64_t)n_cu * 8));
     hipLaunchKernelGGL(fm_merge_bf16_kernel, dim3((unsigned)grid), dim3(MNTH), 0, s, a);
     return hipGetLastError();
 }

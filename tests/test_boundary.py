@@ -61,7 +61,7 @@ def test_layout_bounds(pv):
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.bytes >= lay.off_scratch + lay.scratch_bytes
     lay2 = pv.workspace_layout(4352, 3, 2, 128, 128, 64, 4, False)
-    assert lay2.partial_bytes >= lay2.slot_cap * 2 * (128 * 128 + 256) * 4
+    assert lay2.partial_bytes >= lay2.slot_cap * 2 * (128 * 128 * 2 + 3 * 128 * 4)
     for bad in [dict(N=-1), dict(B=0), dict(H=0), dict(bq=0), dict(S=-2)]:
         a = dict(N=100, B=1, H=1, bq=16, bk=16, S=0)
         a.update(bad)
