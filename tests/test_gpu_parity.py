@@ -341,3 +341,27 @@ def test_extrema_large(pv, n_vec, causal, aligned):
     assert status == 0
     assert np.array_equal(kb_off.cpu().numpy(), okb)
     assert np.array_equal(ext.cpu().numpy().reshape(-1, 8), oext.reshape(-1, 8))
+
+
+@pytest.mark.parametrize("vexp", [-40, 0, 24, 100])
+@pytest.mark.parametrize("S", [2, -1])
+def test_split_partials_any_scale(pv, vexp, S):
+    """Split rows keep their partials as fp16 with a power-of-two scale per
+    row: V multiplied by 2^vexp (exact in bf16) must give out multiplied by
+    2^vexp, within the out bar relative to that scale, on rows split into
+    many chunks; lse does not depend on V.  Without the per-row scale, 2^24
+    and 2^100 would overflow fp16 and 2^-40 would vanish."""
+    w = W.document_workload([1500, 300, 700], H=2, seed=21)
+    sc = 2.0 ** vexp
+    oo, ol = O.attention(w.q, w.k, w.v, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale)
+    q, k, v, cu, sv = dev_inputs(w)
+    out, lse = pv.attn_fwd(q, k, (v.float() * sc).to(torch.bfloat16), cu, sv, w.n_vec, w.causal, float(w.scale),
+                           max_kb_per_item=S)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64) / sc
+    l = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ol)
+    e_out = float(np.max(np.abs(o - oo)))
+    e_lse = float(np.max(np.abs(l[fin] - ol[fin]), initial=0.0))
+    say("  V x 2^%d, S=%d: max|dout|/2^%d=%.3e max|dlse|=%.3e" % (vexp, S, vexp, e_out, e_lse))
+    assert np.all(np.isfinite(o)) and e_out <= OUT_TOL and e_lse <= LSE_TOL
