@@ -326,9 +326,18 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
     // (n_valid * H <= gridDim.x - 1), the longest-first order cannot change
     // the schedule (every item starts at once), so a workgroup takes the
     // (g / H)-th filled slot in slot order, head g % H, and skips the sort.
-    // The writer still sorts and writes the plan. ----
+    // g is the item index with the 8 XCDs in mind: workgroups are dealt to
+    // the XCDs in turn, so workgroup id runs item (id % 8) * c + id / 8,
+    // c = ceil(items / 8): each XCD gets a run of c consecutive items (the
+    // splits of a few q tiles, both heads), whose Q tiles and key ranges
+    // then come from that XCD's own L2, and all 8 XCDs stay busy.  Every
+    // item has one workgroup (id = 8 (g / c) ... < 8 c), and the writer,
+    // G - 1, gets none while 8 c <= G - 1; otherwise workgroup id runs
+    // item id.  The writer still sorts and writes the plan. ----
     if (!writer && (long long)n_valid * H <= (long long)gridDim.x - 1) {
-        const int k = (int)blockIdx.x / H, h = (int)blockIdx.x - k * H;
+        const int id = (int)blockIdx.x, n_it = n_valid * H, c = ceil_div(n_it, 8);
+        const int g = 8 * c > (int)gridDim.x - 1 ? id : (id >> 3) < c ? (id & 7) * c + (id >> 3) : n_it;
+        const int k = g / H, h = g - k * H;
         if (k >= n_valid) return LdsPlan{0, n_valid * H, 0};
         if (wid == 0) {
             int base = 0, slot = -1;
