@@ -340,6 +340,12 @@ size_t fm_bwd_workspace_size(int64_t N, int B, int H, int head_dim, int dtype);
  * chunks (separate workgroups, fp32 partials) and two more launches sum
  * them in chunk order.  The chunking depends on the sizes only: the same
  * inputs give the same bits on every run and device.
+ * Streams: after Delta, the dQ launches run on a second stream the library
+ * creates once per device (default priority), forked from `stream` and
+ * joined back into it with events, so that they can overlap the dK/dV
+ * launches; everything the call enqueues is ordered before whatever is
+ * enqueued on `stream` afterwards, as with a single stream (and a graph
+ * captured from `stream` takes the fork and join with it).
  */
 int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                 const float* softmax_lse, int dtype, int64_t N, int H, int D,
