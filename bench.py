@@ -74,16 +74,19 @@ def parse():
     return ap.parse_args()
 
 
+FWD_SOURCES = ("fm_api.cpp", "fm_attn_bf16.hip", "fm_common.hpp", "fm_internal.h", "fm_lds_plan.h", "fm_plan.hip")
+
+
 def source_hash():
-    """sha256 over the library sources: stored counter figures apply only to
-    the kernels they were taken from."""
+    """sha256 over the sources of the forward bf16 path (the planning and
+    attention kernels and the host code that launches them): stored counter
+    figures apply only to the kernels they were taken from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "packed_varlen_masked_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".cpp", ".h", ".hpp")):
-            h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    for name in FWD_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
