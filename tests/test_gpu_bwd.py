@@ -196,3 +196,32 @@ def test_bwd_bad_cu_and_empty(pv):
                              torch.empty(1, 0, dtype=torch.int32, device="cuda"), 1, True)
     torch.cuda.synchronize()
     assert dq.shape == (0, 2, 128)
+
+
+def test_bwd_stream_order(pv):
+    """The dQ launches run on a second stream of the library's, forked from
+    and joined back into the caller's stream: work enqueued afterwards on a
+    (non-default) caller stream must see the finished gradients.  Two
+    streams each run the backward and copy dq, dk, dv right after it with no
+    host synchronisation; every copy must equal a fully synchronised run,
+    bit for bit, three times over."""
+    w = W.document_workload([300, 700, 1200], H=2, seed=6)
+    ref, _ = run_bwd(pv, w)
+    q, k, v = (bf16(x).cuda() for x in (w.q, w.k, w.v))
+    g = bf16(np.random.default_rng(77).standard_normal(w.q.shape, dtype=np.float32)).cuda()
+    cu = torch.from_numpy(w.cu_seqlens.astype(np.int32)).cuda()
+    sv = torch.from_numpy(np.ascontiguousarray(w.startend.astype(np.int32))).cuda()
+    out, lse = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    copies = []
+    for rep in range(3):
+        for st in streams:
+            with torch.cuda.stream(st):
+                grads = pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale))
+                copies.append([t.clone() for t in grads])
+    torch.cuda.synchronize()
+    say("stream order: %d copies" % len(copies))
+    for c in copies:
+        for x, y in zip(c, ref):
+            assert np.array_equal(x.float().cpu().numpy(), y)
