@@ -13,9 +13,7 @@ Each function cites the passage of the pages it follows:
         the fused QK RoPE
 
 Pinning status (what fixes each function other than itself) is listed in
-the docstring of each function; every function here is pinned, except
-that philox4x32_10 is pinned by statistics only: its identity with the
-published generator's stream is parity unpinned.
+the docstring of each function; every function here is pinned.
 """
 from .flashmask import (  # noqa: F401
     FULL, PARTIAL, UNMASKED,

@@ -492,10 +492,11 @@ def philox4x32_10(ctr, key):
     rounds.  ctr: uint array [..., 4], key: uint array [..., 2] (broadcast);
     returns uint32 [..., 4].  Arithmetic in uint64 (exact products).
 
-    Pinned by statistics only (uniform bytes, avalanche on one counter bit,
-    unrelated streams for different keys, determinism).  That the stream
-    is bit for bit the published generator's is parity unpinned: no
-    known-answer vectors of the paper are stored here."""
+    Pinned by an independent implementation, ROCm's rocRAND Philox4x32-10
+    engine (compiled for the CPU in the test; blocks and subsequences as
+    the counter's two 64-bit halves, carries included), and by statistics
+    (uniform bytes, avalanche on one counter bit, unrelated streams for
+    different keys, determinism)."""
     c = [np.asarray(ctr[..., i], np.uint64) & np.uint64(0xFFFFFFFF) for i in range(4)]
     k0 = np.asarray(key[..., 0], np.uint64) & np.uint64(0xFFFFFFFF)
     k1 = np.asarray(key[..., 1], np.uint64) & np.uint64(0xFFFFFFFF)

@@ -674,3 +674,52 @@ def test_generators():
     q1 = W.make_config(2, H=1).q
     q2 = W.make_config(2, H=1).q
     assert np.array_equal(q1, q2)
+
+
+_ROCRAND_PROBE = r"""
+#include <cstdio>
+#include <cstdlib>
+#include <rocrand/rocrand_philox4x32_10.h>
+// words of rocRAND's Philox4x32-10 engine (host code): seed, subsequence,
+// first block, number of blocks; block m of subsequence s is the generator
+// at counter (m mod 2^32, m >> 32, s mod 2^32, s >> 32)
+int main(int argc, char** argv) {
+    const unsigned long long seed = strtoull(argv[1], nullptr, 0), sub = strtoull(argv[2], nullptr, 0);
+    const unsigned long long m = strtoull(argv[3], nullptr, 0);
+    const int n = atoi(argv[4]);
+    rocrand_device::philox4x32_10_engine e(seed, sub, 0);
+    if (m) e.discard(4 * m);
+    for (int i = 0; i < n; ++i) { const uint4 r = e.next4(); printf("%u %u %u %u\n", r.x, r.y, r.z, r.w); }
+    return 0;
+}
+"""
+
+
+def test_philox_against_rocrand(tmp_path):
+    """Philox4x32-10 bit for bit against an independent implementation, the
+    host-callable engine of ROCm's rocRAND library (its header, compiled here
+    for the CPU): key = the 64-bit seed's two halves, counter = (block,
+    subsequence) as two 64-bit halves, including the carry from word 0 into
+    word 1.  Skipped where hipcc or the header is absent."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    hdr = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
+    import os
+    if not (os.path.exists(hipcc) and os.path.exists(hdr)):
+        pytest.skip("hipcc or rocRAND header not available")
+    src = tmp_path / "probe.cpp"
+    src.write_text(_ROCRAND_PROBE)
+    exe = tmp_path / "probe"
+    subprocess.run([hipcc, "-O1", str(src), "-o", str(exe)], check=True, capture_output=True, timeout=300)
+    cases = [(0x0123456789ABCDEF, 0, 0, 64), (7, 0, 0xFFFFFFFE, 4), (2 ** 64 - 1, 5, 0, 8),
+             (0xDEADBEEF00000001, 2 ** 32 + 3, 2 ** 32 - 1, 3), (12345, 1, 2 ** 40 + 17, 2)]
+    for seed, sub, m0, n in cases:
+        out = subprocess.run([str(exe), str(seed), str(sub), str(m0), str(n)], check=True, capture_output=True,
+                             text=True, timeout=60).stdout.split()
+        got = np.array([int(x) for x in out], np.uint64).reshape(n, 4)
+        m = np.arange(m0, m0 + n, dtype=np.uint64)
+        ctr = np.stack([m & np.uint64(0xFFFFFFFF), m >> np.uint64(32),
+                        np.full(n, sub & 0xFFFFFFFF, np.uint64), np.full(n, sub >> 32, np.uint64)], axis=-1)
+        key = np.array([seed & 0xFFFFFFFF, seed >> 32], np.uint64)
+        assert np.array_equal(O.philox4x32_10(ctr, key).astype(np.uint64), got), (seed, sub, m0)
