@@ -136,6 +136,8 @@ __device__ LdsPlan plan_in_lds(const AttnArgs& a, char* tmp, uint16_t* vis, int3
     for (int i = tid; i <= B; i += blockDim.x) t_cu[i] = a.cu[i];
     int4 rv[U];
     int r1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { rv[u] = int4{0, 0, 0, 0}; r1[u] = 0; }
     if (sv_fits) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
