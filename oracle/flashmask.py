@@ -87,7 +87,8 @@ def _seq_bounds(cu, b):
 
 
 def attention(q, k, v, cu_seqlens, startend, n_vec: int, causal: bool,
-              scale, chunk: int = 512, heads: Optional[Sequence[int]] = None):
+              scale, chunk: int = 512, heads: Optional[Sequence[int]] = None,
+              rows: Optional[Tuple[int, int]] = None):
     """Masked softmax attention per sequence, float64.
 
     q, k, v: [N, H, D] (any float dtype; widened exactly to fp64).
@@ -100,6 +101,9 @@ def attention(q, k, v, cu_seqlens, startend, n_vec: int, causal: bool,
     sequence, not masked), lse_i = log sum exp s_ij and
     out_i = sum_j exp(s_ij - lse_i) v_j.  Computed per (sequence, head) in
     row chunks of at most `chunk` rows over that sequence's keys.
+
+    `heads` and `rows` (a global row range [lo, hi)) restrict which
+    (row, head) results are computed; the others stay out = 0, lse = -inf.
 
     Reading: a row with no allowed key (possible only for hand-made masks)
     gives out = 0 and lse = -inf (log of an empty sum).
@@ -115,16 +119,18 @@ def attention(q, k, v, cu_seqlens, startend, n_vec: int, causal: bool,
     out = np.zeros((N, H, D), np.float64)
     lse = np.full((H, N), -np.inf, np.float64)
     heads = range(H) if heads is None else heads
+    lo, hi = (0, N) if rows is None else (max(int(rows[0]), 0), min(int(rows[1]), N))
     for b in range(len(cu) - 1):
         s, e = _seq_bounds(cu, b)
-        if e <= s:
+        s_r, e_r = max(s, lo), min(e, hi)
+        if e_r <= s_r:
             continue
         cols = np.arange(s, e)
         for h in heads:
             kh = k[s:e, h, :]
             vh = v[s:e, h, :]
-            for r0 in range(s, e, chunk):
-                r1 = min(r0 + chunk, e)
+            for r0 in range(s_r, e_r, chunk):
+                r1 = min(r0 + chunk, e_r)
                 rows = np.arange(r0, r1)
                 sc = scale * (q[r0:r1, h, :] @ kh.T)
                 msk = element_mask(rows, cols, vecs, causal)

@@ -204,7 +204,63 @@ def test_prefix_window_pairs_closed_form():
     assert O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal) == expect
 
 
+@pytest.mark.parametrize("lens", [[5, 9, 20], [64, 1, 300, 17], [1000]])
+def test_bidirectional_document_pairs_closed_form(lens):
+    """Non-causal, two stored vectors: the FlashMask article §2.2 defaults
+    fill the absent ones (LTE = query length, UTS = 0), so a key of document
+    [s, e) stored as LTS = e, UTE = s hides exactly the rows outside its own
+    document.  Under one sequence covering every token (cu = [0, N], the
+    ZeroPadding packing of §6.7), each row then sees its whole document and
+    nothing else: sum_b L_b^2 pairs per head.  Any other reading of the two
+    vectors (for instance LTS and LTE) gives a different count."""
+    N = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    starts = np.repeat(cu[:-1], lens)
+    ends = np.repeat(cu[1:], lens)
+    sv = np.stack([ends, starts]).astype(np.int32)
+    expect = sum(L * L for L in lens)
+    assert O.unmasked_pairs(np.array([0, N], np.int32), sv, 2, False) == expect
+    assert O.unmasked_pairs(cu, sv, 2, False) == expect
+    # the same documents with the two stored rows swapped hide far more
+    assert O.unmasked_pairs(np.array([0, N], np.int32), sv[::-1].copy(), 2, False) != expect or len(lens) == 1
+
+
 # -------------------------------------------------------------- brute force
+@pytest.mark.parametrize("seed", range(8))
+def test_extreme_endpoints_brute_force(seed):
+    """Endpoints anywhere in the int32 range (FlashMask article §2.1: a
+    half-open row interval per column; start >= end is empty): INT32_MIN,
+    -1, 0, N, N + 7 and INT32_MAX mixed with ordinary rows.  The oracle's
+    attention, extrema and tile classes against pure-Python element truth
+    and brute force over single pairs."""
+    w = W.random_case(seed, N_max=28, H=2, D=8, extreme=True)
+    assert w.startend.min() < -1 or w.startend.max() > w.N
+    out, lse = O.attention(w.q, w.k, w.v, w.cu_seqlens, w.startend, w.n_vec, w.causal, w.scale, chunk=5)
+    bo, bl = _brute_attention(w)
+    fin = np.isfinite(bl)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - bl[fin]), initial=0) <= 1e-12
+    assert np.max(np.abs(out - bo)) <= 1e-12
+    assert O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal) == sum(
+        0 if _brute_masked(w, i, j) else 1 for i in range(w.N) for j in range(w.N))
+    cu = [int(x) for x in w.cu_seqlens]
+    for Br, Bc in ((1, 1), (3, 2), (4, 5)):
+        kb_off, ext = O.extrema(w.cu_seqlens, w.startend, w.n_vec, w.causal, Bc)
+        assert ext.dtype.itemsize >= 4 and ext.min() >= W.INT32_MIN and ext.max() <= W.INT32_MAX
+        cls = O.classify(w.cu_seqlens, kb_off, ext, w.causal, Br, Bc)
+        for b, c in enumerate(cls):
+            s, e = cu[b], cu[b + 1]
+            for qt in range(c.shape[0]):
+                for kb in range(c.shape[1]):
+                    el = [_brute_masked(w, i, j)
+                          for i in range(s + qt * Br, min(s + (qt + 1) * Br, e))
+                          for j in range(s + kb * Bc, min(s + (kb + 1) * Bc, e))]
+                    if c[qt, kb] == O.FULL:
+                        assert all(el)
+                    elif c[qt, kb] == O.UNMASKED:
+                        assert not any(el)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_extrema_brute_force(seed):
     w = W.random_case(seed, with_qkv=False)

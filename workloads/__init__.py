@@ -37,7 +37,8 @@ import numpy as np
 
 __all__ = ["Workload", "make_config", "make_lengths", "PAGE_LTS", "PAGE_LTE",
            "causal_document_vectors", "shared_question_vectors", "PACKINGS", "packed_as", "rope_tables",
-           "prefix_window_vectors", "random_case", "CONFIG_IDS"]
+           "prefix_window_vectors", "random_case", "CONFIG_IDS", "extreme_endpoints",
+           "extreme_interval_workload", "INT32_MIN", "INT32_MAX"]
 
 # The 16-column causal example of the FlashMask article, §2.2 (its table is
 # flattened to a digit string in the extracted text; these are the 16 values
@@ -269,12 +270,82 @@ def document_workload(lengths: List[int], H: int = 2, D: int = 128, seed: int = 
     return w
 
 
+INT32_MIN, INT32_MAX = -(2 ** 31), 2 ** 31 - 1
+
+
+def extreme_endpoints(N: int):
+    """Endpoint values at and beyond the ends of the int32 range and of the
+    token axis: every int32 is a legal endpoint (half-open intervals,
+    start >= end empty; FlashMask article §2.1, §2.2)."""
+    return np.array([INT32_MIN, INT32_MIN + 1, -1, 0, N, N + 7, INT32_MAX], np.int64)
+
+
+def extreme_interval_workload(lengths: List[int], causal: bool, n_vec: int, H: int = 2, D: int = 128,
+                              seed: int = 31, with_qkv: bool = True) -> Workload:
+    """Documents of the given lengths whose column intervals use endpoints at
+    the int32 limits and past the token axis, arranged so that q tiles after
+    the first of a long document are cut by them: for a key j of document
+    [s, e), one interval in three is [INT32_MIN or -1, r), one in three
+    [r, N + 7 or INT32_MAX) with r a random row of [j, e] (of [s, e] for
+    the upper triangle), and the rest are empty ([0, 0)).  Causal n_vec = 1
+    stores LTS only (LTE = N), drawn as described at that branch.
+    bf16 q/k/v from `seed`."""
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in lengths]
+    N_ = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    lo_vals = np.array([INT32_MIN, -1], np.int64)
+    hi_vals = np.array([N_ + 7, INT32_MAX], np.int64)
+
+    def draw(s, e, first):
+        kind = rng.integers(0, 3, size=e - s)
+        r = np.array([rng.integers(j if first is None else s, e, endpoint=True) for j in range(s, e)], np.int64)
+        st = np.where(kind == 0, lo_vals[rng.integers(0, 2, e - s)], np.where(kind == 1, r, 0))
+        en = np.where(kind == 0, r, np.where(kind == 1, hi_vals[rng.integers(0, 2, e - s)], 0))
+        return st, en
+
+    lts = np.zeros(N_, np.int64); lte = np.zeros(N_, np.int64)
+    uts = np.zeros(N_, np.int64); ute = np.zeros(N_, np.int64)
+    for b in range(len(lens)):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if e <= s:
+            continue
+        lts[s:e], lte[s:e] = draw(s, e, None)
+        uts[s:e], ute[s:e] = draw(s, e, True)
+    if causal and n_vec == 1:
+        # LTE = N implicitly, so [LTS, N): half the keys hide the rows from a
+        # row r of [j, e] on, 35 % hide nothing (LTS = N + 7 or INT32_MAX),
+        # 15 % hide every row (LTS = INT32_MIN or -1)
+        u = rng.random(N_)
+        r = np.array([rng.integers(j, cu[np.searchsorted(cu, j, side="right")], endpoint=True)
+                      for j in range(N_)], np.int64)
+        lts = np.where(u < 0.5, r, np.where(u < 0.85, hi_vals[rng.integers(0, 2, N_)],
+                                            lo_vals[rng.integers(0, 2, N_)]))
+        sv = np.stack([lts])
+    elif causal:
+        sv = np.stack([lts, lte])
+    elif n_vec == 2:
+        sv = np.stack([lts, ute])
+    else:
+        sv = np.stack([lts, lte, uts, ute])
+    sv = sv.astype(np.int32)
+    w = Workload("extreme_%s%d_%dx%d" % ("c" if causal else "n", n_vec, len(lens), N_), N_, H, D, BF16, causal,
+                 n_vec, cu, sv, np.float32(1.0 / np.sqrt(np.float32(D))))
+    w.meta["seed"] = seed
+    if with_qkv:
+        w.q, w.k, w.v = draw_qkv(seed, w.N, w.H, w.D, w.dtype)
+    return w
+
+
 def random_case(seed: int, N_max: int = 64, H: int = 1, D: int = 16,
                 causal: Optional[bool] = None, n_vec: Optional[int] = None,
-                dtype: str = F32, with_qkv: bool = True, allow_empty: bool = True) -> Workload:
+                dtype: str = F32, with_qkv: bool = True, allow_empty: bool = True,
+                extreme: bool = False) -> Workload:
     """Tiny adversarial case: random sequence lengths (zero-length ones
     included), random interval endpoints in [0, N] including empty and
-    reversed intervals.  Used for brute-force checks."""
+    reversed intervals.  Used for brute-force checks.  extreme=True then
+    replaces about a third of the stored endpoints by values from
+    `extreme_endpoints` (int32 limits, -1, 0, N, N + 7)."""
     rng = np.random.default_rng(seed)
     N = int(rng.integers(1, N_max, endpoint=True))
     n_cuts = int(rng.integers(0, 5, endpoint=True))
@@ -291,7 +362,11 @@ def random_case(seed: int, N_max: int = 64, H: int = 1, D: int = 16,
     j = np.arange(N)
     tidy = rng.random(N) < 0.5
     sv[0] = np.where(tidy, np.minimum(j + rng.integers(0, 8, N), N), sv[0])
-    w = Workload("random_%d" % seed, N, H, D, dtype, causal, n_vec, cu, sv,
+    if extreme:
+        ext = extreme_endpoints(N)
+        pick = rng.random(sv.shape) < 0.35
+        sv = np.where(pick, ext[rng.integers(0, len(ext), size=sv.shape)], sv.astype(np.int64)).astype(np.int32)
+    w = Workload(("random_x%d" if extreme else "random_%d") % seed, N, H, D, dtype, causal, n_vec, cu, sv,
                  np.float32(rng.uniform(0.05, 0.5)))
     w.meta["seed"] = seed
     if with_qkv:
