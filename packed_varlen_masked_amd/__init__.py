@@ -120,6 +120,14 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise FMError(FM_E_UNSUPPORTED, "dtype %s (bf16 and fp32 are built)" % dt)
 
 
+def _workspace(ws: torch.Tensor, device) -> torch.Tensor:
+    """A caller's workspace: a contiguous uint8 CUDA tensor on `device` (its
+    numel() is then its size in bytes)."""
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or not ws.is_cuda or ws.device != device:
+        raise FMError(FM_E_INVAL, "workspace must be a contiguous uint8 CUDA tensor on the inputs' device")
+    return ws
+
+
 def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
     if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
         raise FMError(FM_E_INVAL, "%s must be a contiguous int32 CUDA tensor" % name)
@@ -326,11 +334,17 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
             lay = workspace_layout(N, B, H, D, bq, bk, S, False)
             ws = torch.zeros(lay.bytes, dtype=torch.uint8, device=q.device)
         else:
-            ws = workspace
+            ws = _workspace(workspace, q.device)
     if out is None:
         out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda
+          or out.device != q.device):
+        raise FMError(FM_E_INVAL, "out must be a contiguous CUDA tensor with q's shape, dtype and device")
     if lse is None:
         lse = torch.empty(H, N, dtype=torch.float32, device=q.device)
+    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (H, N) or not lse.is_contiguous() or not lse.is_cuda
+          or lse.device != q.device):
+        raise FMError(FM_E_INVAL, "lse must be a contiguous fp32 CUDA tensor [H, N] = [%d, %d] on q's device" % (H, N))
     if dropout_p > 0.0:
         _check(_lib.fm_attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), N, H, D, _ptr(cu), B,
                                         _ptr(startend) if N > 0 else None, n_vec, int(causal),
@@ -379,12 +393,17 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
         scale = 1.0 / math.sqrt(D)
     if workspace is None:
         workspace = torch.zeros(bwd_workspace_size(N, B, H, D, q.dtype), dtype=torch.uint8, device=q.device)
+    else:
+        workspace = _workspace(workspace, q.device)
+    if not lse.is_cuda or lse.device != q.device:
+        raise FMError(FM_E_INVAL, "lse must be on q's device")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise FMError(FM_E_INVAL, "%s must be contiguous with q's shape and dtype" % nm)
+        if (t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda
+                or t.device != q.device):
+            raise FMError(FM_E_INVAL, "%s must be a contiguous CUDA tensor with q's shape, dtype and device" % nm)
     common = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dtype_code(q.dtype), N, H, D,
               _ptr(cu), B, _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel())

@@ -257,6 +257,10 @@ __device__ __attribute__((always_inline)) inline uint32_t row_bits(int s, int e)
     const int w = e - s;   // s <= 31 whenever w > 0
     return w >= 32 ? 0xffffffffu : ((1u << w) - 1u) << (s & 31);
 }
+// Interval endpoint x (any int32 row index) relative to the wave's first row
+// q0 >= 0, clamped below at 0 before the subtraction: max(x, q0) - q0 lies
+// in [0, 2^31) and cannot wrap, where x - q0 would for x < INT32_MIN + q0.
+__device__ __attribute__((always_inline)) inline int rel_row(int x, int q0) { return max(x, q0) - q0; }
 
 // x, or y where the lane's bit of the 64-lane mask {lo: lanes 0-31, hi:
 // lanes 32-63} is set (one v_cndmask with the mask in scalar registers).
@@ -283,7 +287,9 @@ __device__ __attribute__((always_inline)) inline float mask_max(f32x16 (&sacc)[2
         const int key = c0 + lane;
         uint32_t mk = causal ? row_bits(0, key - q0) : 0u;
         if (key >= c1) mk = 0xffffffffu;
-        if (iv) mk |= row_bits(cmv[lane] - q0, cmv[BC + lane] - q0) | row_bits(cmv[2 * BC + lane] - q0, cmv[3 * BC + lane] - q0);
+        if (iv)
+            mk |= row_bits(rel_row(cmv[lane], q0), rel_row(cmv[BC + lane], q0)) |
+                  row_bits(rel_row(cmv[2 * BC + lane], q0), rel_row(cmv[3 * BC + lane], q0));
         const int mki = (int)mk;
         const float ninf = -INFINITY;
 #pragma unroll

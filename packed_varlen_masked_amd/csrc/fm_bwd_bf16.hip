@@ -102,6 +102,9 @@ __device__ __attribute__((always_inline)) inline uint32_t row_bits(int s, int e)
     const int w = e - s;
     return w >= 32 ? 0xffffffffu : ((1u << w) - 1u) << (s & 31);
 }
+// Interval endpoint x (any int32 row index) relative to the first row q0 >= 0
+// of 32, clamped below at 0 first so that the subtraction cannot wrap.
+__device__ __attribute__((always_inline)) inline int rel_row(int x, int q0) { return max(x, q0) - q0; }
 // x, or y where the lane's bit of {lo: lanes 0-31, hi: lanes 32-63} is set.
 __device__ __attribute__((always_inline)) inline float select_lanes(float x, float y, uint32_t lo, uint32_t hi) {
     const uint64_t m = ((uint64_t)hi << 32) | lo;
@@ -662,7 +665,8 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
             const int key = c0 + lane;
             mk = a.causal ? row_bits(0, key - q0) : 0u;
             if (key >= c1) mk = 0xffffffffu;
-            mk |= row_bits(st.mv.lts - q0, st.mv.lte - q0) | row_bits(st.mv.uts - q0, st.mv.ute - q0);
+            mk |= row_bits(rel_row(st.mv.lts, q0), rel_row(st.mv.lte, q0)) |
+                  row_bits(rel_row(st.mv.uts, q0), rel_row(st.mv.ute, q0));
         }
         __syncthreads();
         bool npart = false;

@@ -95,6 +95,17 @@ def test_bwd_documents(pv, lens):
     compare(w, got, g, "docs")
 
 
+@pytest.mark.parametrize("causal,n_vec", [(True, 1), (True, 2), (False, 2), (False, 4)])
+def test_bwd_extreme_endpoints(pv, causal, n_vec):
+    """Endpoints at the int32 limits and past the token axis on documents of
+    several q tiles: dq (whose kernel builds per-key row masks relative to a
+    wave's first row) agrees with the oracle as dk and dv do."""
+    w = W.extreme_interval_workload([700, 300, 1100], causal, n_vec, H=2, seed=31 + n_vec)
+    say("bwd extreme endpoints", w.name)
+    got, g = run_bwd(pv, w)
+    compare(w, got, g, w.name)
+
+
 def test_bwd_varlen_workload(pv):
     w = W.make_config(2)
     say("bwd varlen workload N=%d" % w.N)

@@ -68,7 +68,14 @@ def test_dropout_forward(pv, idx, p, S):
     err = np.abs(o - oo)
     e_l = float(np.max(np.abs(l[fin] - ol[fin]), initial=0.0))
     at = np.unravel_index(np.argmax(err), o.shape)
-    say("  max|dout|=%.3e at %s (ref %.4f) max|dlse|=%.3e" % (float(err[at]), at, oo[at], e_l))
+    small = np.abs(oo) <= 2.0
+    e_small = float(np.max(err[small], initial=0.0))
+    say("  max|dout|=%.3e at %s (ref %.4f), max|dout| where |ref| <= 2: %.3e, max|dlse|=%.3e"
+        % (float(err[at]), at, oo[at], e_small, e_l))
+    # the plain bar wherever |ref| <= 2 (the range of the inputs' softmax
+    # averages); above it the bf16 store of the inflated kept values adds up
+    # to 2^-8 of the value
+    assert e_small <= 2e-2
     assert np.all(err <= 2e-2 + 2.0 ** -8 * np.abs(oo)) and e_l <= 1e-3
 
 

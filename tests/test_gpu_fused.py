@@ -1,14 +1,14 @@
-"""GPU tests of the fused one-launch path (plan built in LDS by every
-workgroup, items run from a static share, split rows merged by the last
-split to arrive).
+"""GPU tests of the fused path (plan built in LDS by every workgroup of the
+attention launch, items run from a static share; split rows combined in
+split order by a second, merge launch).
 
 - the plan the fused launch writes into the workspace equals the oracle's
   (bit-exact extrema, kb offsets, class counts, work items);
 - out / lse are within the parity bars of the fp64 oracle;
 - the fused path and the plan-in-workspace path give identical bits (same
   plan, same item code, split merge independent of arrival order);
-- a workspace is reusable: the split arrival counters are back at zero
-  after every call, across paths.
+- a workspace is reusable across calls and paths (the planned kernel's
+  work counter is back at zero after every call).
 """
 import sys
 

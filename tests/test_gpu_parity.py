@@ -155,8 +155,9 @@ def test_random_plan_ints(pv, seed):
 
 @pytest.mark.parametrize("k,S", [(1, 0), (2, 0), (2, 4), (3, 0), (4, 3), (5, 0)])
 def test_fused_plan_matches_oracle(pv, k, S):
-    """The plan path (one workgroup per sequence: extrema + classes, then the
-    sort) writes the same integers as the oracle into the workspace."""
+    """The plan path (the extrema launch, the tile-class launch with 16
+    workgroups per sequence, then the sort) writes the same integers as the
+    oracle into the workspace."""
     w = W.make_config(k, with_qkv=False)
     _, _, _, cu, sv = dev_inputs(w)
     dt = torch.float32 if w.dtype == W.F32 else torch.bfloat16
@@ -214,12 +215,70 @@ def test_reduced_configs_full(pv, k, N, H):
     compare_full(w, out2, lse2, "cfg%d reduced split3" % k)
 
 
+# Heads compared on every row at full size: the first and the last (the
+# prefix-LM workload, 131072 tokens, only head 0 to keep the oracle's time
+# in bounds); every head is covered by the sampled rows.
+FULL_HEADS = {3: [0, 31], 4: [0, 31], 5: [0]}
+
+
 @pytest.mark.parametrize("k", [3, 4, 5])
-def test_full_configs_sampled(pv, k):
+def test_full_config(pv, k):
+    """The full-size workloads through the default call (the path and split
+    fm_attn_fwd chooses for them) and through the planned path with a plan
+    built beforehand: both give the same bits, every row of the heads in
+    FULL_HEADS matches the oracle (out <= 2e-2, lse <= 1e-3, -inf exactly
+    where the oracle has it), and 64 sampled (row, head) pairs of all heads
+    too."""
+    from par_oracle import attention_heads
     w = W.make_config(k)
-    say("full cfg", k, w.N, w.H, w.B)
-    out, lse = run(pv, w)
+    fused = pv.fused_path(w.N, w.B, w.H, w.D, torch.bfloat16, w.n_vec, w.causal)
+    say("full cfg", k, "N=%d H=%d B=%d fused=%d" % (w.N, w.H, w.B, fused))
+    q, kk, v, cu, sv = dev_inputs(w)
+    out, lse = pv.attn_fwd(q, kk, v, cu, sv, w.n_vec, w.causal, float(w.scale))
+    plan = pv.build_plan(cu, sv, w.n_vec, w.causal, w.N, w.H, w.D, torch.bfloat16)
+    out2, lse2 = pv.attn_fwd(q, kk, v, cu, sv, w.n_vec, w.causal, float(w.scale), plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    del q, kk, v, out2, lse2
+    heads = FULL_HEADS[k]
+    oo, ol = attention_heads(w, heads)
+    o = out[:, heads].float().cpu().numpy().astype(np.float64)
+    l = lse[heads].cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(l), np.isneginf(ol)), "lse -inf pattern differs"
+    fin = np.isfinite(ol)
+    e_out = float(np.max(np.abs(o - oo)))
+    e_lse = float(np.max(np.abs(l[fin] - ol[fin]), initial=0.0))
+    say("  heads %s, all %d rows: max|dout|=%.3e max|dlse|=%.3e" % (heads, w.N, e_out, e_lse))
+    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
     compare_rows(w, out, lse, n_rows=64, seed=k)
+
+
+@pytest.mark.parametrize("k", [3, 4, 5])
+@pytest.mark.parametrize("S", [0, 6])
+def test_full_plan_ints_library_tiles(pv, k, S):
+    """Extrema, classes, class counts and the work list of the full-size
+    workloads at the tiles fm_attn_fwd runs (fm_get_tile_config: 256 x 64),
+    bit-exact against the oracle, through the separate calls and through
+    fm_build_plan's workspace; S = 0 is the split the library chooses for
+    these sizes (fm_auto_split), S = 6 splits long rows."""
+    w = W.make_config(k, with_qkv=False)
+    Br, Bc = pv.tile_config(torch.bfloat16, 128)
+    assert (Br, Bc) == (256, 64)
+    assert pv.auto_split(w.N, w.B, w.H, torch.bfloat16, 128) == 0
+    check_plan_ints(pv, w, Br, Bc, S)
+    _, _, _, cu, sv = dev_inputs(w)
+    plan = pv.build_plan(cu, sv, w.n_vec, w.causal, w.N, w.H, w.D, torch.bfloat16, max_kb_per_item=S,
+                         want_class_map=True)
+    hdr = plan.header()
+    okb, oext, ocls, ocnt, oitems = oracle_plan(w, Br, Bc, w.H, S)
+    assert hdr["status"] == 0 and hdr["n_kblocks"] == len(oext)
+    assert np.array_equal(plan.kb_off().cpu().numpy(), okb)
+    assert np.array_equal(plan.extrema(len(oext)).cpu().numpy(), oext)
+    assert hdr["class_counts"] == ocnt.tolist()
+    flat = np.concatenate([c.reshape(-1) for c in ocls])
+    assert np.array_equal(plan.tile_class(flat.size).cpu().numpy().astype(np.int8), flat)
+    assert hdr["n_items"] == len(oitems)
+    assert np.array_equal(plan.items(len(oitems)).cpu().numpy()[:, :8], oitems)
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -230,6 +289,30 @@ def test_random_bf16(pv, seed):
     compare_full(w, out, lse, "random bf16")
     out2, lse2 = run(pv, w, max_kb_per_item=1)
     compare_full(w, out2, lse2, "random bf16 split1")
+
+
+@pytest.mark.parametrize("causal,n_vec", [(True, 1), (True, 2), (False, 2), (False, 4)])
+def test_extreme_endpoints(pv, causal, n_vec):
+    """Interval endpoints at the int32 limits and past the token axis
+    (INT32_MIN, -1, N + 7, INT32_MAX; FlashMask article §2.1, §2.2: any
+    half-open interval, start >= end empty) on documents of several q tiles,
+    so that tiles of q tiles after the first are PARTIAL under them: the
+    extrema, classes and work list bit-exact, out and lse within the bars on
+    the fused path (split and unsplit) and on the planned path."""
+    w = W.extreme_interval_workload([700, 300, 1100], causal, n_vec, H=2, seed=31 + n_vec)
+    say("extreme endpoints", w.name)
+    okb, oext, ocls, _, _ = oracle_plan(w, 256, 64, w.H, 0)
+    assert int(w.startend.min()) == W.INT32_MIN or int(w.startend.max()) == W.INT32_MAX
+    assert any((c[1:] == O.PARTIAL).any() for c in ocls if c.shape[0] > 1)
+    for S in (0, 2):
+        check_plan_ints(pv, w, 256, 64, S)
+        out, lse = run(pv, w, max_kb_per_item=S)
+        compare_full(w, out, lse, "extreme S=%d" % S)
+    q, k, v, cu, sv = dev_inputs(w)
+    plan = pv.build_plan(cu, sv, w.n_vec, w.causal, w.N, w.H, w.D, torch.bfloat16, max_kb_per_item=0)
+    out, lse = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), plan=plan)
+    torch.cuda.synchronize()
+    compare_full(w, out, lse, "extreme planned")
 
 
 # ---------------------------------------------------------- properties
