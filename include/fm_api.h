@@ -294,6 +294,41 @@ int fm_attn_fwd_dropout(const void* q, const void* k, const void* v, int dtype,
                         unsigned flags, float dropout_p, uint64_t seed, uint64_t offset,
                         hipStream_t stream);
 
+/* ---- allocation-free forward ------------------------------------------ */
+/* Size of the library's own per-device array that fm_attn_fwd_noalloc uses
+ * as its workspace: 64 MiB.                                                */
+#define FM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * fm_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Its workspace is a fixed array
+ * of FM_NOALLOC_SCRATCH_BYTES in the library's device code, one per GPU,
+ * held until the process ends; the call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).  The caller still passes every
+ * input and output.  Arguments, results and kernels are those of
+ * fm_attn_fwd, except:
+ *   - the problem's workspace, fm_workspace_layout(...).bytes for the tiles
+ *     and split the call resolves to (fm_workspace_size for the defaults),
+ *     must fit in FM_NOALLOC_SCRATCH_BYTES; larger problems are rejected
+ *     with FM_E_WORKSPACE before anything is enqueued (the default calls of
+ *     every workload up to 131072 tokens x 8 heads, and 32768 x 32, fit);
+ *   - FM_FLAG_PLAN_READY is rejected (FM_E_INVAL): the array keeps only the
+ *     last call's contents, so every call builds its own plan;
+ *   - every call on one GPU shares that GPU's array: calls that can overlap
+ *     on one GPU (unordered streams, several host threads) race on it and
+ *     must be serialised by the caller.  Nothing in the array needs clearing
+ *     between calls: each call writes every header word and plan entry it
+ *     reads before reading it.
+ * The array's device address is looked up (hipGetSymbolAddress) on the
+ * first call made with a device current and kept per device.
+ */
+int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v, int dtype,
+                        int64_t N, int H, int D, const int32_t* cu_seqlens, int B,
+                        const int32_t* startend, int n_vec, int causal, float scale,
+                        void* out, float* softmax_lse, int block_q, int block_k,
+                        int max_kb_per_item, unsigned flags, hipStream_t stream);
+
 /*
  * 1 if fm_attn_fwd with these sizes and flags takes the fused one-launch
  * path (bf16, head_dim 128, default tiles, no FM_FLAG_NO_SKIP or

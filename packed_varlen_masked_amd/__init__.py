@@ -8,7 +8,8 @@ raises.
 
 Entry points mirror include/fm_api.h:
   tile_config, auto_split, workspace_layout, workspace_size,
-  preprocess_mask, build_worklist, build_plan, attn_fwd, read_status.
+  preprocess_mask, build_worklist, build_plan, attn_fwd, attn_fwd_noalloc,
+  attn_bwd, rope_qk_, read_status.
 """
 from __future__ import annotations
 
@@ -83,6 +84,7 @@ def _load():
         "fm_rope_qk": (I, [P, P, I, I64, I, I, I, P, I, P, P, I64, I, P, P]),
         "fm_attn_fwd_dropout": (I, [P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, I, I, I, P, SZ, U, F, U64, U64, P]),
         "fm_attn_bwd_dropout": (I, [P, P, P, P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, P, P, SZ, F, U64, U64, P]),
+        "fm_attn_fwd_noalloc": (I, [P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, I, I, I, U, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -96,7 +98,8 @@ EXPORTED = ("fm_last_error", "fm_version", "fm_self_check", "fm_get_tile_config"
             "fm_workspace_layout", "fm_workspace_size", "fm_worklist_scratch_size",
             "fm_preprocess_mask", "fm_build_worklist", "fm_build_plan", "fm_attn_fwd",
             "fm_read_status", "fm_fused_path", "fm_bwd_workspace_size", "fm_attn_bwd", "fm_rope_qk",
-            "fm_attn_fwd_dropout", "fm_attn_bwd_dropout")
+            "fm_attn_fwd_dropout", "fm_attn_bwd_dropout", "fm_attn_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # FM_NOALLOC_SCRATCH_BYTES
 
 
 def _check(rc: int):
@@ -354,6 +357,42 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
         _check(_lib.fm_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), N, H, D, _ptr(cu), B,
                                 _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
                                 _ptr(out), _ptr(lse), bq, bk, S, _ptr(ws), ws.numel(), flags, _stream()))
+    return out, lse
+
+
+def attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                     startend: torch.Tensor, n_vec: int, causal: bool, out: torch.Tensor, lse: torch.Tensor,
+                     scale: Optional[float] = None, max_kb_per_item: int = -1, block_q: int = 0,
+                     block_k: int = 0, flags: int = 0):
+    """fm_attn_fwd_noalloc: the forward with the library's own per-device
+    workspace array; neither this call nor the library allocates anything,
+    so out [N, H, D] and lse fp32 [H, N] come from the caller.  Calls that
+    can overlap on one GPU race on the array."""
+    if q.shape != k.shape or q.shape != v.shape or q.dim() != 3:
+        raise FMError(FM_E_INVAL, "q, k, v must share one [N, H, D] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FMError(FM_E_INVAL, "q, k, v must share one dtype")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise FMError(FM_E_INVAL, "%s must be a contiguous CUDA tensor" % nm)
+    N, H, D = q.shape
+    if (out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda
+            or out.device != q.device):
+        raise FMError(FM_E_INVAL, "out must be a contiguous CUDA tensor with q's shape, dtype and device")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (H, N) or not lse.is_contiguous() or not lse.is_cuda
+            or lse.device != q.device):
+        raise FMError(FM_E_INVAL, "lse must be a contiguous fp32 CUDA tensor [H, N] = [%d, %d] on q's device" % (H, N))
+    cu = _i32(cu_seqlens, "cu_seqlens")
+    B = cu.numel() - 1
+    if N > 0:
+        _i32(startend, "startend")
+        if tuple(startend.shape) != (n_vec, N):
+            raise FMError(FM_E_INVAL, "startend must be [n_vec, N] = [%d, %d]" % (n_vec, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(_lib.fm_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), N, H, D, _ptr(cu), B,
+                                    _ptr(startend) if N > 0 else None, n_vec, int(causal), ctypes.c_float(scale),
+                                    _ptr(out), _ptr(lse), block_q, block_k, max_kb_per_item, flags, _stream()))
     return out, lse
 
 

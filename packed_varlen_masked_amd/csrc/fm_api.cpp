@@ -179,6 +179,31 @@ int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_
     return FM_OK;
 }
 
+// Workspace of fm_attn_fwd_noalloc.  Each GPU the library runs on holds its
+// own copy (loaded with the library's device code) until the process ends.
+// On the host `scratch` names a stand-in, not device memory: host code uses
+// only the device address hipGetSymbolAddress returns for it, looked up
+// once per device with that device current.
+static __device__ __align__(256) char scratch[FM_NOALLOC_SCRATCH_BYTES];
+
+int noalloc_scratch(void** out) {
+    static std::mutex mu;
+    static std::vector<void*> addr;   // per device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(FM_E_HIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(FM_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return FM_OK;
+}
+
 // Flag value of one call that marks the partials it wrote: a process-wide
 // counter, never 0, so flags need no clearing between calls.
 uint32_t next_call_id() {
@@ -559,6 +584,33 @@ int fm_attn_fwd_dropout(const void* q, const void* k, const void* v, int dtype, 
     return attn_fwd_impl(q, k, v, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal, scale, out, softmax_lse,
                          block_q, block_k, max_kb_per_item, workspace, ws_bytes, flags, dropout_p, seed, offset,
                          stream);
+}
+
+int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v, int dtype, int64_t N, int H, int D,
+                        const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
+                        float scale, void* out, float* softmax_lse, int block_q, int block_k,
+                        int max_kb_per_item, unsigned flags, hipStream_t stream) {
+    int rc = check_sizes(N, B, H);
+    if (rc) return rc;
+    if (flags & FM_FLAG_PLAN_READY)
+        return fail(FM_E_INVAL, "FM_FLAG_PLAN_READY is not accepted: the allocation-free call builds its plan");
+    // the layout fm_attn_fwd would need (its argument checks follow there)
+    int dq, dk;
+    if ((rc = tile_config(dtype, D, &dq, &dk))) return rc;
+    const int bq = block_q ? block_q : dq, bk = block_k ? block_k : dk;
+    const int S = dtype == FM_F32 ? 0 : max_kb_per_item < 0 ? auto_split(N, B, H, dtype) : max_kb_per_item;
+    fm_ws_layout L;
+    if ((rc = layout_impl(N, B, H, D, bq, bk, S, 0, &L))) return rc;
+    if (L.bytes > FM_NOALLOC_SCRATCH_BYTES)
+        return fail(FM_E_WORKSPACE,
+                    "this problem needs a %zu-byte workspace, more than the %zu bytes of the allocation-free "
+                    "entry point's array: call fm_attn_fwd with a workspace",
+                    L.bytes, (size_t)FM_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((rc = noalloc_scratch(&ws))) return rc;
+    rc = attn_fwd_impl(q, k, v, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal, scale, out, softmax_lse,
+                       block_q, block_k, max_kb_per_item, ws, FM_NOALLOC_SCRATCH_BYTES, flags, 0.f, 0, 0, stream);
+    return rc ? rc : ok();
 }
 
 int fm_fused_path(int64_t N, int B, int H, int head_dim, int dtype, int n_vec, int causal,

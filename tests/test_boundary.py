@@ -101,6 +101,25 @@ def test_attn_rejects_on_host(pv, kw, code):
     assert msg
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=2), 1),                         # FM_FLAG_PLAN_READY: the array holds no plan of the caller's
+    (dict(N=16384, H=32, B=14, S=6), 3),        # a 6 GB workspace does not fit the 64 MiB array
+    (dict(D=64), 2), (dict(B=0), 1), (dict(H=0), 1),
+])
+def test_noalloc_rejects_on_host(pv, kw, code):
+    """The allocation-free forward rejects a ready-plan flag and problems
+    whose workspace exceeds its array before it touches the device."""
+    a = dict(dtype=pv.FM_BF16, N=256, H=2, D=128, B=1, S=0, flags=0)
+    a.update(kw)
+    rc = pv._lib.fm_attn_fwd_noalloc(FAKE, FAKE, FAKE, a["dtype"], a["N"], a["H"], a["D"], FAKE, a["B"], FAKE, 1, 1,
+                                     ctypes.c_float(0.1), FAKE, FAKE, 0, 0, a["S"], a["flags"], None)
+    msg = pv._lib.fm_last_error().decode()
+    assert rc == code, msg
+    assert msg
+    if code == 3:
+        assert str(pv.NOALLOC_SCRATCH_BYTES) in msg
+
+
 def test_preprocess_rejects_on_host(pv):
     L = pv._lib
     r = L.fm_preprocess_mask(FAKE, 3, 1, FAKE, 1, 64, 16, FAKE, FAKE, 100, FAKE, FAKE, None)
