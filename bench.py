@@ -74,7 +74,7 @@ def parse():
     return ap.parse_args()
 
 
-FWD_SOURCES = ("fm_api.cpp", "fm_attn_bf16.hip", "fm_common.hpp", "fm_internal.h", "fm_lds_plan.h", "fm_plan.hip")
+FWD_SOURCES = ("fm_api.cpp", "fm_attn_bf16.hip", "fm_common.hpp", "fm_internal.h", "fm_own_plan.h", "fm_plan.hip")
 
 
 def source_hash():
@@ -229,7 +229,7 @@ def make_setup(w, args):
             attn_with_plan()
             if ev_b is not None:
                 ev_b.record()
-    hdr = (plan if not fused else pv.Plan(ws, plan.layout, w.N, w.B, w.H, w.D, dt, w.causal, w.n_vec, S)).header
+    hdr = plan.header   # the plan built above (the fused path writes none)
     return dict(dt=dt, dev=dev, step=step, attn_with_plan=attn_with_plan, plan=plan, S=S, fused=fused, hdr=hdr,
                 tensors=(q, k, v, cu, sv))
 

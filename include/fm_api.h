@@ -125,7 +125,8 @@ int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim);
  * 256-byte aligned.  `*_cap` are host-side upper bounds computed from
  * (N, B, H, Br, Bc, S) only.
  *   hdr:        int32 status, n_kblocks, n_items, sched_counter, n_slots,
- *               n_merge at byte 0..23; int64 class_counts[3] at byte 64.
+ *               n_merge, n_fused at byte 0..27; int64 class_counts[3] at
+ *               byte 64.
  *   kb_off:     int32 [B+1]         first key block of each sequence
  *   extrema:    int32 [kb_cap][8]   per key block: min/max of LTS, LTE,
  *                                   UTS, UTE (in that order)
@@ -135,10 +136,13 @@ int fm_auto_split(int64_t N, int B, int H, int dtype, int head_dim);
  *   partial:    split partials (S > 0), per (slot, head) Br*D fp16 values of
  *               the split's O / l scaled by 2^-e (e per row), then Br each of
  *               fp32 m, fp32 l and int32 e: Br*D*2 + 3*Br*4 bytes
- *   merge:      int32 [slot_cap * H / 2 + 1][8] (S > 0): the split rows,
- *               one entry per (split row, head): slot of split 0, head,
- *               first row, end row, number of splits, 3 zero words;
- *               n_merge entries, written by the planners for the merge.
+ *   merge:      int32 [max(slot_cap * H / 2 + 1, qt_cap * H)][8] (S > 0),
+ *               entries of slot of split 0, head, first row, end row,
+ *               number of splits, 3 zero words: the planners list the split
+ *               rows (n_merge entries, one per split row and head); the
+ *               fused path of fm_attn_fwd keeps one entry per (q tile,
+ *               head), q tile r at r * H + head (n_fused entries; rows of
+ *               one chunk say 1 split), qt_cap = ceil(N / block_q) + B.
  */
 typedef struct fm_ws_layout {
     size_t  bytes;
@@ -260,11 +264,13 @@ int fm_build_plan(const int32_t* cu_seqlens, int B, int64_t N, int H, int head_d
  *   (class map not needed).  flags: FM_FLAG_*.
  * Without FM_FLAG_PLAN_READY the plan is built first.  Small bf16 problems
  * (see fm_fused_path) take the fused path: ONE attention launch in which
- * every workgroup rebuilds the plan in LDS and runs its share of the
- * items; the plan is still written to the workspace, identical to
- * fm_build_plan's.  Split rows (S > 0) write partials that a second
- * launch combines in split order.  Results are deterministic: the same
- * inputs give the same bits, on either path.
+ * every workgroup derives its own work items (the chunks of the work list
+ * above) from cu_seqlens and the mask vectors of its own q-tile row; no
+ * plan is written to the workspace (its header then lists no items, so a
+ * later FM_FLAG_PLAN_READY call on it runs nothing until fm_build_plan
+ * fills it).  Split rows (S > 0) write partials that a second launch
+ * combines in split order.  Results are deterministic: the same inputs
+ * give the same bits, on either path.
  */
 int fm_attn_fwd(const void* q, const void* k, const void* v, int dtype,
                 int64_t N, int H, int D, const int32_t* cu_seqlens, int B,
@@ -332,10 +338,11 @@ int fm_attn_fwd_noalloc(const void* q, const void* k, const void* v, int dtype,
 /*
  * 1 if fm_attn_fwd with these sizes and flags takes the fused one-launch
  * path (bf16, head_dim 128, default tiles, no FM_FLAG_NO_SKIP or
- * FM_FLAG_PLAN_READY, B <= 255, n_vec * N <= 16384, and the plan's bounds
- * on key blocks, q tiles, tiles, split chunks and items fit one
- * workgroup's LDS and the launch); 0 if not; -1 on bad arguments.
- * max_kb_per_item < 0 = auto.  Queries the current device's CU count.
+ * FM_FLAG_PLAN_READY, N <= 16384, B <= 255, at most 1024 q tiles and at
+ * most 8 work items per workgroup of a launch with one workgroup per
+ * compute unit, by the host's upper bounds); 0 if not; -1 on bad
+ * arguments.  max_kb_per_item < 0 = auto.  Queries the current device's
+ * CU count.
  */
 int fm_fused_path(int64_t N, int B, int H, int head_dim, int dtype, int n_vec, int causal,
                   int max_kb_per_item, unsigned flags);

@@ -5,7 +5,6 @@
 #include "fm_api.h"
 #include "fm_internal.h"
 #include "fm_bf16_copies.h"
-#include "fm_lds_plan.h"
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -128,18 +127,28 @@ int auto_split(int64_t N, int B, int H, int dtype) {
     return est_items >= 512 ? 0 : 6;
 }
 
-// The fused path (one launch that plans in LDS and attends) takes a call
-// when every bound of the in-workgroup planner holds for these sizes.
+// The fused path (one launch in which every workgroup plans its own items)
+// takes small problems: every bound of its tables holds for these sizes, and
+// a workgroup runs at most a few items (each item pays its own planning, so
+// larger problems are faster with the planning launches and the longest-first
+// schedule of the planned path).
+constexpr int64_t kFusedMaxTokens = 16384;
+
 bool fused_eligible(int64_t N, int B, int H, int dtype, int D, int bq, int bk, int S, int n_vec,
                     unsigned flags, int n_cu) {
-    if (dtype != FM_BF16 || D != 128 || bq != 256 || bk != 64 || N <= 0) return false;
+    (void)n_vec;
+    if (dtype != FM_BF16 || D != 128 || bq != 256 || bk != 64 || N <= 0 || N > kFusedMaxTokens) return false;
     if (flags & (FM_FLAG_NO_SKIP | FM_FLAG_PLAN_READY)) return false;
-    if (B > fm::LP_MAX_B || (int64_t)n_vec * N > fm::LP_MAX_SV) return false;
+    if (B > fm::FUSED_MAX_B) return false;
     Caps c;
     if (!compute_caps(N, B, H, bq, bk, S, &c)) return false;
-    return c.kb <= fm::LP_MAX_KB && c.qt <= fm::LP_MAX_ROWS && c.map <= fm::LP_MAX_TILES &&
-           c.slot <= fm::LP_MAX_SLOTS && c.item <= (int64_t)fm::LP_MAX_MY * fm::fused_grid(n_cu);
+    return c.qt <= fm::FUSED_MAX_ROWS && c.item <= (int64_t)fm::FUSED_MAX_MY * fm::fused_grid(n_cu);
 }
+
+// Entries of the merge table: the planners list split rows only (a split
+// row has >= 2 slots, so slot_cap * H / 2 + 1 entries suffice); the fused
+// path keeps one entry per (q tile, head).
+int64_t merge_entries(const Caps& c, int H) { return std::max<int64_t>(c.slot * H / 2 + 1, c.qt * H); }
 
 int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_map,
                 fm_ws_layout* out) {
@@ -168,9 +177,9 @@ int layout_impl(int64_t N, int B, int H, int D, int Br, int Bc, int S, int want_
     // per (slot, head): Br x D fp16 values of O / l, then m, l and the scale exponent per row
     L.partial_bytes = S > 0 ? (size_t)c.slot * H * ((size_t)Br * D * 2 + 3 * (size_t)Br * 4) : 0;
     L.off_partial = S > 0 ? off : 0; off = align256(off + L.partial_bytes);
-    // split-row list: a split row has >= 2 slots, so slot_cap * H / 2 + 1 entries suffice
+    // merge table (split rows)
     L.off_merge = S > 0 ? off : 0;
-    if (S > 0) off = align256(off + ((size_t)c.slot * H / 2 + 1) * fm::MERGE_WORDS * 4);
+    if (S > 0) off = align256(off + (size_t)merge_entries(c, H) * fm::MERGE_WORDS * 4);
     if ((int64_t)off > kMaxBytes) return fail(FM_E_INVAL, "workspace would exceed 64 TiB");
     L.bytes = off;
     L.kb_cap = c.kb; L.item_cap = c.item; L.map_cap = want_map ? c.map : 0; L.slot_cap = c.slot;
@@ -550,7 +559,11 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, int dtype,
     a.partial = S > 0 ? (float*)(w.base + w.L.off_partial) : nullptr;
     a.merge_list = S > 0 ? (const int32_t*)(w.base + w.L.off_merge) : nullptr;
     a.n_merge = w.hdr() + fm::HDR_NMERGE;
-    a.merge_cap = S > 0 ? (int64_t)(w.L.slot_cap * H / 2 + 1) : 0;
+    a.merge_cap = S > 0 ? [&] {
+        Caps c;
+        compute_caps(N, B, H, bq, bk, S, &c);
+        return merge_entries(c, H);
+    }() : 0;
     a.flags = flags;
     a.w_hdr = w.hdr();
     a.w_kb_off = (int32_t*)(w.base + w.L.off_kb_off);
@@ -560,6 +573,10 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, int dtype,
     a.w_merge = S > 0 ? (int32_t*)(w.base + w.L.off_merge) : nullptr;
     a.drop_t = drop_t; a.drop_ks = drop_ks;
     a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32); a.offset = (uint32_t)offset;
+    if (fused) {   // the fused path's merge table: one entry per (q tile, head)
+        a.n_merge = w.hdr() + fm::HDR_NFUSED;
+        if (S > 0) a.merge_cap = (cdiv(N, bq) + B) * (int64_t)H;
+    }
     const hipError_t e = fused ? fm::launch_fused_bf16(a, n_cu, stream)
                        : dtype == FM_BF16 ? fm::launch_attn_bf16(a, n_cu, stream)
                                           : fm::launch_attn_f32(a, n_cu, stream);

@@ -45,7 +45,6 @@
 #include "fm_internal.h"
 #include "fm_api.h"
 #include "fm_bf16_copies.h"
-#include "fm_lds_plan.h"
 
 namespace fm {
 
@@ -678,6 +677,20 @@ __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a
     }
 }
 
+// Q^T fragments (B operand) of the wave's 32 query rows: lane holds query
+// qrow, channels 16s + 8hh .. +7 in qf[s]; rows at or past r1 are zero.
+__device__ __attribute__((always_inline)) inline void load_q(const AttnArgs& a, const Wave& Wv, int r1, int64_t hoff,
+                                                             bf16x8 (&qf)[8]) {
+    if (Wv.qrow < r1) {
+        const uint16_t* qp = (const uint16_t*)a.q + (int64_t)Wv.qrow * ((int64_t)a.H * HD) + hoff + 8 * Wv.hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
+    } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+}
+
 // ---- one work item ----------------------------------------------------
 // Q tile in registers, the first K/V tile on its way, the visit list, the KV
 // loop, the epilogue.  STD: the visit list is built here from the block
@@ -687,7 +700,7 @@ __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a
 template <bool STD, bool DROP>
 __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a, Wave& Wv, const Item& I,
                                                                int vis_off, bool& rec_pending, int fv, int& nrec,
-                                                               int n_items) {
+                                                               int n_items, bf16x8 (&qf)[8], int pre_kb = -1) {
     const int tid = Wv.tid, lane = Wv.lane, w = Wv.w;
     const int64_t rs = (int64_t)a.H * HD;
     Wv.qrow = I.r0 + 32 * w + Wv.n;
@@ -708,16 +721,10 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
             xw1 = *(const u32x4*)(I.xb + (int64_t)kb * 8 + 4);
         }
     }
-    if (!Wv.no_skip && lo < hi) copy_tile_pair(a, I, Wv, Kh, Vh, lo);
-    bf16x8 qf[8];   // Q^T fragments (B operand): lane holds query n, channels 16s+8hh..+7
-    if (Wv.qrow < I.r1) {
-        const uint16_t* qp = (const uint16_t*)a.q + (int64_t)Wv.qrow * rs + I.hoff + 8 * Wv.hh;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
-    } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
-    }
+    // (the fused kernel loaded Q before planning and may have copied the
+    // first tile already: pre_kb)
+    if (!Wv.no_skip && lo < hi && lo != pre_kb) copy_tile_pair(a, I, Wv, Kh, Vh, lo);
+    if constexpr (STD) load_q(a, Wv, I.r1, I.hoff, qf);
 
     int T;
     const uint16_t* vis;
@@ -861,7 +868,8 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
         if (tid == 0) fv = atomicAdd(a.sched_counter, 1);
         const Item I = item_of(a, s_rec);
         bool rec_pending = (w == 0);
-        run_item<true, DROP>(a, Wv, I, 0, rec_pending, fv, nrec, n_items);
+        bf16x8 qf[8];
+        run_item<true, DROP>(a, Wv, I, 0, rec_pending, fv, nrec, n_items, qf);
         int nxt = G + __builtin_amdgcn_readfirstlane(fv);
         if (rec_pending) {
             if (nxt < n_items && lane < ITEM_WORDS) nrec = a.items[(int64_t)nxt * ITEM_WORDS + lane];
@@ -881,26 +889,67 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
 }
 
-// ---- fused kernel: plan in LDS, then attention -------------------------
-// Every workgroup builds the whole plan of the call (fm_lds_plan.h) and runs
-// items g, g + gridDim.x, ... of its longest-first order: one launch for the
-// whole forward of a small problem.
-__shared__ __attribute__((aligned(16))) int32_t s_myrec[LP_MAX_MY][ITEM_WORDS];
-static_assert(LP_TMP_BYTES <= 6 * SLOT_BYTES, "planner temporaries fit in the K/V ring");
-static_assert(LP_MAX_TILES <= VIS_CAP, "visit lists of the whole plan fit");
+// ---- fused kernel: each workgroup plans its own items, then attends ------
+// One launch for the whole forward of a small problem: wave 0 of every
+// workgroup builds the launch-wide slot tables from cu_seqlens and resolves
+// the workgroup's items (fm_own_plan.h); for each item the workgroup loads
+// Q, copies the K/V tile its chunk most likely starts with (the chunk's
+// start when every block of the row is visited) and, while those loads are
+// in flight, derives the row's visit list from the mask vectors; then it
+// runs its chunk.  No workgroup waits for another; split rows are combined
+// by the merge launch that follows.
+}  // namespace fm
+#include "fm_own_plan.h"
+namespace fm {
+__shared__ OwnTables s_own;
 
 __global__ __launch_bounds__(NTH, 2) void fm_fused_bf16_kernel(AttnArgs a) {
+    static_assert(NW == 8 && NTH == 512, "the planner maps eight waves to the bytes of a 64-block window");
     Wave Wv;
-    const LdsPlan P = plan_in_lds<BR, BC>(a, s_kv, s_vis, s_myrec);
-    if (P.status != 0) return;
     wave_setup(a, Wv);
+    const int status = own_setup<BR, BC>(a, s_own);
+    if (blockIdx.x == 0 && Wv.tid == 0) {
+        // header: status, no plan in the workspace (no items and no split
+        // rows listed, so a call with a ready plan on this workspace runs
+        // nothing), the merge table of R q tiles x H heads
+        a.w_hdr[HDR_STATUS] = status;
+        a.w_hdr[HDR_NKB] = 0;
+        a.w_hdr[HDR_NITEMS] = 0;
+        a.w_hdr[HDR_SCHED] = 0;
+        a.w_hdr[HDR_NSLOTS] = 0;
+        a.w_hdr[HDR_NMERGE] = 0;
+        a.w_hdr[HDR_NFUSED] = status ? 0 : s_own.misc[1] * a.H;
+    }
+    if (status != 0) return;
+    const int n_my = __builtin_amdgcn_readfirstlane(s_own.misc[3]);
+    const int n_items = __builtin_amdgcn_readfirstlane(s_own.misc[2]) * a.H;
     bool rec_pending = false;
     int nrec = 0;
-    for (int k = 0; k < P.n_my; ++k) {
-        const Item I = item_of(a, s_myrec[k]);
-        const int vis_off = __builtin_amdgcn_readfirstlane(s_myrec[k][12]);
-        run_item<false, false>(a, Wv, I, vis_off, rec_pending, 0, nrec, P.n_items);
-        item_barrier();   // the ring is free for the next item
+    for (int k = 0; k < n_my; ++k) {
+        auto u = [](int x) { return __builtin_amdgcn_readfirstlane(x); };   // wave-uniform copies
+        const MyItem m = {u(s_own.my[k].b), u(s_own.my[k].qt), u(s_own.my[k].r), u(s_own.my[k].s),
+                          u(s_own.my[k].h), u(s_own.my[k].U)};
+        const int s_b = u(s_own.cu[m.b]), e_b = u(s_own.cu[m.b + 1]);
+        const int r0 = s_b + m.qt * BR;
+        Wv.qrow = r0 + 32 * Wv.w + Wv.n;
+        bf16x8 qf[8];
+        load_q(a, Wv, min(r0 + BR, e_b), (int64_t)m.h * HD, qf);   // in flight during the planning
+        const int pre_kb = guess_first_block(m.U, m.s, a.S);
+        if (pre_kb >= 0) {
+            Item G;
+            G.s_b = s_b; G.e_b = e_b;
+            copy_tile_pair(a, G, Wv, (const char*)a.k + (int64_t)m.h * HD * 2, (const char*)a.v + (int64_t)m.h * HD * 2,
+                           pre_kb);
+        }
+        Item I;
+        int vis_off = 0;
+        if (!own_item<BR, BC, HD>(a, s_own, m, I, vis_off, s_vis, s_wvis, s_wiv)) {
+            __builtin_amdgcn_s_waitcnt(0);   // the guessed copy lands before the ring is reused
+            __syncthreads();                 // every wave is done with the window masks
+            continue;
+        }
+        run_item<false, false>(a, Wv, I, vis_off, rec_pending, 0, nrec, n_items, qf, pre_kb);
+        item_barrier();   // the ring, the visit list and the masks are free for the next item
     }
     __builtin_amdgcn_s_waitcnt(0);
 }
@@ -930,7 +979,7 @@ __global__ __launch_bounds__(MNTH) void fm_merge_bf16_kernel(AttnArgs a) {
         const int nsp = a.merge_list[k * MERGE_WORDS + 4];
         const int slot0 = e0.x, h = e0.y, lr = 32 * w + n;
         const int64_t qrow = (int64_t)e0.z + lr;
-        if (qrow >= e0.w) continue;
+        if (qrow >= e0.w || nsp <= 1) continue;   // rows of one chunk wrote out themselves
         const uint32_t* p0 = (const uint32_t*)a.partial + ((int64_t)slot0 * a.H + h) * PART;
         const int64_t step = (int64_t)a.H * PART;
         const int oi = part_index(w, dt, gp, lane);

@@ -8,7 +8,10 @@
 namespace fm {
 
 // Header words of the workspace (int32 index) and class counts (byte offset).
-enum : int { HDR_STATUS = 0, HDR_NKB = 1, HDR_NITEMS = 2, HDR_SCHED = 3, HDR_NSLOTS = 4, HDR_NMERGE = 5 };
+// HDR_NMERGE counts the planners' split-row list, HDR_NFUSED the fused
+// path's merge table (one entry per q tile and head).
+enum : int { HDR_STATUS = 0, HDR_NKB = 1, HDR_NITEMS = 2, HDR_SCHED = 3, HDR_NSLOTS = 4, HDR_NMERGE = 5,
+             HDR_NFUSED = 6 };
 // Split-row list entry (int32 x MERGE_WORDS): slot of split 0, head, first
 // row, end row (exclusive), number of splits, three zero words.
 constexpr int MERGE_WORDS = 8;
@@ -16,6 +19,11 @@ constexpr int HDR_COUNTS_BYTE = 64;
 constexpr int ITEM_WORDS = 16;  // seq, head, q_tile, kb_begin, kb_end, split_idx, n_splits, cost,
                                 // seq_start, seq_end, kb_base, split0_slot, 0, 0, 0, 0
 constexpr int SLOT_WORDS = 8;   // seq, q_tile, split_idx, n_splits, kb_begin, kb_end, cost, valid
+// Bounds of the fused path's per-workgroup planner (fm_own_plan.h): the host
+// takes the fused path only when they hold.
+constexpr int FUSED_MAX_B = 255;      // sequences
+constexpr int FUSED_MAX_ROWS = 512;   // q tiles over all sequences
+constexpr int FUSED_MAX_MY = 8;       // work items per workgroup
 // Workgroups per sequence of the tile-class launch (each classifies every
 // PLAN_RC-th group of q tiles); class counts are kept per (sequence, group).
 constexpr int PLAN_RC = 16;

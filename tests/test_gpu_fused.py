@@ -1,14 +1,15 @@
-"""GPU tests of the fused path (plan built in LDS by every workgroup of the
-attention launch, items run from a static share; split rows combined in
-split order by a second, merge launch).
+"""GPU tests of the fused path (one attention launch in which every
+workgroup derives its own work items from cu_seqlens and the mask vectors
+of its own q-tile row; split rows combined in split order by a second,
+merge launch).
 
-- the plan the fused launch writes into the workspace equals the oracle's
-  (bit-exact extrema, kb offsets, class counts, work items);
+- the header and merge table the fused launch writes into the workspace:
+  no plan listed, one merge entry per (q tile, head) with the split count of
+  the oracle's work list;
 - out / lse are within the parity bars of the fp64 oracle;
-- the fused path and the plan-in-workspace path give identical bits (same
-  plan, same item code, split merge independent of arrival order);
-- a workspace is reusable across calls and paths (the planned kernel's
-  work counter is back at zero after every call).
+- the fused path and the plan-in-workspace path give identical bits (the
+  same chunks, the same item code, split merge in split order);
+- a workspace is reusable across calls and paths.
 """
 import sys
 
@@ -82,24 +83,42 @@ def compare(w, out, lse, tag):
     assert e_out <= OUT_TOL and e_lse <= LSE_TOL
 
 
-def check_written_plan(pv, w, S, ws, lay):
-    hdr = ws[:256].view(torch.int32).cpu().numpy()
-    counts = ws[64:88].view(torch.int64).cpu().tolist()
+def fused_table(w, S):
+    """The fused path's merge table for workload w, from the documented rule:
+    q tiles in order (sequences in order, q tiles in order); q tile (b, qt)
+    owns ceil(U / S) slots (one when S = 0 or U <= S), U = its key blocks not
+    past the causal diagonal (all of them without the causal flag); its entry
+    r * H + h is (first slot, h, first row, end row, number of splits of the
+    oracle's work list)."""
     kb_off, ext = O.extrema(w.cu_seqlens, w.startend, w.n_vec, w.causal, BC)
     cls = O.classify(w.cu_seqlens, kb_off, ext, w.causal, BR, BC)
-    oitems = O.worklist(cls, w.H, S)
-    assert hdr[0] == 0 and hdr[1] == len(ext) and hdr[2] == len(oitems) and hdr[3] == 0
-    assert counts == O.class_counts(cls).tolist()
-    g = lambda off, n: ws[off:off + 4 * n].view(torch.int32).cpu().numpy()
-    assert np.array_equal(g(lay.off_kb_off, w.B + 1), kb_off)
-    assert np.array_equal(g(lay.off_extrema, 8 * len(ext)).reshape(-1, 8), ext.reshape(-1, 8))
-    items = g(lay.off_items, 16 * len(oitems)).reshape(-1, 16)
-    assert np.array_equal(items[:, :8], oitems)
+    nsplit = {}
+    for it in O.worklist(cls, w.H, S):
+        nsplit[(int(it[0]), int(it[2]))] = int(it[6])
     cu = w.cu_seqlens.astype(np.int64)
-    b = items[:, 0]
-    assert np.array_equal(items[:, 8], cu[b]) and np.array_equal(items[:, 9], cu[b + 1])
-    assert np.array_equal(items[:, 10], kb_off[b]) and np.all(items[:, 12:] == 0)
-    return items
+    rows, slot = [], 0
+    for b in range(w.B):
+        L = int(cu[b + 1] - cu[b])
+        Tc = -(-L // BC)
+        for qt in range(-(-L // BR)):
+            U = min(Tc, -(-min((qt + 1) * BR, L) // BC)) if w.causal else Tc
+            r0 = int(cu[b]) + qt * BR
+            for h in range(w.H):
+                rows.append([slot, h, r0, min(r0 + BR, int(cu[b + 1])), nsplit[(b, qt)], 0, 0, 0])
+            slot += 1 if (S == 0 or U <= S) else -(-U // S)
+    return np.array(rows, np.int64).reshape(-1, 8)
+
+
+def check_header(pv, w, S, ws, lay):
+    """Status 0, no plan listed (items, split-row list), and the merge table."""
+    hdr = ws[:256].view(torch.int32).cpu().numpy()
+    want = fused_table(w, S)
+    assert hdr[0] == 0 and hdr[2] == 0 and hdr[3] == 0 and hdr[5] == 0
+    if S == 0:
+        return
+    assert hdr[6] == len(want)
+    got = ws[lay.off_merge:lay.off_merge + 32 * len(want)].view(torch.int32).view(-1, 8).cpu().numpy()
+    assert np.array_equal(got.astype(np.int64), want)
 
 
 def test_fused_path_selection(pv):
@@ -111,6 +130,7 @@ def test_fused_path_selection(pv):
     assert not pv.fused_path(w.N, w.B, w.H, 32, torch.float32, w.n_vec, w.causal)
     assert not pv.fused_path(16384, 20, 32, 128, bf, 1, True)          # SFT packing: too big
     assert not pv.fused_path(4096, 300, 1, 128, bf, 1, True)           # too many sequences
+    assert not pv.fused_path(20000, 3, 1, 128, bf, 1, True)            # more than 16384 tokens
 
 
 @pytest.mark.parametrize("S", [-1, 0, 3, 2, 1])
@@ -123,7 +143,7 @@ def test_fused_cfg2(pv, S):
         pytest.skip("split bound beyond the fused path")
     lay, ws = fused_ws(pv, w, S_eff)
     out, lse, _ = run_fused(pv, w, S_eff, ws)
-    check_written_plan(pv, w, S_eff, ws, lay)
+    check_header(pv, w, S_eff, ws, lay)
     compare(w, out, lse, "fused cfg2 S=%d" % S_eff)
     o2, l2 = run_planned(pv, w, S_eff)
     assert torch.equal(out, o2) and torch.equal(lse, l2)
@@ -139,7 +159,7 @@ def test_fused_random(pv, seed):
     say("fused random", w.name, "N=%d B=%d H=%d causal=%d n_vec=%d S=%d" % (w.N, w.B, w.H, w.causal, w.n_vec, S))
     lay, ws = fused_ws(pv, w, S)
     out, lse, _ = run_fused(pv, w, S, ws)
-    check_written_plan(pv, w, S, ws, lay)
+    check_header(pv, w, S, ws, lay)
     compare(w, out, lse, "fused random")
     o2, l2 = run_planned(pv, w, S)
     assert torch.equal(out, o2) and torch.equal(lse, l2)
@@ -154,14 +174,16 @@ def test_fused_reduced_configs(pv, k, N, H):
         say("fused reduced cfg", k, w.N, w.H, w.B, "S", S)
         lay, ws = fused_ws(pv, w, S)
         out, lse, _ = run_fused(pv, w, S, ws)
-        check_written_plan(pv, w, S, ws, lay)
+        check_header(pv, w, S, ws, lay)
         compare(w, out, lse, "fused cfg%d S=%d" % (k, S))
 
 
 def test_workspace_reuse_across_paths(pv):
     """One workspace serves fused, planned and fused calls again with
-    identical results; both planners list the same split rows for the
-    merge (one entry per split row and head)."""
+    identical results: the planner lists the oracle's split rows for the
+    merge (one entry per split row and head), the fused call keeps its own
+    table; a ready-plan call right after a fused call finds no plan and
+    writes nothing."""
     w = W.make_config(2)
     S = 2
     lay, ws = fused_ws(pv, w, S)
@@ -182,8 +204,14 @@ def test_workspace_reuse_across_paths(pv):
         return sorted(got)
 
     o1, l1, _ = run_fused(pv, w, S, ws)
-    assert merge_rows() == want
+    check_header(pv, w, S, ws, lay)
     q, k, v, cu, sv = dev_inputs(w)
+    out = torch.full_like(o1, 3.0)
+    lse = torch.full_like(l1, 3.0)
+    pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), max_kb_per_item=S, workspace=ws,
+                flags=pv.FM_FLAG_PLAN_READY, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0).item() and torch.all(lse == 3.0).item()
     pv.build_plan_into(pv.Plan(ws, lay, w.N, w.B, w.H, w.D, torch.bfloat16, w.causal, w.n_vec, S), cu, sv)
     assert merge_rows() == want
     o2, l2 = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), max_kb_per_item=S,
