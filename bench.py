@@ -2,23 +2,31 @@
 
 One step = one pass of the whole hot path over the workload, inputs already
 resident in HBM:  block extrema (N2) -> tile classes + work list (N3) ->
-attention (N4, plus the split merge when rows are split).  The metric is
-effective TFLOP/s: unmasked FLOPs (4 * D per attending (query, key, head)
-triple) divided by the time of one step.
+attention (N4, plus the split merge when rows are split).  Small problems
+take the fused path (one attention launch in which every workgroup plans its
+own items, then the merge); the others the planning launches and the
+plan-reading attention launch.  The metric is effective TFLOP/s: attending
+(query, key, head) triples times 4 D flops, divided by the time of one step.
 
-Timing: W untimed warm-up steps, then K steps between two HIP events on
-the library's stream, with nothing else queued between the steps.  A spin
-kernel is queued first so the host can enqueue all K steps ahead and the
-GPU runs them back to back.  A second pass of K steps then brackets every
-attention launch with two more events; their mean elapsed time is the
-dominant kernel's average launch duration for the roofline figure.  The
-events stay out of the first pass because an event recorded between two
-launches keeps the GPU from starting the next launch while the previous one
-drains (several microseconds per step at the small configurations).
-The oracle (fp64 NumPy, the parity reference) is timed on the host cores
-on a bounded sample of the same workload as the CPU baseline.  For bf16
-workloads the line also reports, for information, the backward (dq, dk,
-dv) and the fused q/k rotary embedding on the same inputs.
+Timing (K = --steps, W = --warmup):
+  1. W untimed steps, then K steps back to back between two HIP events on
+     the library's stream (a spin kernel queued first lets the host enqueue
+     all K ahead): value and ms_per_step.
+  2. K steps, each between its own pair of events: the median and p10/p90
+     of one step (an event between launches keeps the next launch from
+     starting while the previous one drains, so these run a little longer).
+  3. Up to 20 steps, each after a 512 MiB write that evicts the caches: the
+     cold-cache step.
+  4. The dominant launches alone, K back to back between two events: the
+     attention kernel (+ merge) of the step on the fused path, the
+     plan-reading attention launches with a plan built once on the planned
+     path: roofline.achieved.  roofline.profiled and roofline.traffic come
+     from the rocprofv3 runs summarised in profiles/ while the forward
+     sources are the ones they were taken from.
+The oracle (fp64 NumPy, the parity reference) is timed on the host cores on
+a bounded sample of the same workload as the CPU baseline.  For bf16
+workloads the line also reports, for information, the backward (dq, dk, dv)
+and the fused q/k rotary embedding on the same inputs.
 """
 from __future__ import annotations
 
@@ -48,6 +56,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload config id (1..5); 2 is the headline")
     ap.add_argument("--split", type=int, default=-1, help="max key blocks per item (-1 auto, 0 none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="leave out the backward and rotary-embedding legs")
+    ap.add_argument("--seeds", type=int, default=1, help="measure this many seeds (seed, seed + 1, ...), one line each")
     ap.add_argument("--planned", action="store_true",
                     help="time the planning launches + plan-reading attention even where the fused path applies")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on oracle CPU time")
@@ -90,53 +100,143 @@ def source_hash():
     return h.hexdigest()
 
 
-def stored_traffic(key):
-    """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs summarised in profiles/traffic.json (scaled by the copy
-    calibration recorded there), or None when absent or taken from other
-    sources."""
+def stored_profile(key):
+    """Per-launch figures of the dominant kernels from the rocprofv3 runs
+    summarised in profiles/ (profiles/roofline.json): HBM bytes from the
+    FETCH_SIZE / WRITE_SIZE runs (scaled by a plain-copy calibration) and the
+    kernel-trace average durations, or None when absent or taken from other
+    sources than the current ones."""
     try:
-        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        with open(os.path.join(ROOT, "profiles", "roofline.json")) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
     e = d.get("entries", {}).get(key)
     if not e or e.get("src_sha256") != source_hash():
         return None
-    return e.get("bytes_per_launch")
+    return e
 
 
-def cpu_baseline(w, flops, budget_s):
-    """Times the oracle on the host cores.  Sample: whole sequences of the
-    workload for all heads, taken in order until the budget is spent (the
-    whole workload when it fits)."""
-    import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
-    cu = w.cu_seqlens.astype(np.int64)
-    done_flops, t_total, seqs = 0, 0.0, 0
-    t_start = time.perf_counter()
-    for b in range(w.B):
-        s, e = int(cu[b]), int(cu[b + 1])
+def count_pairs(w, device=None):
+    """Attending (query, key) pairs per head of workload w: pairs of one
+    sequence whose key column does not hide the query row.  Column j hides
+    rows [LTS_j, LTE_j) and, without the causal flag, [UTS_j, UTE_j); the
+    causal flag hides keys after the query; absent stored vectors take the
+    defaults LTS = UTS = 0, LTE = UTE = N (FlashMask article, section 2).
+    Evaluated densely per sequence in row chunks with torch (on the GPU when
+    there is one); the effective FLOPs of the metric are 4 D H times this."""
+    import torch
+    dev = device or (torch.device("cuda:0") if torch.cuda.is_available() else torch.device("cpu"))
+    N = w.N
+    sv = torch.from_numpy(np.asarray(w.startend, np.int64)).to(dev)
+    full = torch.full((N,), N, dtype=torch.int64, device=dev)
+    zero = torch.zeros(N, dtype=torch.int64, device=dev)
+    if w.causal:
+        lts, lte, uts, ute = sv[0], (sv[1] if w.n_vec == 2 else full), zero, zero
+    elif w.n_vec == 2:
+        lts, lte, uts, ute = sv[0], full, zero, sv[1]
+    else:
+        lts, lte, uts, ute = sv[0], sv[1], sv[2], sv[3]
+    cu = [int(x) for x in w.cu_seqlens]
+    total = 0
+    for b in range(len(cu) - 1):
+        s, e = cu[b], cu[b + 1]
         if e <= s:
             continue
-        sv = w.startend[:, s:e].astype(np.int64) - s
-        t0 = time.perf_counter()
-        O.attention(w.q[s:e], w.k[s:e], w.v[s:e], np.array([0, e - s]), sv, w.n_vec, w.causal, w.scale)
-        t_total += time.perf_counter() - t0
-        pairs = O.unmasked_pairs(np.array([0, e - s]), sv, w.n_vec, w.causal)
-        done_flops += O.effective_flops(pairs, w.H, w.D)
-        seqs += 1
-        if time.perf_counter() - t_start > budget_s:
-            break
-    return {"value": done_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": "%d of %d sequences (all %d heads), %.3g effective GFLOP, %.2f s fp64 NumPy" % (
-                seqs, w.B, w.H, done_flops / 1e9, t_total),
-            "host_cpus": len(os.sched_getaffinity(0))}
+        j = torch.arange(s, e, device=dev)[None, :]
+        for r0 in range(s, e, 2048):
+            i = torch.arange(r0, min(r0 + 2048, e), device=dev)[:, None]
+            hid = (lts[j] <= i) & (i < lte[j])
+            if w.causal:
+                hid |= j > i
+            else:
+                hid |= (uts[j] <= i) & (i < ute[j])
+            total += int((~hid).sum().item())
+    return total
+
+
+def host_info():
+    """CPU model, usable cores and the NumPy BLAS behind the oracle."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = "%s %s" % (libs[0].get("internal_api"), libs[0].get("version"))
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "host_cpus": len(os.sched_getaffinity(0)), "blas": blas}
+
+
+_POOL_W = None
+
+
+def _oracle_task(task):
+    """One (sequence, head) of the oracle, rebased to the sequence (pairs of
+    different sequences never attend): seconds and effective FLOPs."""
+    import oracle as O
+    w = _POOL_W
+    s, e, h = task
+    sv = w.startend[:, s:e].astype(np.int64) - s
+    sl = (slice(s, e), slice(h, h + 1))
+    t0 = time.perf_counter()
+    O.attention(w.q[sl], w.k[sl], w.v[sl], np.array([0, e - s]), sv, w.n_vec, w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    pairs = O.unmasked_pairs(np.array([0, e - s]), sv, w.n_vec, w.causal)
+    return dt, O.effective_flops(pairs, 1, w.D)
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle (fp64 NumPy) on the host cores: a process pool of C
+    workers (C = the usable cores, at most 16), one BLAS thread each, over
+    (sequence, head) pieces of the workload, longest sequences first, until
+    about budget_s seconds of wall time are spent (the whole workload when it
+    fits).  Throughput = effective FLOPs of the pieces done / wall time."""
+    import multiprocessing as mp
+    global _POOL_W
+    info = host_info()
+    C = max(1, min(16, info["host_cpus"]))
+    cu = [int(x) for x in w.cu_seqlens]
+    tasks = sorted(((cu[b], cu[b + 1], h) for b in range(len(cu) - 1) if cu[b + 1] > cu[b] for h in range(w.H)),
+                   key=lambda t: -(t[1] - t[0]))
+    _POOL_W = w
+    old = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in old:
+        os.environ[k] = "1"
+    done_flops, pieces = 0, 0
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            ctx = mp.get_context("fork")
+            with ctx.Pool(C) as pool:
+                t0 = time.perf_counter()
+                for dt, fl in pool.imap_unordered(_oracle_task, tasks, chunksize=1):
+                    done_flops += fl
+                    pieces += 1
+                    if time.perf_counter() - t0 > budget_s:
+                        pool.terminate()
+                        break
+                wall = time.perf_counter() - t0
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    res = {"value": done_flops / wall / 1e12, "unit": "TFLOP/s", "cores": C, "kind": "oracle",
+           "sample": "%d of %d (sequence, head) pieces, %.3g effective GFLOP, %.2f s wall, fp64 NumPy, "
+                     "process pool of %d workers x 1 BLAS thread" % (pieces, len(tasks), done_flops / 1e9, wall, C)}
+    res.update(info)
+    return res
 
 
 def preprocess_sweep(args):
@@ -262,33 +362,35 @@ def time_calls(fn, K):
 
 
 def sparsity_sweep(args):
-    """Step time against unmasked work on the shape of the varlen workload
-    (N = 4352, H = 2, D = 128, causal documents): the documents are resized
-    (k equal documents, k = 1 .. 34, plus the [128, 128, 4096] mix), which
-    moves the unmasked fraction 1 - rho of the N x N score matrix; the
-    pages expect latency linear in it."""
+    """Step time against unmasked work at the shape of workload --config
+    (the varlen workload: N = 4352, H = 2; the SFT packing: N = 16384,
+    H = 32; D = 128, causal documents): the documents are resized (k equal
+    documents, plus the workload's own length mix), which moves the unmasked
+    fraction 1 - rho of the N x N score matrix; the FlashMask article (§4.3)
+    expects latency linear in it."""
     import workloads as W
-    import oracle as O
-    N = 4352
-    cases = [[N // k] * (k - 1) + [N - (N // k) * (k - 1)] for k in (1, 2, 4, 8, 17, 34)] + [[128, 128, 4096]]
+    base = W.make_config(args.config, seed=args.seed, with_qkv=False)
+    N, H = base.N, base.H
+    ks = (1, 2, 4, 8, 17, 34) if N <= 8192 else (1, 2, 4, 8, 16, 32, 64, 128)
+    cases = [[N // k] * (k - 1) + [N - (N // k) * (k - 1)] for k in ks] + [[int(x) for x in base.lengths]]
     rows = []
     for lens in cases:
-        w = W.document_workload(lens, H=2, D=128, seed=1002)
+        w = W.document_workload(lens, H=H, D=128, seed=base.meta["seed"])
         st = make_setup(w, args)
         for _ in range(args.warmup):
             st["step"]()
         ms, _, _ = time_calls(st["step"], args.steps)
-        pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
+        pairs = count_pairs(w)
         rows.append({"documents": len(lens), "lengths": lens[:4] + (["..."] if len(lens) > 4 else []),
                      "unmasked_fraction": round(pairs / float(N * N), 5), "unmasked_pairs_per_head": int(pairs),
                      "path": "fused" if st["fused"] else "planned", "max_kb_per_item": st["S"],
                      "us_per_step": round(ms * 1e3, 2),
-                     "effective_TFLOP_s": round(O.effective_flops(pairs, w.H, w.D) / (ms * 1e-3) / 1e12, 2)})
+                     "effective_TFLOP_s": round(4 * w.D * w.H * pairs / (ms * 1e-3) / 1e12, 2)})
     x = np.array([r["unmasked_fraction"] for r in rows])
     y = np.array([r["us_per_step"] for r in rows])
     slope, icpt = np.polyfit(x, y, 1)
     r2 = 1.0 - float(np.sum((y - (slope * x + icpt)) ** 2)) / float(np.sum((y - y.mean()) ** 2))
-    print(json.dumps({"metric": "step latency against unmasked fraction (varlen workload shape)", "unit": "us",
+    print(json.dumps({"metric": "step latency against unmasked fraction (shape of %s)" % base.name, "unit": "us",
                       "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
                       "fit": {"us_per_unit_fraction": round(float(slope), 2), "intercept_us": round(float(icpt), 2),
                               "r2": round(r2, 4)},
@@ -307,10 +409,9 @@ def packing_sweep(args):
     every case; `computed_pairs_per_head` is what the layout leaves
     unmasked."""
     import workloads as W
-    import oracle as O
     base = W.make_config(args.config, seed=args.seed)
-    useful = O.unmasked_pairs(base.cu_seqlens, base.startend, base.n_vec, base.causal)
-    flops = O.effective_flops(useful, base.H, base.D)
+    useful = count_pairs(base)
+    flops = 4 * base.D * base.H * useful
     rows = []
     for kind in [x for x in args.packings.split(",") if x]:
         w = W.packed_as(base, kind)
@@ -321,7 +422,7 @@ def packing_sweep(args):
         st["attn_with_plan"]()
         ms_r, _, _ = time_calls(st["attn_with_plan"], args.steps)
         hdr = st["hdr"]()
-        pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
+        pairs = count_pairs(w)
         rows.append({"packing": kind, "tokens_stored": w.N, "sequences": w.B, "n_vec": w.n_vec,
                      "path": "fused" if st["fused"] else "planned", "max_kb_per_item": st["S"],
                      "n_items": hdr["n_items"], "class_counts": hdr["class_counts"],
@@ -345,7 +446,6 @@ def backward_bench(args):
     which is not counted."""
     import torch
     import workloads as W
-    import oracle as O
     import packed_varlen_masked_amd as pv
     w = W.make_config(args.config, seed=args.seed)
     if w.dtype != W.BF16:
@@ -358,16 +458,17 @@ def backward_bench(args):
         (w.N, w.H, w.D), dtype=np.float32)).to(torch.bfloat16).to(dev)
     ws = torch.zeros(pv.bwd_workspace_size(w.N, w.B, w.H, w.D, torch.bfloat16), dtype=torch.uint8, device=dev)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    side = torch.cuda.Stream()   # the dQ launches overlap dK/dV on it (fm_attn_bwd_streams)
 
     def step():
         pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale), workspace=ws,
-                    dq=dq, dk=dk, dv=dv)
+                    dq=dq, dk=dk, dv=dv, dq_stream=side)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     ms, host_ms, ahead = time_calls(step, args.steps)
-    pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
-    flops = 2.5 * O.effective_flops(pairs, w.H, w.D)
+    pairs = count_pairs(w)
+    flops = 2.5 * 4 * w.D * w.H * pairs
     value = flops / (ms * 1e-3) / 1e12
     print(json.dumps({"metric": "backward effective TFLOP/s (5 products per unmasked pair) + % bf16 MFMA peak",
                       "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -387,7 +488,6 @@ def dropout_bench(args):
     inputs; the useful work is counted as without dropout."""
     import torch
     import workloads as W
-    import oracle as O
     import packed_varlen_masked_amd as pv
     w = W.make_config(args.config, seed=args.seed)
     if w.dtype != W.BF16:
@@ -399,8 +499,8 @@ def dropout_bench(args):
     g = torch.from_numpy(np.random.default_rng(w.meta["seed"] + 2).standard_normal(
         (w.N, w.H, w.D), dtype=np.float32)).to(torch.bfloat16).to(dev)
     wsb = torch.zeros(pv.bwd_workspace_size(w.N, w.B, w.H, w.D, torch.bfloat16), dtype=torch.uint8, device=dev)
-    pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
-    flops = O.effective_flops(pairs, w.H, w.D)
+    pairs = count_pairs(w)
+    flops = 4 * w.D * w.H * pairs
     res = {}
     for p in (0.0, args.dropout):
         kw = dict(dropout_p=p, seed=0x5EED, offset=1) if p > 0 else {}
@@ -491,10 +591,11 @@ def extra_legs(w, st, K, flops):
         (w.N, w.H, w.D), dtype=np.float32)).to(torch.bfloat16).to(q.device)
     ws = torch.zeros(pv.bwd_workspace_size(w.N, w.B, w.H, w.D, torch.bfloat16), dtype=torch.uint8, device=q.device)
     grads = [torch.empty_like(q) for _ in range(3)]
+    side = torch.cuda.Stream()   # the dQ launches overlap dK/dV on it (fm_attn_bwd_streams)
 
     def bwd():
         pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale), workspace=ws,
-                    dq=grads[0], dk=grads[1], dv=grads[2])
+                    dq=grads[0], dk=grads[1], dv=grads[2], dq_stream=side)
     for _ in range(5):
         bwd()
     ms_b, _, _ = time_calls(bwd, K)
@@ -508,8 +609,8 @@ def extra_legs(w, st, K, flops):
         rope()
     ms_r, _, _ = time_calls(rope, K)
     rope_bytes = 2 * 2 * w.N * w.H * w.D * 2 + w.N * w.D * 4
-    return {"backward": {"what": "fm_attn_bwd (dq, dk, dv) on the same inputs; useful work = 5 products per "
-                                 "unmasked pair = 2.5 x the forward's effective FLOPs",
+    return {"backward": {"what": "fm_attn_bwd_streams (dq, dk, dv; dQ on a second stream) on the same inputs; "
+                                 "useful work = 5 products per unmasked pair = 2.5 x the forward's effective FLOPs",
                          "ms_per_call": round(ms_b, 6),
                          "effective_TFLOP_s": round(2.5 * flops / (ms_b * 1e-3) / 1e12, 3)},
             "rope": {"what": "fm_rope_qk on the workload's q and k in place (mean of a forward and an inverse call)",
@@ -543,15 +644,31 @@ def main():
         return
     import torch
     import workloads as W
+    seeds = [args.seed if args.seed is not None else 1000 + args.config]
+    seeds += [seeds[0] + i for i in range(1, max(1, args.seeds))]
+    for sd in seeds:
+        res = measure(W.make_config(args.config, seed=sd), args)
+        print(json.dumps(res), flush=True)
 
-    w = W.make_config(args.config, seed=args.seed)
+
+def measure(w, args):
+    """The bench line of workload w (see the module docstring)."""
+    import torch
+    import workloads as W
+    import packed_varlen_masked_amd as pv
     st = make_setup(w, args)
     dt, dev, step, plan, S, fused = st["dt"], st["dev"], st["step"], st["plan"], st["S"], st["fused"]
 
-    # algorithmic work: closed form for causal documents, else the oracle's count
-    import oracle as O
-    pairs = O.unmasked_pairs(w.cu_seqlens, w.startend, w.n_vec, w.causal)
-    flops = O.effective_flops(pairs, w.H, w.D)
+    # algorithmic work: attending pairs per head (the bench's own count from
+    # the interval vectors), 4 D flops per pair and head
+    pairs = count_pairs(w)
+    flops = 4 * w.D * w.H * pairs
+    hdr = st["hdr"]()
+    Br, Bc = plan.layout.block_q, plan.layout.block_k
+    # tiles the kernels visit: PARTIAL + UNMASKED of the library's own plan,
+    # each a full Br x Bc MFMA tile for every head
+    visited = int(hdr["class_counts"][1] + hdr["class_counts"][2])
+    mfma_flops = 4 * w.D * w.H * visited * Br * Bc
 
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
@@ -564,61 +681,91 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
 
-    # pass 1: the timed steps
+    # pass 1: the timed steps, back to back between two events
     ms_step, host_ms, host_ahead = time_calls(step, K)
-    # pass 2: the same steps, events around every attention launch
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    # pass 2: every step between its own two events (the median and spread of
+    # one step; an event between launches keeps the next launch from starting
+    # while the previous one drains, so these run a little longer than pass 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     spin()
-    for i in range(K):
-        step(ev_a[i], ev_b[i])
+    for a_, b_ in ev:
+        a_.record()
+        step()
+        b_.record()
     torch.cuda.synchronize()
-    attn_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
-    attn_avg = float(attn_ms.mean())
-    # pass 3: attention alone with the plan already built (a plan reused
-    # across layers that share the mask)
+    one = np.array([a_.elapsed_time(b_) for a_, b_ in ev])
+    # pass 3: cold caches: a 512 MiB write (twice the 256 MiB last-level
+    # cache) before each of up to 20 steps
+    n_cold = min(K, 20)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+    for a_, b_ in evc:
+        flush.fill_(1)
+        a_.record()
+        step()
+        b_.record()
+    torch.cuda.synchronize()
+    cold = np.array([a_.elapsed_time(b_) for a_, b_ in evc])
+    del flush
+    # pass 4: the dominant launches (the attention kernel and, when rows are
+    # split, the merge) back to back: on the fused path they are the whole
+    # step; on the planned path the attention launches reading a plan built
+    # once (the per-layer cost when layers share a mask)
     st["attn_with_plan"]()
     ms_reuse, _, _ = time_calls(st["attn_with_plan"], K)
+    ms_kernel = ms_step if fused else ms_reuse
     value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (attn_avg * 1e-3) / 1e12
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
 
-    hdr = st["hdr"]()
     path = "fused" if fused else "planned"
-    kernel = ("fm_fused_bf16_kernel" if fused else "fm_attn_bf16_kernel") + (" + fm_merge_bf16_kernel" if S > 0 else "")
-    traffic = stored_traffic("%s:%s:S%d" % (w.name, path, S))
+    kernels = (["fm_fused_bf16_kernel"] if fused else ["fm_attn_bf16_kernel<false>"]) + (
+        ["fm_merge_bf16_kernel"] if S > 0 else [])
+    prof = stored_profile("%s:%s:S%d" % (w.name, path, S))
     esz = 2 if dt == torch.bfloat16 else 4
     algo_bytes = 4 * w.N * w.H * w.D * esz + 4 * w.N * w.H   # q, k, v read once, out and lse written
+    roof = {"bound": "mfma", "kernel": " + ".join(kernels),
+            "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": prof.get("bytes_per_launch") if prof else None,
+            "algorithmic_bytes": int(algo_bytes),
+            "avg_launch_ms": round(ms_kernel, 6),
+            "duration_from": "HIP events around K back-to-back calls of the launch(es) on the library's stream"}
+    if prof and prof.get("kernel_avg_us"):
+        us = float(sum(prof["kernel_avg_us"].values()))
+        roof["profiled"] = {"avg_us": round(us, 3), "per_kernel_avg_us": prof["kernel_avg_us"],
+                            "frac": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                            "summary": prof.get("summary")}
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
         "data": "synthetic (seeded N(0,1) q/k/v, page-derived lengths and masks)",
         "config": {"workload": w.name, "seed": w.meta["seed"], "N": w.N, "B": w.B, "H": w.H, "D": w.D,
                    "lengths": [int(x) for x in w.lengths][:16], "causal": bool(w.causal),
-                   "n_vec": w.n_vec, "block_q": plan.layout.block_q, "block_k": plan.layout.block_k,
+                   "n_vec": w.n_vec, "block_q": Br, "block_k": Bc,
                    "max_kb_per_item": S, "n_items": hdr["n_items"],
                    "class_counts": hdr["class_counts"], "unmasked_pairs_per_head": int(pairs),
                    "effective_gflop": round(flops / 1e9, 4)},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "timing": {"host_enqueue_ms_per_step": round(host_ms, 4), "host_ran_ahead": host_ahead,
-                   "kernel_duration": "second pass of the same K steps, HIP events around each attention launch"},
+        "visited_tile_overhead": round((mfma_flops - flops) / flops, 4) if flops else None,
+        "step_ms": {"back_to_back_mean": round(ms_step, 6),
+                    "one_step_p10_p50_p90": [round(float(x), 6) for x in np.percentile(one, [10, 50, 90])],
+                    "cold_cache_p10_p50_p90": [round(float(x), 6) for x in np.percentile(cold, [10, 50, 90])],
+                    "cold_cache": "512 MiB written before each of %d steps" % n_cold},
+        "timing": {"host_enqueue_ms_per_step": round(host_ms, 4), "host_ran_ahead": host_ahead},
         "path": path,
-        "roofline": {"bound": "mfma", "kernel": kernel,
-                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "algorithmic_bytes": int(algo_bytes),
-                     "avg_launch_ms": round(attn_avg, 6),
-                     "p10_p50_p90_ms": [round(float(x), 6) for x in np.percentile(attn_ms, [10, 50, 90])]},
+        "roofline": roof,
         "reused_plan": {"what": "attention launches alone, plan built once (fm_attn_bf16_kernel%s)" % (
                             " + fm_merge_bf16_kernel" if S > 0 else ""),
                         "ms_per_call": round(ms_reuse, 6),
                         "effective_TFLOP_s": round(flops / (ms_reuse * 1e-3) / 1e12, 3)},
     }
-    if dt == torch.bfloat16:
+    if dt == torch.bfloat16 and not args.no_extra:
         res.update(extra_legs(w, st, K, flops))
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, flops, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    return res
 
 
 if __name__ == "__main__":

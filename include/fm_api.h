@@ -381,19 +381,34 @@ size_t fm_bwd_workspace_size(int64_t N, int B, int H, int head_dim, int dtype);
  * q tiles of a key tile and the key blocks of a query tile are cut into
  * chunks (separate workgroups, fp32 partials) and two more launches sum
  * them in chunk order.  The chunking depends on the sizes only: the same
- * inputs give the same bits on every run and device.
- * Streams: after Delta, the dQ launches run on a second stream the library
- * creates once per device (default priority), forked from `stream` and
- * joined back into it with events, so that they can overlap the dK/dV
- * launches; everything the call enqueues is ordered before whatever is
- * enqueued on `stream` afterwards, as with a single stream (and a graph
- * captured from `stream` takes the fork and join with it).
+ * inputs give the same bits on every run and device.  Everything runs on
+ * `stream` (fm_attn_bwd_streams lets the dQ launches overlap the dK/dV ones
+ * on a second stream of the caller's).
  */
 int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                 const float* softmax_lse, int dtype, int64_t N, int H, int D,
                 const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
                 float scale, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                 hipStream_t stream);
+
+/*
+ * fm_attn_bwd with the dQ launches on a second stream of the caller's
+ * (same arguments and results, the same bits): after Delta the call
+ * records `fork` on `stream`, makes `dq_stream` wait for it, enqueues the dQ
+ * launches on `dq_stream` and the dK/dV launches on `stream`, then records
+ * `join` on `dq_stream` and makes `stream` wait for it.  Everything the call
+ * enqueues is thus ordered before whatever is enqueued on `stream`
+ * afterwards, as with one stream, and on problems where neither launch
+ * fills the chip the two run side by side.  The caller creates and owns
+ * both streams and both events (hipEventDisableTiming is enough); calls that
+ * share the events or dq_stream must be ordered by the caller.  dq_stream
+ * must differ from `stream`; FM_E_INVAL otherwise or when an event is null.
+ */
+int fm_attn_bwd_streams(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* softmax_lse, int dtype, int64_t N, int H, int D,
+                        const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
+                        float scale, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                        hipStream_t stream, hipStream_t dq_stream, hipEvent_t fork, hipEvent_t join);
 
 /*
  * fm_attn_bwd for a forward run with fm_attn_fwd_dropout: the same

@@ -650,8 +650,10 @@ static int attn_bwd_impl(const void* q, const void* k, const void* v, const void
                   const float* softmax_lse, int dtype, int64_t N, int H, int D, const int32_t* cu_seqlens,
                   int B, const int32_t* startend, int n_vec, int causal, float scale, void* dq, void* dk,
                   void* dv, void* workspace, size_t ws_bytes, float dropout_p, uint64_t seed, uint64_t offset,
-                  hipStream_t stream) {
+                  hipStream_t stream, hipStream_t dq_stream, hipEvent_t fork, hipEvent_t join) {
     int rc = check_sizes(N, B, H);
+    if (dq_stream && (!fork || !join || dq_stream == stream))
+        return fail(FM_E_INVAL, "a dQ stream needs two events and must differ from the stream");
     if (rc) return rc;
     int drop_t = 0;
     float drop_ks = 1.f;
@@ -691,7 +693,7 @@ static int attn_bwd_impl(const void* q, const void* k, const void* v, const void
     a.call_id = next_call_id();
     a.drop_t = drop_t; a.drop_ks = drop_ks;
     a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32); a.offset = (uint32_t)offset;
-    if ((rc = hip_check(fm::launch_bwd_bf16(a, L.kb_cap, stream), "backward launch"))) return rc;
+    if ((rc = hip_check(fm::launch_bwd_bf16(a, L.kb_cap, stream, dq_stream, fork, join), "backward launch"))) return rc;
     return ok();
 }
 
@@ -700,7 +702,17 @@ int fm_attn_bwd(const void* q, const void* k, const void* v, const void* out, co
                 int B, const int32_t* startend, int n_vec, int causal, float scale, void* dq, void* dk,
                 void* dv, void* workspace, size_t ws_bytes, hipStream_t stream) {
     return attn_bwd_impl(q, k, v, out, dout, softmax_lse, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal,
-                         scale, dq, dk, dv, workspace, ws_bytes, 0.f, 0, 0, stream);
+                         scale, dq, dk, dv, workspace, ws_bytes, 0.f, 0, 0, stream, nullptr, nullptr, nullptr);
+}
+
+int fm_attn_bwd_streams(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* softmax_lse, int dtype, int64_t N, int H, int D, const int32_t* cu_seqlens,
+                        int B, const int32_t* startend, int n_vec, int causal, float scale, void* dq, void* dk,
+                        void* dv, void* workspace, size_t ws_bytes, hipStream_t stream, hipStream_t dq_stream,
+                        hipEvent_t fork, hipEvent_t join) {
+    if (!dq_stream) return fail(FM_E_INVAL, "null dQ stream (use fm_attn_bwd for one stream)");
+    return attn_bwd_impl(q, k, v, out, dout, softmax_lse, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal,
+                         scale, dq, dk, dv, workspace, ws_bytes, 0.f, 0, 0, stream, dq_stream, fork, join);
 }
 
 int fm_attn_bwd_dropout(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -709,7 +721,8 @@ int fm_attn_bwd_dropout(const void* q, const void* k, const void* v, const void*
                         void* dv, void* workspace, size_t ws_bytes, float dropout_p, uint64_t seed,
                         uint64_t offset, hipStream_t stream) {
     return attn_bwd_impl(q, k, v, out, dout, softmax_lse, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal,
-                         scale, dq, dk, dv, workspace, ws_bytes, dropout_p, seed, offset, stream);
+                         scale, dq, dk, dv, workspace, ws_bytes, dropout_p, seed, offset, stream, nullptr, nullptr,
+                         nullptr);
 }
 
 int fm_rope_qk(void* q, void* k, int dtype, int64_t N, int Hq, int Hk, int head_dim, const int32_t* cu_seqlens,

@@ -35,7 +35,6 @@
 //     sum them in chunk order.
 //   * every output element is written by exactly one workgroup, and chunk
 //     sums run in a fixed order: the same inputs give the same bits.
-#include <mutex>
 
 #include "fm_common.hpp"
 #include "fm_internal.h"
@@ -756,35 +755,6 @@ __global__ __launch_bounds__(NTQ) void fm_bwd_dq_reduce_kernel(BwdArgs a) {
 }  // namespace bwd
 
 namespace {
-// The dK/dV and dQ launches (and their reduces) are independent once Delta
-// is written, so dQ runs on a second stream of the library's, forked from
-// and joined back into the caller's stream with events: on small problems,
-// where neither launch fills the chip, the two run side by side.  One
-// side stream and event pair per device; the fork/join is enqueued under a
-// lock so that concurrent callers cannot interleave their event records.
-struct SideStream {
-    hipStream_t st = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    bool ok = false;
-};
-constexpr int MAX_DEV = 64;
-SideStream g_side[MAX_DEV];
-std::mutex g_side_mu;
-
-SideStream* side_for_current_device() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return nullptr;
-    SideStream& ss = g_side[dev];
-    if (!ss.ok) {
-        if (hipStreamCreateWithFlags(&ss.st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-            return nullptr;
-        ss.ok = true;
-    }
-    return &ss;
-}
-
 hipError_t launch_dq_part(const BwdArgs& a, const dim3& grid, const dim3& rgrid, hipStream_t s) {
     if (a.drop_t > 0) hipLaunchKernelGGL(bwd::fm_bwd_dq_kernel<true>, grid, dim3(bwd::NTQ), 0, s, a);
     else hipLaunchKernelGGL(bwd::fm_bwd_dq_kernel<false>, grid, dim3(bwd::NTQ), 0, s, a);
@@ -803,7 +773,14 @@ hipError_t launch_dkdv_part(const BwdArgs& a, const dim3& grid, const dim3& rgri
 }
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s) {
+// Delta, then the dK/dV and dQ launches (and their reduces), which are
+// independent of each other once Delta is written.  With a caller's second
+// stream s_dq (and the caller's two events), the dQ launches are forked onto
+// it after Delta and joined back into s, so that on problems where neither
+// launch fills the chip the two run side by side; without one, everything
+// runs on s, dK/dV first.
+hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s, hipStream_t s_dq, hipEvent_t fork,
+                           hipEvent_t join) {
     const int64_t nh = a.N * a.H;
     if (nh > 0) {
         const int64_t grid = (nh * 16 + bwd::NTH - 1) / bwd::NTH;
@@ -814,19 +791,17 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s) {
     if (kb_cap <= 0 || a.N == 0) return hipSuccess;
     const dim3 grid((unsigned)kb_cap, (unsigned)a.H, (unsigned)a.nc);
     const dim3 rgrid((unsigned)kb_cap, (unsigned)a.H, (unsigned)bwd::RZ);
-    std::lock_guard<std::mutex> lk(g_side_mu);
-    SideStream* ss = side_for_current_device();
-    if (!ss) {   // no second stream: the two parts one after the other
-        hipError_t e = launch_dkdv_part(a, grid, rgrid, s);
-        return e != hipSuccess ? e : launch_dq_part(a, grid, rgrid, s);
-    }
     hipError_t e;
-    if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(ss->st, ss->fork, 0)) != hipSuccess) return e;
-    if ((e = launch_dq_part(a, grid, rgrid, ss->st)) != hipSuccess) return e;
+    if (!s_dq) {
+        if ((e = launch_dkdv_part(a, grid, rgrid, s)) != hipSuccess) return e;
+        return launch_dq_part(a, grid, rgrid, s);
+    }
+    if ((e = hipEventRecord(fork, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s_dq, fork, 0)) != hipSuccess) return e;
+    if ((e = launch_dq_part(a, grid, rgrid, s_dq)) != hipSuccess) return e;
     if ((e = launch_dkdv_part(a, grid, rgrid, s)) != hipSuccess) return e;
-    if ((e = hipEventRecord(ss->join, ss->st)) != hipSuccess) return e;
-    return hipStreamWaitEvent(s, ss->join, 0);
+    if ((e = hipEventRecord(join, s_dq)) != hipSuccess) return e;
+    return hipStreamWaitEvent(s, join, 0);
 }
 
 }  // namespace fm

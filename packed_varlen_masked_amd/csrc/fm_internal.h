@@ -135,6 +135,9 @@ constexpr int BWD_MAX_CHUNKS = 8;
 // Key block (columns per extrema row) of the backward's plan.
 constexpr int bwd_block_k() { return 64; }
 // Delta, then dK/dV, then dQ; kb_cap bounds the number of 64-key blocks.
-hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s);
+// s_dq, fork, join: a second stream and two events of the caller's for the
+// dQ launches, or all null (everything on s).
+hipError_t launch_bwd_bf16(const BwdArgs& a, int64_t kb_cap, hipStream_t s, hipStream_t s_dq, hipEvent_t fork,
+                           hipEvent_t join);
 
 }  // namespace fm

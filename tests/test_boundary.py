@@ -169,6 +169,23 @@ def test_bwd_rejects_on_host(pv, kw, code):
     assert msg
 
 
+@pytest.mark.parametrize("streams,code", [
+    ((None, FAKE, FAKE), 1),          # no dQ stream: the one-stream call is fm_attn_bwd
+    ((FAKE, None, FAKE), 1),          # missing event
+    ((FAKE, FAKE, None), 1),
+])
+def test_bwd_streams_rejects_on_host(pv, streams, code):
+    """The two-stream backward needs the caller's second stream and both
+    events; it rejects a missing one before enqueueing anything."""
+    dq_stream, fork, join = streams
+    rc = pv._lib.fm_attn_bwd_streams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, pv.FM_BF16, 256, 2, 128, FAKE, 1, FAKE, 1, 1,
+                                     ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE, 1 << 40, ctypes.c_void_p(8192),
+                                     dq_stream, fork, join)
+    msg = pv._lib.fm_last_error().decode()
+    assert rc == code, msg
+    assert msg
+
+
 def test_bwd_workspace_size(pv):
     """Header, kb_off, extrema at 64-key blocks, Delta fp32 [H][N]."""
     L = pv._lib

@@ -209,13 +209,15 @@ def test_bwd_bad_cu_and_empty(pv):
     assert dq.shape == (0, 2, 128)
 
 
-def test_bwd_stream_order(pv):
-    """The dQ launches run on a second stream of the library's, forked from
-    and joined back into the caller's stream: work enqueued afterwards on a
-    (non-default) caller stream must see the finished gradients.  Two
-    streams each run the backward and copy dq, dk, dv right after it with no
-    host synchronisation; every copy must equal a fully synchronised run,
-    bit for bit, three times over."""
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_bwd_stream_order(pv, two_streams):
+    """Work enqueued after the backward on a (non-default) caller stream
+    sees the finished gradients: on one stream, and with the dQ launches on
+    a second stream of the caller's (fm_attn_bwd_streams: forked after Delta,
+    joined back with the caller's events).  Two streams each run the
+    backward and copy dq, dk, dv right after it with no host
+    synchronisation; every copy must equal a fully synchronised run, bit for
+    bit, three times over."""
     w = W.document_workload([300, 700, 1200], H=2, seed=6)
     ref, _ = run_bwd(pv, w)
     q, k, v = (bf16(x).cuda() for x in (w.q, w.k, w.v))
@@ -225,14 +227,15 @@ def test_bwd_stream_order(pv):
     out, lse = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale))
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    side = [torch.cuda.Stream(), torch.cuda.Stream()] if two_streams else [None, None]
     copies = []
     for rep in range(3):
-        for st in streams:
+        for st, sd in zip(streams, side):
             with torch.cuda.stream(st):
-                grads = pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale))
+                grads = pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale), dq_stream=sd)
                 copies.append([t.clone() for t in grads])
     torch.cuda.synchronize()
-    say("stream order: %d copies" % len(copies))
+    say("stream order (two streams: %s): %d copies" % (two_streams, len(copies)))
     for c in copies:
         for x, y in zip(c, ref):
             assert np.array_equal(x.float().cpu().numpy(), y)
