@@ -663,11 +663,13 @@ __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
             const int j = 8 * gp;
-            *(u32x4*)(po + part_index(Wv.w, dt, gp, Wv.lane)) =
-                u32x4{f16_pair(st.o[dt][j] * sc, st.o[dt][j + 1] * sc),
-                      f16_pair(st.o[dt][j + 2] * sc, st.o[dt][j + 3] * sc),
-                      f16_pair(st.o[dt][j + 4] * sc, st.o[dt][j + 5] * sc),
-                      f16_pair(st.o[dt][j + 6] * sc, st.o[dt][j + 7] * sc)};
+            // non-temporal: the partials are read once, by the merge launch;
+            // streaming them out of the L2 keeps the end of this launch short
+            __builtin_nontemporal_store(u32x4{f16_pair(st.o[dt][j] * sc, st.o[dt][j + 1] * sc),
+                                              f16_pair(st.o[dt][j + 2] * sc, st.o[dt][j + 3] * sc),
+                                              f16_pair(st.o[dt][j + 4] * sc, st.o[dt][j + 5] * sc),
+                                              f16_pair(st.o[dt][j + 6] * sc, st.o[dt][j + 7] * sc)},
+                                        (u32x4*)(po + part_index(Wv.w, dt, gp, Wv.lane)));
         }
     const int lr = 32 * Wv.w + Wv.n;
     if (Wv.hh == 0) {
@@ -969,14 +971,18 @@ __global__ __launch_bounds__(NTH, 2) void fm_fused_bf16_kernel(AttnArgs a) {
 constexpr int MNTH = 256, MSPL = 16;
 
 __global__ __launch_bounds__(MNTH) void fm_merge_bf16_kernel(AttnArgs a) {
-    const int n_merge = *a.n_merge;
     const int lane = threadIdx.x & 63, dt = threadIdx.x >> 6, n = lane & 31, hh = lane >> 5;
-    const int64_t n_tasks = (int64_t)min((int64_t)n_merge, a.merge_cap) * NW * 2;
+    // every entry below merge_cap lies inside the list, so a task's entry is
+    // read together with the entry count (one memory round trip, not two)
+    // and entries at or past the count are skipped
+    const int n_merge = *a.n_merge;
+    const int64_t n_tasks = a.merge_cap * NW * 2;
     for (int64_t task = blockIdx.x; task < n_tasks; task += gridDim.x) {
         const int64_t k = task / (NW * 2);
         const int w = (int)((task / 2) % NW), gp = (int)(task % 2);
         const int4 e0 = *(const int4*)(a.merge_list + k * MERGE_WORDS);
         const int nsp = a.merge_list[k * MERGE_WORDS + 4];
+        if (k >= n_merge) break;                 // tasks only grow along the loop
         const int slot0 = e0.x, h = e0.y, lr = 32 * w + n;
         const int64_t qrow = (int64_t)e0.z + lr;
         if (qrow >= e0.w || nsp <= 1) continue;   // rows of one chunk wrote out themselves
