@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--split", type=int, default=-1, help="max key blocks per item (-1 auto, 0 none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="leave out the backward and rotary-embedding legs")
+    ap.add_argument("--only-timed", action="store_true",
+                    help="run only the warm-up and the timed back-to-back steps (for profiler runs whose "
+                         "per-kernel averages should be those of the timed steps)")
     ap.add_argument("--seeds", type=int, default=1, help="measure this many seeds (seed, seed + 1, ...), one line each")
     ap.add_argument("--planned", action="store_true",
                     help="time the planning launches + plan-reading attention even where the fused path applies")
@@ -683,6 +686,11 @@ def measure(w, args):
 
     # pass 1: the timed steps, back to back between two events
     ms_step, host_ms, host_ahead = time_calls(step, K)
+    if args.only_timed:
+        return {"metric": METRIC, "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+                "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+                "higher_is_better": True, "config": {"workload": w.name, "seed": w.meta["seed"]},
+                "path": "fused" if fused else "planned", "only_timed": True}
     # pass 2: every step between its own two events (the median and spread of
     # one step; an event between launches keeps the next launch from starting
     # while the previous one drains, so these run a little longer than pass 1)
