@@ -200,11 +200,12 @@ __shared__ __attribute__((aligned(16))) char s_vt[2 * BLK * ROW_R];
 
 // One q tile's staging data in registers: QU chunks of Q and of dO per
 // thread (row c >> 4, chunk c & 15 of c = tid + 512 u), and threads 0..63
-// the lse (log2 units; +inf for rows that attend nothing or lie past the
-// sequence, so that P = 0 there) and Delta of row tid.
+// the lse and Delta of row tid (-inf and 0 past the sequence).  The lse is
+// kept as loaded and turned into log2 units only when it is staged, so
+// nothing waits for these loads before the next tile's turn.
 struct QStage {
     u32x4 q[QU], g[QU];
-    float l2, dl;
+    float lse, dl;
 };
 __device__ inline void load_qstage(const BwdArgs& a, int h, int r0, int r1, int tid, QStage& st) {
     const int64_t rsb = (int64_t)a.H * 2 * HD;
@@ -219,11 +220,10 @@ __device__ inline void load_qstage(const BwdArgs& a, int h, int r0, int r1, int 
             st.g[u] = *(const u32x4*)((const char*)a.dout + off);
         }
     }
-    st.l2 = INFINITY;
+    st.lse = -INFINITY;
     st.dl = 0.f;
     if (tid < BLK && r0 + tid < r1) {
-        const float l = a.lse[(int64_t)h * a.N + r0 + tid];
-        st.l2 = l == -INFINITY ? INFINITY : l * LOG2E;
+        st.lse = a.lse[(int64_t)h * a.N + r0 + tid];
         st.dl = a.delta[(int64_t)h * a.N + r0 + tid];
     }
 }
@@ -235,7 +235,9 @@ __device__ inline void store_qstage(const QStage& st, int tid) {
         *(u32x4*)(s_dkv + OFF_G + soff(row, ch)) = st.g[u];
     }
     if (tid < BLK) {
-        ((float*)(s_dkv + OFF_L2))[tid] = st.l2;
+        // lse in log2 units; +inf where no key is allowed or past the
+        // sequence, so that P = 0 there
+        ((float*)(s_dkv + OFF_L2))[tid] = st.lse == -INFINITY ? INFINITY : st.lse * LOG2E;
         ((float*)(s_dkv + OFF_DL))[tid] = st.dl;
     }
 }
@@ -568,9 +570,22 @@ __device__ inline void load_kstage(const BwdArgs& a, int h, int c0, int c1, bool
             st.v[u] = *(const u32x4*)((const char*)a.v + off);
         }
     }
-    st.mv = Vec4{0, 0, 0, 0};
+    // the stored vectors straight into their slots, defaults preset (as
+    // fill_column fills them), with no arithmetic on the loaded values: the
+    // wave waits for these loads only at the next block's turn
     const int key = c0 + (tid & 63);
-    if (part && key < c1) st.mv = fill_column(a.sv, a.n_vec, a.causal, a.N, key);
+    const bool ld = part && key < c1;
+    const int64_t N = a.N;
+    // stored vector behind LTE, UTS, UTE (-1: absent, the default stays)
+    const int s1 = (a.n_vec == 4 || (a.causal && a.n_vec == 2)) ? 1 : -1;
+    const int s2 = a.n_vec == 4 ? 2 : -1;
+    const int s3 = a.n_vec == 4 ? 3 : (!a.causal && a.n_vec == 2) ? 1 : -1;
+    int m0 = 0, m1 = (int)N, m2 = 0, m3 = 0;
+    if (ld) m0 = a.sv[key];
+    if (ld && s1 >= 0) m1 = a.sv[s1 * N + key];
+    if (ld && s2 >= 0) m2 = a.sv[s2 * N + key];
+    if (ld && s3 >= 0) m3 = a.sv[s3 * N + key];
+    st.mv = Vec4{m0, m1, m2, m3};
 }
 __device__ inline void store_kstage(const KStage& st, int tid) {
 #pragma unroll
@@ -622,25 +637,37 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
     const int kb_end = a.nc > 1 ? min(kb_lim, (ch + 1) * a.kc) : kb_lim;
     const int kb_first = a.nc > 1 ? ch * a.kc : 0;
     const int32_t* xb = a.extrema + (int64_t)a.kb_off[sp.b] * 8;
+    // Classes of a window of 64 key blocks from `wbase` (lane = block), kept
+    // as ballots: the block extrema are read once per window, not once per
+    // visited block.
+    int wbase = -1;
+    uint64_t wv = 0, wp = 0;
     auto next_visit = [&](int from, bool& part) -> int {
-        for (int w0 = from; w0 < kb_end; w0 += 64) {
-            const int kb = w0 + lane;
-            bool v = false, p = false;
-            if (kb < kb_end) {
-                const int4 e0 = *(const int4*)(xb + (int64_t)kb * 8);
-                const int4 e1 = *(const int4*)(xb + (int64_t)kb * 8 + 4);
-                const int x[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-                const int c0 = sp.s_b + kb * BLK, c1 = min(c0 + BLK, sp.e_b);
-                const TileInfo ti = classify_tile(r0, r1, c0, c1, x, a.causal);
-                v = ti.cls != CLS_FULL;
-                p = ti.cls == CLS_PARTIAL;
+        while (from < kb_end) {
+            if (wbase < 0 || from >= wbase + 64) {
+                wbase = from;
+                const int kb = from + lane;
+                bool v = false, p = false;
+                if (kb < kb_end) {
+                    const int4 e0 = *(const int4*)(xb + (int64_t)kb * 8);
+                    const int4 e1 = *(const int4*)(xb + (int64_t)kb * 8 + 4);
+                    const int x[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+                    const int c0 = sp.s_b + kb * BLK, c1 = min(c0 + BLK, sp.e_b);
+                    const TileInfo ti = classify_tile(r0, r1, c0, c1, x, a.causal);
+                    v = ti.cls != CLS_FULL;
+                    p = ti.cls == CLS_PARTIAL;
+                }
+                wv = __ballot(v);
+                wp = __ballot(p);
             }
-            const uint64_t vm = __ballot(v);
-            if (vm) {
-                const int bit = __builtin_ctzll(vm);
-                part = ((__ballot(p) >> bit) & 1ull) != 0;
-                return w0 + bit;
+            const int off = from - wbase;   // 0..63
+            const uint64_t m = wv >> off;
+            if (m) {
+                const int bit = __builtin_ctzll(m);
+                part = ((wp >> (off + bit)) & 1ull) != 0;
+                return from + bit;
             }
+            from = wbase + 64;
         }
         return kb_end;
     };
