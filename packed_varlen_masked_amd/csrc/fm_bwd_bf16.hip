@@ -209,13 +209,16 @@ struct QStage {
 };
 __device__ inline void load_qstage(const BwdArgs& a, int h, int r0, int r1, int tid, QStage& st) {
     const int64_t rsb = (int64_t)a.H * 2 * HD;
+    // the tile's first row (uniform) plus the thread's part (the same for
+    // every tile, so it is computed once)
+    const int64_t tile = (int64_t)r0 * rsb + (int64_t)h * 2 * HD;
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
         const int c = tid + NTK * u, row = c >> 4, ch = c & 15;
         st.q[u] = u32x4{0, 0, 0, 0};
         st.g[u] = u32x4{0, 0, 0, 0};
         if (r0 + row < r1) {
-            const int64_t off = (int64_t)(r0 + row) * rsb + (int64_t)h * 2 * HD + 16 * ch;
+            const int64_t off = tile + ((int64_t)row * rsb + 16 * ch);
             st.q[u] = *(const u32x4*)((const char*)a.q + off);
             st.g[u] = *(const u32x4*)((const char*)a.dout + off);
         }
@@ -404,23 +407,34 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
     const int ch = blockIdx.z;
     const int Tq = a.nc > 1 ? min(Tq_all, (ch + 1) * a.qc) : Tq_all;
     const int i_first = max(a.causal ? (c0 - sp.s_b) / BLK : 0, a.nc > 1 ? ch * a.qc : 0);
-    // next q tile at or after `from` whose class is not FULL (Tq if none)
+    // next q tile at or after `from` whose class is not FULL (Tq if none);
+    // the classes of a window of 64 q tiles from `wbase` (lane = tile) are
+    // kept as ballots, so a step only scans bits
+    int wbase = -1;
+    uint64_t wv = 0, wp = 0;
     auto next_visit = [&](int from, bool& part) -> int {
-        for (int w0 = from; w0 < Tq; w0 += 64) {
-            const int i = w0 + lane;
-            bool v = false, p = false;
-            if (i < Tq) {
-                const int r0 = sp.s_b + i * BLK, r1 = min(r0 + BLK, sp.e_b);
-                const TileInfo ti = classify_tile(r0, r1, c0, c1, xe, a.causal);
-                v = ti.cls != CLS_FULL;
-                p = ti.cls == CLS_PARTIAL;
+        while (from < Tq) {
+            if (wbase < 0 || from >= wbase + 64) {
+                wbase = from;
+                const int i = from + lane;
+                bool v = false, p = false;
+                if (i < Tq) {
+                    const int r0 = sp.s_b + i * BLK, r1 = min(r0 + BLK, sp.e_b);
+                    const TileInfo ti = classify_tile(r0, r1, c0, c1, xe, a.causal);
+                    v = ti.cls != CLS_FULL;
+                    p = ti.cls == CLS_PARTIAL;
+                }
+                wv = __ballot(v);
+                wp = __ballot(p);
             }
-            const uint64_t vm = __ballot(v);
-            if (vm) {
-                const int bit = __builtin_ctzll(vm);
-                part = ((__ballot(p) >> bit) & 1ull) != 0;
-                return w0 + bit;
+            const int off = from - wbase;   // 0..63
+            const uint64_t m = wv >> off;
+            if (m) {
+                const int bit = __builtin_ctzll(m);
+                part = ((wp >> (off + bit)) & 1ull) != 0;
+                return from + bit;
             }
+            from = wbase + 64;
         }
         return Tq;
     };
@@ -441,9 +455,6 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
         __syncthreads();   // every wave is done with the previous tile
         store_qstage(st, tid);
         __syncthreads();
-        bool npart = false;
-        const int ni = next_visit(i + 1, npart);
-        if (ni < Tq) load_qstage(a, h, sp.s_b + ni * BLK, min(sp.s_b + (ni + 1) * BLK, sp.e_b), tid, st);
 
         // S = Q K^T and dP = dO V^T for rows 32g..32g+31 of the tile:
         // register e is row 32g + 8(e>>2) + 4hh + (e&3), column = this lane's key
@@ -457,6 +468,10 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
             sc = mfma(as_bf16x8(*(const u32x4*)(s_q + o)), as_bf16x8(*(const u32x4*)(kb_l + 32 * s)), sc);
             dp = mfma(as_bf16x8(*(const u32x4*)(s_g + o)), as_bf16x8(*(const u32x4*)(vb_l + 32 * s)), dp);
         }
+        // the next visited tile and its loads, issued while the products run
+        bool npart = false;
+        const int ni = next_visit(i + 1, npart);
+        if (ni < Tq) load_qstage(a, h, sp.s_b + ni * BLK, min(sp.s_b + (ni + 1) * BLK, sp.e_b), tid, st);
         if constexpr (DROP) {   // this wave's dropout bytes for the tile
             uint32_t w0 = (uint32_t)(r0 + 32 * g + (lane & 31));
             uint32_t w1 = (uint32_t)(((c0 - sp.s_b) >> 4) + 2 * t + (lane >> 5)), w2 = (uint32_t)h, w3 = a.offset;
