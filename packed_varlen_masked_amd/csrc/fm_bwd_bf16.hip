@@ -574,13 +574,16 @@ struct KStage {
 constexpr int KU = BLK * 16 / NTQ;   // 16-byte chunks of K (and of V) per thread
 __device__ inline void load_kstage(const BwdArgs& a, int h, int c0, int c1, bool part, int tid, KStage& st) {
     const int64_t rsb = (int64_t)a.H * 2 * HD;
+    // the block's first key (uniform) plus the thread's part (the same for
+    // every block, so it is computed once)
+    const int64_t blk = (int64_t)c0 * rsb + (int64_t)h * 2 * HD;
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
         const int c = tid + NTQ * u, row = c >> 4, ch = c & 15;
         st.k[u] = u32x4{0, 0, 0, 0};
         st.v[u] = u32x4{0, 0, 0, 0};
         if (c0 + row < c1) {
-            const int64_t off = (int64_t)(c0 + row) * rsb + (int64_t)h * 2 * HD + 16 * ch;
+            const int64_t off = blk + ((int64_t)row * rsb + 16 * ch);
             st.k[u] = *(const u32x4*)((const char*)a.k + off);
             st.v[u] = *(const u32x4*)((const char*)a.v + off);
         }
@@ -710,12 +713,6 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
                   row_bits(rel_row(st.mv.uts, q0), rel_row(st.mv.ute, q0));
         }
         __syncthreads();
-        bool npart = false;
-        const int nkb = next_visit(kb + 1, npart);
-        if (nkb < kb_end) {
-            const int nc0 = sp.s_b + nkb * BLK;
-            load_kstage(a, h, nc0, min(nc0 + BLK, sp.e_b), npart, tid, st);
-        }
 
         // S^T = K Q^T and dP^T = V dO^T: register e of result t is key
         // 32t + 8(e>>2) + 4hh + (e&3) of the block, column = this lane's query
@@ -732,6 +729,13 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
                 sc[t] = mfma(as_bf16x8(*(const u32x4*)(s_k + soff(32 * t + n, 2 * s + hh))), qf[s], sc[t]);
                 dp[t] = mfma(as_bf16x8(*(const u32x4*)(va + 32 * t * ROW_R + 32 * s)), gf[s], dp[t]);
             }
+        // the next visited block and its loads, issued while the products run
+        bool npart = false;
+        const int nkb = next_visit(kb + 1, npart);
+        if (nkb < kb_end) {
+            const int nc0 = sp.s_b + nkb * BLK;
+            load_kstage(a, h, nc0, min(nc0 + BLK, sp.e_b), npart, tid, st);
+        }
         if (part) {   // keys k and k + 4 of register e: the masks built by lanes k and k + 4
             const int mki = (int)mk;
 #pragma unroll
