@@ -173,6 +173,7 @@ struct Wave {
     uint32_t rsb;      // row stride of q/k/v in bytes
     uint32_t vo[5];    // per-lane source byte offsets of the wave's copies in a tile of 64 rows
     bool no_skip;
+    bool idle;         // the wave's 32 rows lie past the item's rows: it only copies
 };
 
 // MFMA phase, part 1: S^T = K Q^T, two 32-key tiles x 8 k-steps.  K
@@ -538,6 +539,42 @@ __device__ __attribute__((always_inline)) inline void kv_step(
     phase_barrier();
 }
 
+// Step j for a wave without rows: the same copies, queue, waits and
+// barrier as kv_step, none of the products or the softmax.
+template <int G>
+__device__ __attribute__((always_inline)) inline void kv_step_idle(const AttnArgs& a, const Item& I, Queue& Qu,
+                                                                   const Wave& Wv, Slots& sl, int j, int T,
+                                                                   bool& rec_pending, int fv, int& nrec, int n_items,
+                                                                   const char* Kh, const char* Vh, const uint16_t* vis) {
+    const int nk_raw = vis[min(j + 4, T - 1)];
+    if (rec_pending) {
+        const int nx = (int)gridDim.x + __builtin_amdgcn_readfirstlane(fv);
+        if (nx < n_items && Wv.lane < ITEM_WORDS) nrec = a.items[(int64_t)nx * ITEM_WORDS + Wv.lane];
+        rec_pending = false;
+    }
+    if constexpr (G == 0) {
+        const Tile tl = tile_at(I, Wv, Qu.k2);
+        const i32x4 rs = tile_rsrc(Wv, Kh + tl.off, tl.last);
+        char* kd = kbuf(sl.u2);
+#pragma unroll
+        for (int s = 0; s < 5; ++s) copy_one(Wv, rs, kd, s);
+        copy_mask(a, Wv, tl, s_mv + ((j + 2) & 3) * MVW);
+    } else {
+        const Tile tl = tile_at(I, Wv, Qu.k1);
+        const i32x4 rs = tile_rsrc(Wv, Vh + tl.off, tl.last);
+        char* vd = vbuf(sl.u1);
+#pragma unroll
+        for (int s = 0; s < 5; ++s) copy_one(Wv, rs, vd, s);
+    }
+    const int nk = __builtin_amdgcn_readfirstlane(nk_raw);
+    Qu.kp = Qu.k0;
+    Qu.k0 = Qu.k1; Qu.k1 = Qu.k2; Qu.k2 = Qu.k3; Qu.k3 = nk & 0x7fff;
+    Qu.iv = ((Qu.iv >> 1) & 7u) | ((uint32_t)(nk >> 15) << 3) | ((Qu.iv & 1u) << 4);
+    sl.next();
+    if constexpr (G == 0) wait_vm<BATCH_G0>(); else wait_vm<BATCH_G1>();
+    phase_barrier();
+}
+
 // ---- per-launch and per-item set-up ----------------------------------
 __device__ __attribute__((always_inline)) inline void wave_setup(const AttnArgs& a, Wave& Wv) {
     Wv.tid = threadIdx.x; Wv.lane = Wv.tid & 63; Wv.w = __builtin_amdgcn_readfirstlane(Wv.tid >> 6);
@@ -706,6 +743,10 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
     const int tid = Wv.tid, lane = Wv.lane, w = Wv.w;
     const int64_t rs = (int64_t)a.H * HD;
     Wv.qrow = I.r0 + 32 * w + Wv.n;
+    // a wave whose rows all lie past the q tile's end (short sequences) has
+    // no products to compute: it runs the copy-only step below, and its O,
+    // m and l stay empty (it writes no row)
+    Wv.idle = I.r0 + 32 * w >= I.r1;
     const char* Kh = (const char*)a.k + I.hoff * 2;
     const char* Vh = (const char*)a.v + I.hoff * 2;
     const int lo = Wv.no_skip ? 0 : I.kbb, hi = Wv.no_skip ? I.Tc : I.kbe;
@@ -813,7 +854,14 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
             for (int c = 0; c < 2; ++c) pb[t][c] = as_bf16x8(u32x4{0, 0, 0, 0});   // P_{-1}
         Slots sl{0, 1, 2};
         Qu.kp = Qu.k0;
-        if (Wv.g == 0)
+        if (Wv.idle) {
+            if (Wv.g == 0)
+                for (int j = 0; j < T; ++j)
+                    kv_step_idle<0>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, Kh, Vh, vis);
+            else
+                for (int j = 0; j < T; ++j)
+                    kv_step_idle<1>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, Kh, Vh, vis);
+        } else if (Wv.g == 0)
             for (int j = 0; j < T; ++j)
                 kv_step<0, DROP>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
         else
@@ -821,7 +869,7 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
                 kv_step<1, DROP>(a, I, Qu, Wv, sl, j, T, rec_pending, fv, nrec, n_items, qf, sacc, pb, st, Kh, Vh, vis);
         // the last tile (V_{T-1} sits in slot u2 now): group 1 still owes its
         // softmax; then O += V_{T-1} P_{T-1}
-        if (Wv.g == 1) {
+        if (Wv.g == 1 && !Wv.idle) {
             float rsum;
             const float alpha = softmax_tile<DROP>(a, I, Wv, sacc, Qu.kp, (Qu.iv & 16u) != 0, s_mv + ((T - 1) & 3) * MVW,
                                              st, pb, rsum);
@@ -833,7 +881,7 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
             }
             st.l_run = st.l_run * alpha + rsum;
         }
-        pv_part(vbuf(sl.u2), pb, st, lane);
+        if (!Wv.idle) pv_part(vbuf(sl.u2), pb, st, lane);
     }
     // copies past the item's last tile may still be in flight: drain them
     // here, before the output stores, so that the next item can refill the
