@@ -699,6 +699,24 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
         load_kstage(a, h, c0, min(c0 + BLK, sp.e_b), part, tid, st);
     }
     const float sl2 = a.scale_log2;
+    // a wave whose 32 queries all lie past the tile's end (short sequences)
+    // only stages its share of each block and keeps the barriers; its dQ
+    // stays zero (separate loop, so that the full one is unchanged)
+    if (q0 >= r1) {
+        while (kb < kb_end) {
+            __syncthreads();
+            store_kstage(st, tid);
+            __syncthreads();
+            bool npart = false;
+            const int nkb = next_visit(kb + 1, npart);
+            if (nkb < kb_end) {
+                const int nc0 = sp.s_b + nkb * BLK;
+                load_kstage(a, h, nc0, min(nc0 + BLK, sp.e_b), npart, tid, st);
+            }
+            kb = nkb;
+            part = npart;
+        }
+    }
     while (kb < kb_end) {
         const int c0 = sp.s_b + kb * BLK, c1 = min(c0 + BLK, sp.e_b);
         __syncthreads();   // every wave is done with the previous block
