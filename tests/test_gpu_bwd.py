@@ -129,16 +129,32 @@ def test_bwd_deterministic(pv):
         assert np.array_equal(x, y)
 
 
+def compare_heads(w, got, g, heads, tag):
+    """dq, dk, dv of the given heads against the full oracle (heads are
+    independent: each is one single-head problem on the same mask)."""
+    for h in heads:
+        w1 = W.Workload(w.name + "_h%d" % h, w.N, 1, w.D, w.dtype, w.causal, w.n_vec, w.cu_seqlens, w.startend,
+                        w.scale, w.q[:, h:h + 1], w.k[:, h:h + 1], w.v[:, h:h + 1])
+        compare(w1, tuple(x[:, h:h + 1] for x in got), g[:, h:h + 1], "%s head %d" % (tag, h))
+
+
 def test_bwd_sft_full_one_head(pv):
-    """SFT packing workload at full size (16384 tokens, 32 heads): head 0's
-    dq, dk, dv against the full oracle (heads are independent)."""
+    """SFT packing workload at full size (16384 tokens, 32 heads): dq, dk,
+    dv of heads 0 and H - 1 against the full oracle."""
     w = W.make_config(3)
     say("bwd SFT full N=%d H=%d" % (w.N, w.H))
     got, g = run_bwd(pv, w)
-    h = 0
-    w1 = W.Workload(w.name + "_h0", w.N, 1, w.D, w.dtype, w.causal, w.n_vec, w.cu_seqlens, w.startend, w.scale,
-                    w.q[:, h:h + 1], w.k[:, h:h + 1], w.v[:, h:h + 1])
-    compare(w1, tuple(x[:, h:h + 1] for x in got), g[:, h:h + 1], "cfg3 head 0")
+    compare_heads(w, got, g, (0, w.H - 1), "cfg3")
+
+
+def test_bwd_shared_question_full_heads(pv):
+    """Shared-question workload at full size (32768 tokens, 32 heads; each
+    answer attends to its prompt and itself, not to its siblings): dq, dk,
+    dv of heads 0 and H - 1 against the full oracle."""
+    w = W.make_config(4)
+    say("bwd shared-question full N=%d H=%d" % (w.N, w.H))
+    got, g = run_bwd(pv, w)
+    compare_heads(w, got, g, (0, w.H - 1), "cfg4")
 
 
 def test_bwd_prefix_window_full_sampled(pv):
