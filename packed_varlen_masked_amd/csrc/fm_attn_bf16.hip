@@ -454,7 +454,9 @@ __device__ __attribute__((always_inline)) inline float softmax_tile(const AttnAr
                                                                     const int32_t* cmv, State& st, bf16x8 (&pb)[2][2],
                                                                     float& rsum) {
     const int c0 = I.s_b + kb * BC, c1 = min(c0 + BC, I.e_b);
-    const bool causal = a.causal && (c1 > I.r0 + 1);
+    // the causal rule can mask a pair of this wave's rows only when the
+    // tile's last key lies past the wave's first row
+    const bool causal = a.causal && (c1 - 1 > Wv.qrow - Wv.n);
     const float mx = mask_max(sacc, causal, (c1 - c0) < BC, iv, c0, c1, Wv.qrow - Wv.n, cmv, a.scale_log2, Wv.lane);
     DropW dw;
     if constexpr (DROP) dw = drop_words(a.seed_lo, a.seed_hi, a.offset, Wv.qrow, kb, I.h, Wv.hh);
