@@ -559,42 +559,63 @@ __global__ __launch_bounds__(NTK) void fm_bwd_dkdv_reduce_kernel(BwdArgs a) {
 }
 
 // ---- dQ --------------------------------------------------------------------
+// 8 waves, 256 queries (wave w: queries 32w..32w+31), two groups of four
+// (one wave of each per SIMD) in opposite phase, as in the forward: in the
+// step of key block j, group 0 issues dQ += dS_{j-1} K_{j-1} and S_j, dP_j,
+// then turns S_j, dP_j into dS_j; group 1 first turns S_{j-1}, dP_{j-1}
+// into dS_{j-1}, then issues the same products.  While one wave of a SIMD
+// feeds its matrix unit, the other keeps its vector unit busy.  K, V and
+// the mask intervals of a block sit in a 3-slot LDS ring: block j + 1 is
+// stored (from registers loaded a step earlier) into the slot that block
+// j - 2 has left, so one barrier per step suffices.
 constexpr int NTQ = 512;         // dQ workgroup: 8 waves, 256 queries (two waves per SIMD)
 constexpr int QBLK = NTQ / 128;  // 64-row blocks per dQ workgroup
-__shared__ __attribute__((aligned(16))) char s_k[BLK * ROW_S];
-__shared__ __attribute__((aligned(16))) char s_v[BLK * ROW_R];
+constexpr int QSLOTS = 3;
+__shared__ __attribute__((aligned(16))) char s_qk[QSLOTS][BLK * ROW_S];
+__shared__ __attribute__((aligned(16))) char s_qv[QSLOTS][BLK * ROW_S];
+__shared__ __attribute__((aligned(16))) Vec4 s_qmv[QSLOTS][BLK];
 
-// One key block's staging data in registers: 4 chunks of K and of V per
-// thread (rows past the sequence are zero), and for partial blocks the
-// mask intervals of key c0 + lane (every wave loads its own copy).
-struct KStage {
-    u32x4 k[BLK * 16 / 512], v[BLK * 16 / 512];
-    Vec4 mv;
-};
-constexpr int KU = BLK * 16 / NTQ;   // 16-byte chunks of K (and of V) per thread
-__device__ inline void load_kstage(const BwdArgs& a, int h, int c0, int c1, bool part, int tid, KStage& st) {
-    const int64_t rsb = (int64_t)a.H * 2 * HD;
-    // the block's first key (uniform) plus the thread's part (the same for
-    // every block, so it is computed once)
-    const int64_t blk = (int64_t)c0 * rsb + (int64_t)h * 2 * HD;
+// Staging of a key block: K and V rows go from global memory straight into
+// their LDS slot with asynchronous copies (buffer_load ... lds: 64 lanes x
+// 16 bytes into 1 KB of LDS at M0 + 16 lane, rows past the sequence read
+// as zeros through the buffer's byte count); each lane's source is the
+// chunk that the swizzled layout puts at its LDS position, so copy i of a
+// block fills rows 4i..4i+3 (16 copies per tensor, 2 per wave).  The
+// copies are issued with inline assembly and waited for explicitly.  Wave
+// 0 also loads the mask intervals of key c0 + lane of a partial block into
+// registers and stores them to the slot before the block is published.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __attribute__((always_inline)) inline void dma_b16(void* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+                 "{m0}"((uint32_t)(uintptr_t)(lds_char*)dst)
+                 : "memory");
+}
+// Source offset (bytes from the block's first row) of this lane in copy i.
+__device__ __attribute__((always_inline)) inline uint32_t stage_voff(int i, int lane, uint32_t rsb) {
+    const int r = 4 * i + (lane >> 4);
+    return (uint32_t)r * rsb + 16u * (uint32_t)((lane & 15) ^ swz(r));
+}
+__device__ __attribute__((always_inline)) inline void stage_block(const BwdArgs& a, int h, int c0, int c1, int slot,
+                                                                  int w, const uint32_t (&vo)[2]) {
+    const uint32_t rsb = (uint32_t)a.H * 2 * HD;
+    const int64_t base = (int64_t)c0 * rsb + (int64_t)h * 2 * HD;
+    const int nbytes = (c1 - c0 - 1) * (int)rsb + 2 * HD;   // through the block's last row
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.k + base), (short)0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.v + base), (short)0, nbytes, 0x00020000);
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-        const int c = tid + NTQ * u, row = c >> 4, ch = c & 15;
-        st.k[u] = u32x4{0, 0, 0, 0};
-        st.v[u] = u32x4{0, 0, 0, 0};
-        if (c0 + row < c1) {
-            const int64_t off = blk + ((int64_t)row * rsb + 16 * ch);
-            st.k[u] = *(const u32x4*)((const char*)a.k + off);
-            st.v[u] = *(const u32x4*)((const char*)a.v + off);
-        }
+    for (int x = 0; x < 2; ++x) {
+        dma_b16(s_qk[slot] + 1024 * (2 * w + x), rk, vo[x]);
+        dma_b16(s_qv[slot] + 1024 * (2 * w + x), rv, vo[x]);
     }
-    // the stored vectors straight into their slots, defaults preset (as
-    // fill_column fills them), with no arithmetic on the loaded values: the
-    // wave waits for these loads only at the next block's turn
-    const int key = c0 + (tid & 63);
+}
+// The stored vectors behind LTS, LTE, UTS, UTE of key c0 + lane (wave 0,
+// partial blocks), defaults preset (as fill_column fills them).
+__device__ __attribute__((always_inline)) inline Vec4 load_mv(const BwdArgs& a, int c0, int c1, bool part, int lane) {
+    const int key = c0 + lane;
     const bool ld = part && key < c1;
     const int64_t N = a.N;
-    // stored vector behind LTE, UTS, UTE (-1: absent, the default stays)
     const int s1 = (a.n_vec == 4 || (a.causal && a.n_vec == 2)) ? 1 : -1;
     const int s2 = a.n_vec == 4 ? 2 : -1;
     const int s3 = a.n_vec == 4 ? 3 : (!a.causal && a.n_vec == 2) ? 1 : -1;
@@ -603,14 +624,69 @@ __device__ inline void load_kstage(const BwdArgs& a, int h, int c0, int c1, bool
     if (ld && s1 >= 0) m1 = a.sv[s1 * N + key];
     if (ld && s2 >= 0) m2 = a.sv[s2 * N + key];
     if (ld && s3 >= 0) m3 = a.sv[s3 * N + key];
-    st.mv = Vec4{m0, m1, m2, m3};
+    return Vec4{m0, m1, m2, m3};
 }
-__device__ inline void store_kstage(const KStage& st, int tid) {
+
+// The products of half u (keys 32u..32u+31) of a staged block: S^T = K Q^T
+// and dP^T = V dO^T, register e = key 32u + 8(e>>2) + 4hh + (e&3), column =
+// this lane's query.
+__device__ __attribute__((always_inline)) inline void dq_sdp(int slot, int u, const bf16x8 (&qf)[8],
+                                                             const bf16x8 (&gf)[8], f32x16& sc, f32x16& dp, int n,
+                                                             int hh) {
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-        const int c = tid + NTQ * u, row = c >> 4, ch = c & 15;
-        *(u32x4*)(s_k + soff(row, ch)) = st.k[u];
-        *(u32x4*)(s_v + row * ROW_R + 16 * ch) = st.v[u];
+    for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
+    const char* kt = s_qk[slot];
+    const char* vt = s_qv[slot];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int o = soff(32 * u + n, 2 * s + hh);
+        sc = mfma(as_bf16x8(*(const u32x4*)(kt + o)), qf[s], sc);
+        dp = mfma(as_bf16x8(*(const u32x4*)(vt + o)), gf[s], dp);
+    }
+}
+// dQ^T += K^T dS^T over the 16-key groups 2u, 2u + 1 of a staged block.
+__device__ __attribute__((always_inline)) inline void dq_acc(int slot, int u, const bf16x8 (&db)[2], f32x16 (&dq)[4],
+                                                             int lane) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dq[dt] = mfma(tr_frag_s(s_qk[slot], 2 * u + k, dt, lane), db[k], dq[dt]);
+}
+// dS = P o (dP - Delta) of half u of a block as the B operand of dq_acc,
+// with the element mask of a partial block (keys k and k + 4 of register e:
+// the 32-row masks built by lanes k and k + 4 from the staged intervals).
+template <bool DROP>
+__device__ __attribute__((always_inline)) inline void dq_ds(const BwdArgs& a, f32x16& sc, const f32x16& dp,
+                                                            bf16x8 (&db)[2], int slot, int u, bool part, int c0, int c1,
+                                                            int kb, int q0, int qr, float l2, float dl, int h,
+                                                            int lane, int hh) {
+    if (part) {
+        const int key = c0 + lane;
+        const Vec4 mv = s_qmv[slot][lane];
+        uint32_t mk = a.causal ? row_bits(0, key - q0) : 0u;
+        if (key >= c1) mk = 0xffffffffu;
+        mk |= row_bits(rel_row(mv.lts, q0), rel_row(mv.lte, q0)) | row_bits(rel_row(mv.uts, q0), rel_row(mv.ute, q0));
+        const int mki = (int)mk;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int k0 = 32 * u + 8 * (e >> 2) + (e & 3);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(mki, k0);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(mki, k0 + 4);
+            sc[e] = select_lanes(sc[e], -INFINITY, lo, hi);
+        }
+    }
+    DropW dw;
+    if constexpr (DROP) dw = drop_words(a.seed_lo, a.seed_hi, a.offset, qr, kb, h, hh);
+    const float sl2 = a.scale_log2;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], sl2, -l2));
+        float dpz = dp[e];
+        if constexpr (DROP) {   // register e of half u: block 2u + (e >> 3), word 2((e >> 2) & 1) + hh
+            const uint32_t byte = (dw.w[2 * u + (e >> 3)][(e >> 2) & 1] >> (8 * (e & 3))) & 0xffu;
+            dpz = byte >= (uint32_t)a.drop_t ? dpz * a.drop_ks : 0.f;
+        }
+        db[e >> 3][e & 7] = (__bf16)(p * (dpz - dl));
     }
 }
 
@@ -620,7 +696,7 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
     const Span sp = span_of<QBLK>(a, blockIdx.x);
     if (!sp.ok) return;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = lane & 31, hh = lane >> 5;
+    const int n = lane & 31, hh = lane >> 5, g = w >> 2;
     const int r0 = sp.lo, r1 = sp.hi;
     const int q0 = r0 + 32 * w;          // the wave's first row
     const int qr = q0 + n;               // this lane's query
@@ -660,7 +736,7 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
     // visited block.
     int wbase = -1;
     uint64_t wv = 0, wp = 0;
-    auto next_visit = [&](int from, bool& part) -> int {
+    auto next_visit = [&](int from, bool& part) __attribute__((always_inline)) -> int {
         while (from < kb_end) {
             if (wbase < 0 || from >= wbase + 64) {
                 wbase = from;
@@ -689,106 +765,110 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
         }
         return kb_end;
     };
+    auto cstart = [&](int kb) __attribute__((always_inline)) { return sp.s_b + kb * BLK; };
+    auto cend = [&](int kb) __attribute__((always_inline)) { return min(sp.s_b + (kb + 1) * BLK, sp.e_b); };
 
-    KStage st;
-    bool part = false;
-    int kb = next_visit(kb_first, part);
-    if (a.nc > 1 && kb >= kb_end) return;   // empty chunk: no partial, its flag stays stale
-    if (kb < kb_end) {
-        const int c0 = sp.s_b + kb * BLK;
-        load_kstage(a, h, c0, min(c0 + BLK, sp.e_b), part, tid, st);
-    }
-    const float sl2 = a.scale_log2;
-    // a wave whose 32 queries all lie past the tile's end (short sequences)
-    // only stages its share of each block and keeps the barriers; its dQ
-    // stays zero (separate loop, so that the full one is unchanged)
-    if (q0 >= r1) {
-        while (kb < kb_end) {
-            __syncthreads();
-            store_kstage(st, tid);
-            __syncthreads();
-            bool npart = false;
-            const int nkb = next_visit(kb + 1, npart);
-            if (nkb < kb_end) {
-                const int nc0 = sp.s_b + nkb * BLK;
-                load_kstage(a, h, nc0, min(nc0 + BLK, sp.e_b), npart, tid, st);
-            }
-            kb = nkb;
-            part = npart;
-        }
-    }
-    while (kb < kb_end) {
-        const int c0 = sp.s_b + kb * BLK, c1 = min(c0 + BLK, sp.e_b);
-        __syncthreads();   // every wave is done with the previous block
-        store_kstage(st, tid);
-        // 32-row mask of key c0 + lane for this wave's rows (partial blocks)
-        uint32_t mk = 0;
-        if (part) {
-            const int key = c0 + lane;
-            mk = a.causal ? row_bits(0, key - q0) : 0u;
-            if (key >= c1) mk = 0xffffffffu;
-            mk |= row_bits(rel_row(st.mv.lts, q0), rel_row(st.mv.lte, q0)) |
-                  row_bits(rel_row(st.mv.uts, q0), rel_row(st.mv.ute, q0));
-        }
+    // The pipeline, per visited block j (slot j mod 3) two half steps and one
+    // barrier (nothing a block's second half reads changes inside the
+    // block).  In the first half of block j every wave issues its
+    // copies of block j + 1 into the slot block j - 2 has left; they (and
+    // wave 0's mask intervals) are waited for at the end of block j, before
+    // the barrier that publishes block j + 1.
+    const uint32_t rsb = (uint32_t)a.H * 2 * HD;
+    const uint32_t vo[2] = {stage_voff(2 * w, lane, rsb), stage_voff(2 * w + 1, lane, rsb)};
+    Vec4 mvr = Vec4{0, 0, 0, 0};         // wave 0: mask intervals of the block in flight
+    bool pc = false, pn = false;
+    int kc = next_visit(kb_first, pc);   // block j
+    if (a.nc > 1 && kc >= kb_end) return;   // empty chunk: no partial, its flag stays stale
+    int kn = kb_end;                     // block j + 1
+    // publish: wait for this wave's copies (and loads) of the block in
+    // flight, put its mask intervals in place, barrier
+    auto publish = [&](int slot, bool part) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0)
+        asm volatile("" ::: "memory");
+        if (w == 0 && part) s_qmv[slot][lane] = mvr;
         __syncthreads();
-
-        // S^T = K Q^T and dP^T = V dO^T: register e of result t is key
-        // 32t + 8(e>>2) + 4hh + (e&3) of the block, column = this lane's query
-        f32x16 sc[2], dp[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) { sc[t][e] = 0.f; dp[t][e] = 0.f; }
-        const char* va = s_v + n * ROW_R + 16 * hh;
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                sc[t] = mfma(as_bf16x8(*(const u32x4*)(s_k + soff(32 * t + n, 2 * s + hh))), qf[s], sc[t]);
-                dp[t] = mfma(as_bf16x8(*(const u32x4*)(va + 32 * t * ROW_R + 32 * s)), gf[s], dp[t]);
-            }
-        // the next visited block and its loads, issued while the products run
-        bool npart = false;
-        const int nkb = next_visit(kb + 1, npart);
-        if (nkb < kb_end) {
-            const int nc0 = sp.s_b + nkb * BLK;
-            load_kstage(a, h, nc0, min(nc0 + BLK, sp.e_b), npart, tid, st);
+    };
+    if (kc < kb_end) {
+        stage_block(a, h, cstart(kc), cend(kc), 0, w, vo);
+        if (w == 0 && pc) mvr = load_mv(a, cstart(kc), cend(kc), pc, lane);
+        kn = next_visit(kc + 1, pn);
+        publish(0, pc);
+    } else {
+        __syncthreads();
+    }
+    // issue block j + 1's copies into slot sn; returns block j + 2
+    auto advance = [&](int sn, int& kn2, bool& pn2) __attribute__((always_inline)) {
+        kn2 = kb_end;
+        pn2 = false;
+        if (kn < kb_end) {
+            stage_block(a, h, cstart(kn), cend(kn), sn, w, vo);
+            if (w == 0 && pn) mvr = load_mv(a, cstart(kn), cend(kn), pn, lane);
+            kn2 = next_visit(kn + 1, pn2);
         }
-        if (part) {   // keys k and k + 4 of register e: the masks built by lanes k and k + 4
-            const int mki = (int)mk;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int k0 = 32 * t + 8 * (e >> 2) + (e & 3);
-                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(mki, k0);
-                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(mki, k0 + 4);
-                    sc[t][e] = select_lanes(sc[t][e], -INFINITY, lo, hi);
-                }
+    };
+    int sp_ = 2, sc_ = 0, sn_ = 1;   // slots of blocks j - 1, j, j + 1
+    if (q0 >= r1) {
+        // a wave whose 32 queries all lie past the tile's end (short
+        // sequences) only stages its share of each block and keeps the
+        // barriers; its dQ stays zero
+        for (bool first = true; kc < kb_end; first = false) {
+            if (!first) publish(sc_, pc);
+            int kn2;
+            bool pn2;
+            advance(sn_, kn2, pn2);
+            kc = kn; pc = pn; kn = kn2; pn = pn2;
+            const int t = sp_; sp_ = sc_; sc_ = sn_; sn_ = t;
         }
-        bf16x8 db[2][2];
-        DropW dw;
-        if constexpr (DROP) dw = drop_words(a.seed_lo, a.seed_hi, a.offset, qr, kb, h, hh);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][e], sl2, -l2));
-                float dpz = dp[t][e];
-                if constexpr (DROP) {   // register e of tile t: block 2t + (e >> 3), word 2((e >> 2) & 1) + hh
-                    const uint32_t byte = (dw.w[2 * t + (e >> 3)][(e >> 2) & 1] >> (8 * (e & 3))) & 0xffu;
-                    dpz = byte >= (uint32_t)a.drop_t ? dpz * a.drop_ks : 0.f;
-                }
-                db[t][e >> 3][e & 7] = (__bf16)(p * (dpz - dl));
+    } else if (g == 0) {
+        // group 0: products of the half, then its dS
+        f32x16 sc, dp;
+        bf16x8 db[2];
+        const bool any = kc < kb_end;
+        for (bool first = true; kc < kb_end; first = false) {
+            if (!first) {
+                publish(sc_, pc);
+                dq_acc(sp_, 1, db, dq, lane);            // previous block, half 1
             }
-        // dQ^T += K^T dS^T: 16-key groups kg of the block
-#pragma unroll
-        for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-                dq[dt] = mfma(tr_frag_s(s_k, kg, dt, lane), db[kg >> 1][kg & 1], dq[dt]);
-        kb = nkb;
-        part = npart;
+            dq_sdp(sc_, 0, qf, gf, sc, dp, n, hh);
+            int kn2;
+            bool pn2;
+            advance(sn_, kn2, pn2);
+            dq_ds<DROP>(a, sc, dp, db, sc_, 0, pc, cstart(kc), cend(kc), kc, q0, qr, l2, dl, h, lane, hh);
+            dq_acc(sc_, 0, db, dq, lane);
+            dq_sdp(sc_, 1, qf, gf, sc, dp, n, hh);
+            dq_ds<DROP>(a, sc, dp, db, sc_, 1, pc, cstart(kc), cend(kc), kc, q0, qr, l2, dl, h, lane, hh);
+            kc = kn; pc = pn; kn = kn2; pn = pn2;
+            const int t = sp_; sp_ = sc_; sc_ = sn_; sn_ = t;
+        }
+        if (any) dq_acc(sp_, 1, db, dq, lane);           // the last block, half 1
+    } else {
+        // group 1: dS of the previous half, then the products of this one
+        f32x16 sc, dp;
+        bf16x8 db[2];
+        int kp = kb_end;
+        bool pp = false;
+        for (bool first = true; kc < kb_end; first = false) {
+            if (!first) {
+                publish(sc_, pc);
+                dq_ds<DROP>(a, sc, dp, db, sp_, 1, pp, cstart(kp), cend(kp), kp, q0, qr, l2, dl, h, lane, hh);
+            }
+            int kn2;
+            bool pn2;
+            advance(sn_, kn2, pn2);
+            if (!first) dq_acc(sp_, 1, db, dq, lane);   // previous block, half 1
+            dq_sdp(sc_, 0, qf, gf, sc, dp, n, hh);
+            dq_ds<DROP>(a, sc, dp, db, sc_, 0, pc, cstart(kc), cend(kc), kc, q0, qr, l2, dl, h, lane, hh);
+            dq_acc(sc_, 0, db, dq, lane);
+            dq_sdp(sc_, 1, qf, gf, sc, dp, n, hh);
+            kp = kc; pp = pc;
+            kc = kn; pc = pn; kn = kn2; pn = pn2;
+            const int t = sp_; sp_ = sc_; sc_ = sn_; sn_ = t;
+        }
+        if (kp < kb_end) {   // the last block, half 1: dS, then its dQ
+            dq_ds<DROP>(a, sc, dp, db, sp_, 1, pp, cstart(kp), cend(kp), kp, q0, qr, l2, dl, h, lane, hh);
+            dq_acc(sp_, 1, db, dq, lane);
+        }
     }
 
     if (a.nc > 1) {   // this chunk's dQ^T, unscaled
