@@ -27,8 +27,11 @@
 //   * dQ kernel: one workgroup of 8 waves per (256-query tile, head); wave
 //     w owns queries 32w..32w+31 with their Q and dO fragments, lse and
 //     Delta in registers.  It walks the visited 64-key blocks, stages K and
-//     V in LDS, computes S^T = K Q^T and dP^T = V dO^T with one query per
-//     lane (as the forward does), and accumulates dQ^T = K^T dS^T.
+//     V in an LDS ring with asynchronous copies, computes S^T = K Q^T and
+//     dP^T = V dO^T with one query per lane (as the forward does), and
+//     accumulates dQ^T = K^T dS^T; its two wave groups work in opposite
+//     phase on 32-key half blocks, so that one wave of a SIMD issues
+//     products while the other computes dS.
 //   * small problems (fewer workgroups than compute units) cut each key
 //     tile's q tiles and each query tile's key blocks into chunks that run
 //     as separate workgroups and write fp32 partials; two reduce launches
