@@ -16,14 +16,16 @@
 // Layout and schedule (this file's own):
 //   * delta kernel: Delta[h, i] = <dO_i, O_i> in fp32, 16 lanes per row.
 //   * dK/dV kernel: one workgroup of 8 waves per (128-key tile, head);
-//     wave 4g + t owns keys 32t..32t+31 (K and V fragments in registers)
-//     and query rows 32g..32g+31 of each staged tile.  It walks the
-//     sequence's 64-row q tiles that are not FULL against its key tile,
-//     stages Q, dO, lse and Delta of each in LDS (the next tile is loaded
-//     into registers while the current one is used), computes S = Q K^T
-//     and dP = dO V^T with one key per lane (so the key's mask intervals
-//     are lane constants), and accumulates dV^T = dO^T P and dK^T = Q^T dS
-//     with the LDS transpose read; the two row halves are summed in LDS.
+//     wave 4g + t owns keys 32t..32t+31 (half of its key's K row in
+//     registers, the rest of K and V in LDS) and query rows 32g..32g+31 of
+//     each staged tile.  It walks the sequence's 64-row q tiles that are
+//     not FULL against its key tile, stages Q, dO, lse and Delta of each in
+//     an LDS ring with asynchronous copies, computes S = Q K^T and
+//     dP = dO V^T with one key per lane (so the key's mask intervals are
+//     lane constants), and accumulates dV^T = dO^T P and dK^T = Q^T dS
+//     with the LDS transpose read; its two wave groups work in opposite
+//     phase (in phase with dropout), and the two row halves are summed in
+//     LDS.
 //   * dQ kernel: one workgroup of 8 waves per (256-query tile, head); wave
 //     w owns queries 32w..32w+31 with their Q and dO fragments, lse and
 //     Delta in registers.  It walks the visited 64-key blocks, stages K and
@@ -153,6 +155,25 @@ __device__ inline Span span_of(const BwdArgs& a, int x) {
     return sp;
 }
 
+// Asynchronous copies of 64-row tiles (K and V in the dQ kernel, Q and dO in
+// the dK/dV kernel) from global memory straight into swizzled LDS rows
+// (buffer_load ... lds: 64 lanes x 16 bytes into 1 KB of LDS at M0 + 16
+// lane; rows past the sequence read as zeros through the buffer's byte
+// count).  Each lane's source is the chunk that the swizzled layout puts
+// at its LDS position, so copy i of a tile fills rows 4i..4i+3 (16 copies
+// per tensor, 2 per wave).  The copies are issued with inline assembly and
+// waited for explicitly.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __attribute__((always_inline)) inline void dma_b16(void* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+                 "{m0}"((uint32_t)(uintptr_t)(lds_char*)dst)
+                 : "memory");
+}
+// Source offset (bytes from the block's first row) of this lane in copy i.
+__device__ __attribute__((always_inline)) inline uint32_t stage_voff(int i, int lane, uint32_t rsb) {
+    const int r = 4 * i + (lane >> 4);
+    return (uint32_t)r * rsb + 16u * (uint32_t)((lane & 15) ^ swz(r));
+}
 // ---- Delta ---------------------------------------------------------------
 // Delta[h, i] = sum_d dO[i, h, d] O[i, h, d]: 16 lanes per (row, head), 8
 // channels each, summed over the 16 lanes with DPP (quad swaps, then the
@@ -187,65 +208,153 @@ __global__ __launch_bounds__(NTH) void fm_bwd_delta_kernel(BwdArgs a) {
 }
 
 // ---- dK / dV ---------------------------------------------------------------
-// 8 waves: wave w = 4g + t owns keys 32t..32t+31 of the 128-key span and
-// query rows 32g..32g+31 of every staged 64-row q tile (two waves per
-// SIMD).  The two groups' dK^T and dV^T are summed through LDS at the end.
+// 8 waves: wave w = 4g + t owns keys 32t..32t+31 of the 128-key span (its
+// key's K fragments in registers, the span's V rows in LDS) and query rows
+// 32g..32g+31 of every staged 64-row q tile (two waves per SIMD).  The two
+// groups work in opposite phase, as in the dQ kernel: in the step of q tile
+// i, group 0 issues dV^T += dO_{i-1}^T P_{i-1}, dK^T += Q_{i-1}^T dS_{i-1}
+// and S_i, dP_i, then turns S_i, dP_i into P_i, dS_i; group 1 first turns
+// the S, dP it computed in the previous step into P, dS, then issues the
+// same products.  Q, dO, lse and Delta of a tile sit in a 3-slot LDS ring
+// filled by asynchronous copies (tile i + 1 into the slot tile i - 2 has
+// left), one barrier per tile.  The groups' dK^T and dV^T are summed
+// through LDS at the end.
 constexpr int NTK = 512;
-constexpr int QU = BLK * 16 / NTK;   // 16-byte chunks of Q (and of dO) per thread
 constexpr int KV_COMB = 4 * 64 * 16 * 16;   // bytes: one accumulator set of a group (16 x 16 B per lane)
 constexpr int OFF_G = BLK * ROW_S, OFF_L2 = 2 * BLK * ROW_S, OFF_DL = OFF_L2 + 4 * BLK;
-constexpr int DKV_LDS = KV_COMB > OFF_DL + 4 * BLK ? KV_COMB : OFF_DL + 4 * BLK;
-// staging (Q tile, dO tile, lse, Delta) during the loop, the group sums after it
+constexpr int QSLOT = OFF_DL + 4 * BLK;      // one ring slot: Q, dO (swizzled rows), lse (log2 units), Delta
+constexpr int DKV_LDS = KV_COMB > 3 * QSLOT ? KV_COMB : 3 * QSLOT;
+// the ring during the loop, the group sums after it
 __shared__ __attribute__((aligned(16))) char s_dkv[DKV_LDS];
-// the span's K and V rows (128 keys), staged once
-__shared__ __attribute__((aligned(16))) char s_kt[2 * BLK * ROW_R];
+// the span's V rows (128 keys) and the upper half (channels 64..127) of its
+// K rows, staged once (the lower half of a lane's K row stays in
+// registers), and the mask intervals of each key
+constexpr int KH_ROW = 144;   // bytes per row of the K half: 8 chunks + 1 of padding
 __shared__ __attribute__((aligned(16))) char s_vt[2 * BLK * ROW_R];
+__shared__ __attribute__((aligned(16))) char s_kh[2 * BLK * KH_ROW];
+__shared__ __attribute__((aligned(16))) Vec4 s_kmv[2 * BLK];
 
-// One q tile's staging data in registers: QU chunks of Q and of dO per
-// thread (row c >> 4, chunk c & 15 of c = tid + 512 u), and threads 0..63
-// the lse and Delta of row tid (-inf and 0 past the sequence).  The lse is
-// kept as loaded and turned into log2 units only when it is staged, so
-// nothing waits for these loads before the next tile's turn.
-struct QStage {
-    u32x4 q[QU], g[QU];
-    float lse, dl;
-};
-__device__ inline void load_qstage(const BwdArgs& a, int h, int r0, int r1, int tid, QStage& st) {
-    const int64_t rsb = (int64_t)a.H * 2 * HD;
-    // the tile's first row (uniform) plus the thread's part (the same for
-    // every tile, so it is computed once)
-    const int64_t tile = (int64_t)r0 * rsb + (int64_t)h * 2 * HD;
+// Copies of q tile rows [r0, r1) of Q and dO into ring slot `slot`.
+__device__ __attribute__((always_inline)) inline void stage_qtile(const BwdArgs& a, int h, int r0, int r1, int slot,
+                                                                  int w, int lane) {
+    const uint32_t rsb = (uint32_t)a.H * 2 * HD;
+    const uint32_t vo[2] = {stage_voff(2 * w, lane, rsb), stage_voff(2 * w + 1, lane, rsb)};
+    const int64_t base = (int64_t)r0 * rsb + (int64_t)h * 2 * HD;
+    const int nbytes = (r1 - r0 - 1) * (int)rsb + 2 * HD;   // through the tile's last row
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.q + base), (short)0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rg =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.dout + base), (short)0, nbytes, 0x00020000);
+    char* sl = s_dkv + slot * QSLOT;
 #pragma unroll
-    for (int u = 0; u < QU; ++u) {
-        const int c = tid + NTK * u, row = c >> 4, ch = c & 15;
-        st.q[u] = u32x4{0, 0, 0, 0};
-        st.g[u] = u32x4{0, 0, 0, 0};
-        if (r0 + row < r1) {
-            const int64_t off = tile + ((int64_t)row * rsb + 16 * ch);
-            st.q[u] = *(const u32x4*)((const char*)a.q + off);
-            st.g[u] = *(const u32x4*)((const char*)a.dout + off);
-        }
-    }
-    st.lse = -INFINITY;
-    st.dl = 0.f;
-    if (tid < BLK && r0 + tid < r1) {
-        st.lse = a.lse[(int64_t)h * a.N + r0 + tid];
-        st.dl = a.delta[(int64_t)h * a.N + r0 + tid];
+    for (int x = 0; x < 2; ++x) {
+        dma_b16(sl + 1024 * (2 * w + x), rq, vo[x]);
+        dma_b16(sl + OFF_G + 1024 * (2 * w + x), rg, vo[x]);
     }
 }
-__device__ inline void store_qstage(const QStage& st, int tid) {
+
+// S = Q K^T and dP = dO V^T for rows 32g..32g+31 of a staged tile: register
+// e is row 32g + 8(e>>2) + 4hh + (e&3), column = this lane's key.
+// K fragments of k-steps 0..3 come from registers, 4..7 from the span's K
+// half in LDS (kh_l: this lane's key row there).
+__device__ __attribute__((always_inline)) inline void dkdv_sdp(const char* sl, const bf16x8 (&kf)[4], const char* kh_l,
+                                                               const char* vb_l, f32x16& sc, f32x16& dp, int g, int n,
+                                                               int hh) {
 #pragma unroll
-    for (int u = 0; u < QU; ++u) {
-        const int c = tid + NTK * u, row = c >> 4, ch = c & 15;
-        *(u32x4*)(s_dkv + soff(row, ch)) = st.q[u];
-        *(u32x4*)(s_dkv + OFF_G + soff(row, ch)) = st.g[u];
+    for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
+    const int qrow = 32 * g + n;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int o = soff(qrow, 2 * s + hh);
+        const bf16x8 kb = s < 4 ? kf[s & 3] : as_bf16x8(*(const u32x4*)(kh_l + 32 * (s - 4)));
+        sc = mfma(as_bf16x8(*(const u32x4*)(sl + o)), kb, sc);
+        dp = mfma(as_bf16x8(*(const u32x4*)(sl + OFF_G + o)), as_bf16x8(*(const u32x4*)(vb_l + 32 * s)), dp);
     }
-    if (tid < BLK) {
-        // lse in log2 units; +inf where no key is allowed or past the
-        // sequence, so that P = 0 there
-        ((float*)(s_dkv + OFF_L2))[tid] = st.lse == -INFINITY ? INFINITY : st.lse * LOG2E;
-        ((float*)(s_dkv + OFF_DL))[tid] = st.dl;
+}
+// dV^T += dO^T P and dK^T += Q^T dS over the 16-row group 2g + c2.
+__device__ __attribute__((always_inline)) inline void dkdv_acc_half(const char* sl, const bf16x8& pb, const bf16x8& db,
+                                                                    f32x16 (&dv)[4], f32x16 (&dk)[4], int g, int c2,
+                                                                    int lane) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        dv[dt] = mfma(tr_frag_s(sl + OFF_G, 2 * g + c2, dt, lane), pb, dv[dt]);
+        dk[dt] = mfma(tr_frag_s(sl, 2 * g + c2, dt, lane), db, dk[dt]);
     }
+}
+__device__ __attribute__((always_inline)) inline void dkdv_acc(const char* sl, const bf16x8 (&pb)[2],
+                                                               const bf16x8 (&db)[2], f32x16 (&dv)[4], f32x16 (&dk)[4],
+                                                               int g, int lane) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) dkdv_acc_half(sl, pb[c2], db[c2], dv, dk, g, c2, lane);
+}
+
+// Dropout bytes of a wave's 32 rows x 32 keys (dK/dV): lane L writes the
+// four words of (row L & 31, 16-key block L >> 5), u32 index
+// ((row * 2 + block) * 4 + word).
+__shared__ __attribute__((aligned(16))) uint32_t s_drop[8][256];
+
+// This wave's dropout bytes for the tile at r0 (one Philox4x32-10 block per
+// lane), written right after the wave has issued the tile's S and dP (its
+// vector work then runs beside the products) and read by dkdv_pds.
+__device__ __attribute__((always_inline)) inline void dkdv_dropw(const BwdArgs& a, int r0, int c0, int s_b, int h,
+                                                                 int g, int t, int w, int lane) {
+    uint32_t w0 = (uint32_t)(r0 + 32 * g + (lane & 31));
+    uint32_t w1 = (uint32_t)(((c0 - s_b) >> 4) + 2 * t + (lane >> 5)), w2 = (uint32_t)h, w3 = a.offset;
+    philox4x32_10(w0, w1, w2, w3, a.seed_lo, a.seed_hi);
+    *(u32x4*)&s_drop[w][((lane & 31) * 2 + (lane >> 5)) * 4] = u32x4{w0, w1, w2, w3};
+}
+
+// P = exp2(S scale log2e - lse2), masked pairs 0; dS = P (dP - Delta); with
+// dropout Z = keep * 256 / (256 - t): P Z for dV, dS = P (dP Z - Delta).
+// Tile rows from r0, staged lse2 and Delta in slot sl; the B operands of
+// dkdv_acc_half for the 16-row group 2g + c2.
+template <bool DROP>
+__device__ __attribute__((always_inline)) inline void dkdv_pds_half(const BwdArgs& a, const f32x16& sc,
+                                                                    const f32x16& dp, bf16x8& pb, bf16x8& db,
+                                                                    const char* sl, int r0, bool part, int kj,
+                                                                    int g, int t, int w, int lane, int c2) {
+    const int n = lane & 31, hh = lane >> 5;
+    const float* s_l2 = (const float*)(sl + OFF_L2);
+    const float* s_dl = (const float*)(sl + OFF_DL);
+    Vec4 mv{0, 0, 0, 0};
+    if (part) mv = s_kmv[32 * t + n];
+    const float sl2 = a.scale_log2;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * c2 + jj;
+        const float4 l4 = *(const float4*)(s_l2 + 32 * g + 8 * j + 4 * hh);
+        const float4 d4 = *(const float4*)(s_dl + 32 * g + 8 * j + 4 * hh);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int e = 4 * j + c;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], sl2, -lv[c]));
+            if (part) {
+                const int row = r0 + 32 * g + 8 * j + 4 * hh + c;
+                const bool m = (a.causal && kj > row) || (mv.lts <= row && row < mv.lte) ||
+                               (mv.uts <= row && row < mv.ute);
+                p = m ? 0.f : p;
+            }
+            float pz = p, dpz = dp[e];
+            if constexpr (DROP) {
+                const int rw = 8 * j + 4 * hh + c;   // row within the wave's 32
+                const uint32_t word = s_drop[w][(rw * 2 + (n >> 4)) * 4 + ((n & 15) >> 2)];
+                const bool keep = ((word >> (8 * (n & 3))) & 0xffu) >= (uint32_t)a.drop_t;
+                pz = keep ? p * a.drop_ks : 0.f;
+                dpz = keep ? dpz * a.drop_ks : 0.f;
+            }
+            pb[e & 7] = (__bf16)pz;
+            db[e & 7] = (__bf16)(p * (dpz - dv4[c]));
+        }
+    }
+}
+template <bool DROP>
+__device__ __attribute__((always_inline)) inline void dkdv_pds(const BwdArgs& a, const f32x16& sc, const f32x16& dp,
+                                                               bf16x8 (&pb)[2], bf16x8 (&db)[2], const char* sl,
+                                                               int r0, bool part, int kj, int g, int t, int w,
+                                                               int lane) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) dkdv_pds_half<DROP>(a, sc, dp, pb[c2], db[c2], sl, r0, part, kj, g, t, w, lane, c2);
 }
 
 // Group sums: group `from` writes its 4 accumulators, the other group adds
@@ -345,11 +454,6 @@ __device__ __attribute__((always_inline)) inline void store_row_bf16(uint16_t* o
         }
 }
 
-// Dropout bytes of a wave's 32 rows x 32 keys (dK/dV): lane L writes the
-// four words of (row L & 31, 16-key block L >> 5), u32 index
-// ((row * 2 + block) * 4 + word).
-__shared__ __attribute__((aligned(16))) uint32_t s_drop[8][256];
-
 template <bool DROP>
 __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
     const int h = blockIdx.y;
@@ -376,27 +480,33 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
         }
     }
 
-    // the span's K and V rows into LDS (rows past the sequence: zeros);
-    // this lane's key and its mask intervals
+    // the span's V rows and the upper half of its K rows into LDS (rows
+    // past the sequence: zeros), the keys' mask intervals; this lane's key
+    // and the lower half of its K row (B operands: column n, channels
+    // 16s + 8hh, s < 4)
 #pragma unroll
     for (int u = 0; u < 2 * BLK * 16 / NTK; ++u) {
         const int c = tid + NTK * u, row = c >> 4, ch = c & 15;
-        u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
+        u32x4 vv = u32x4{0, 0, 0, 0}, kv = u32x4{0, 0, 0, 0};
+        const int64_t off = ((int64_t)(c0 + row) * a.H + h) * 2 * HD + 16 * ch;
         if (c0 + row < c1) {
-            const int64_t off = ((int64_t)(c0 + row) * a.H + h) * 2 * HD + 16 * ch;
-            kv = *(const u32x4*)((const char*)a.k + off);
             vv = *(const u32x4*)((const char*)a.v + off);
+            if (ch >= 8) kv = *(const u32x4*)((const char*)a.k + off);
         }
-        *(u32x4*)(s_kt + row * ROW_R + 16 * ch) = kv;
         *(u32x4*)(s_vt + row * ROW_R + 16 * ch) = vv;
+        if (ch >= 8) *(u32x4*)(s_kh + row * KH_ROW + 16 * (ch - 8)) = kv;
     }
+    if (tid < 2 * BLK) s_kmv[tid] = c0 + tid < c1 ? fill_column(a.sv, a.n_vec, a.causal, a.N, c0 + tid) : Vec4{0, 0, 0, 0};
     const int kj = c0 + 32 * t + n;
     const bool kvalid = kj < c1;
-    // B-operand fragments of this lane's key (column n, channels 16s + 8hh)
-    const char* kb_l = s_kt + (32 * t + n) * ROW_R + 16 * hh;
+    bf16x8 kf[4];
+    {
+        const char* kp = (const char*)a.k + ((int64_t)kj * a.H + h) * 2 * HD + 16 * hh;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(kvalid ? *(const u32x4*)(kp + 32 * s) : u32x4{0, 0, 0, 0});
+    }
     const char* vb_l = s_vt + (32 * t + n) * ROW_R + 16 * hh;
-    Vec4 mv{0, 0, 0, 0};
-    if (kvalid) mv = fill_column(a.sv, a.n_vec, a.causal, a.N, kj);
+    const char* kh_l = s_kh + (32 * t + n) * KH_ROW + 16 * hh;
 
     f32x16 dk[4], dv[4];
 #pragma unroll
@@ -415,7 +525,7 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
     // kept as ballots, so a step only scans bits
     int wbase = -1;
     uint64_t wv = 0, wp = 0;
-    auto next_visit = [&](int from, bool& part) -> int {
+    auto next_visit = [&](int from, bool& part) __attribute__((always_inline)) -> int {
         while (from < Tq) {
             if (wbase < 0 || from >= wbase + 64) {
                 wbase = from;
@@ -441,91 +551,123 @@ __global__ __launch_bounds__(NTK, 1) void fm_bwd_dkdv_kernel(BwdArgs a) {
         }
         return Tq;
     };
+    auto rstart = [&](int i) __attribute__((always_inline)) { return sp.s_b + i * BLK; };
+    auto rend = [&](int i) __attribute__((always_inline)) { return min(sp.s_b + (i + 1) * BLK, sp.e_b); };
 
-    QStage st;
-    bool part = false;
-    int i = next_visit(i_first, part);
-    const bool any = i < Tq;
-    if (a.nc > 1 && !any) return;   // empty chunk: no partial, its flag stays stale
-    if (i < Tq) load_qstage(a, h, sp.s_b + i * BLK, min(sp.s_b + (i + 1) * BLK, sp.e_b), tid, st);
-    const float sl2 = a.scale_log2;
-    const char* s_q = s_dkv;
-    const char* s_g = s_dkv + OFF_G;
-    const float* s_l2 = (const float*)(s_dkv + OFF_L2);
-    const float* s_dl = (const float*)(s_dkv + OFF_DL);
-    while (i < Tq) {
-        const int r0 = sp.s_b + i * BLK;
-        __syncthreads();   // every wave is done with the previous tile
-        store_qstage(st, tid);
+    // The pipeline: q tile i in slot i mod 3.  In step i every wave issues
+    // its copies of tile i + 1 into the slot tile i - 2 has left, and wave 0
+    // loads that tile's lse and Delta into registers; they are waited for
+    // (and wave 0 stages lse in log2 units, +inf where no key is allowed or
+    // past the sequence, so that P = 0 there) before the barrier that
+    // publishes tile i + 1.
+    float lsr = -INFINITY, dlr = 0.f;    // wave 0: lse, Delta of row `lane` of the tile in flight
+    auto load_ld = [&](int i) __attribute__((always_inline)) {
+        if (w == 0) {
+            lsr = -INFINITY;
+            dlr = 0.f;
+            if (rstart(i) + lane < rend(i)) {
+                lsr = a.lse[(int64_t)h * a.N + rstart(i) + lane];
+                dlr = a.delta[(int64_t)h * a.N + rstart(i) + lane];
+            }
+        }
+    };
+    auto publish = [&](int slot) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0)
+        asm volatile("" ::: "memory");
+        if (w == 0) {
+            ((float*)(s_dkv + slot * QSLOT + OFF_L2))[lane] = lsr == -INFINITY ? INFINITY : lsr * LOG2E;
+            ((float*)(s_dkv + slot * QSLOT + OFF_DL))[lane] = dlr;
+        }
         __syncthreads();
-
-        // S = Q K^T and dP = dO V^T for rows 32g..32g+31 of the tile:
-        // register e is row 32g + 8(e>>2) + 4hh + (e&3), column = this lane's key
+    };
+    bool pc = false, pn = false;
+    int ic = next_visit(i_first, pc);    // tile i
+    const bool any = ic < Tq;
+    if (a.nc > 1 && !any) return;   // empty chunk: no partial, its flag stays stale
+    int in_ = Tq;                        // tile i + 1
+    if (any) {
+        stage_qtile(a, h, rstart(ic), rend(ic), 0, w, lane);
+        load_ld(ic);
+        in_ = next_visit(ic + 1, pn);
+        publish(0);
+    } else {
+        __syncthreads();
+    }
+    auto advance = [&](int sn, int& in2, bool& pn2) __attribute__((always_inline)) {
+        in2 = Tq;
+        pn2 = false;
+        if (in_ < Tq) {
+            stage_qtile(a, h, rstart(in_), rend(in_), sn, w, lane);
+            load_ld(in_);
+            in2 = next_visit(in_ + 1, pn2);
+        }
+    };
+    auto slot = [&](int k) __attribute__((always_inline)) { return (const char*)(s_dkv + k * QSLOT); };
+    int sp_ = 2, sc_ = 0, sn_ = 1;   // slots of tiles i - 1, i, i + 1
+    if constexpr (DROP) {
+        // with dropout the vector work (the keep bytes and their tests)
+        // outweighs the products, so a phase shift cannot hide it, and the
+        // registers a shifted group carries across the barrier would spill:
+        // both groups take each tile's steps in order, in phase
         f32x16 sc, dp;
+        for (bool first = true; ic < Tq; first = false) {
+            if (!first) publish(sc_);
+            dkdv_sdp(slot(sc_), kf, kh_l, vb_l, sc, dp, g, n, hh);
+            dkdv_dropw(a, rstart(ic), c0, sp.s_b, h, g, t, w, lane);
+            int in2;
+            bool pn2;
+            advance(sn_, in2, pn2);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
-        const int qrow = 32 * g + n;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int o = soff(qrow, 2 * s + hh);
-            sc = mfma(as_bf16x8(*(const u32x4*)(s_q + o)), as_bf16x8(*(const u32x4*)(kb_l + 32 * s)), sc);
-            dp = mfma(as_bf16x8(*(const u32x4*)(s_g + o)), as_bf16x8(*(const u32x4*)(vb_l + 32 * s)), dp);
-        }
-        // the next visited tile and its loads, issued while the products run
-        bool npart = false;
-        const int ni = next_visit(i + 1, npart);
-        if (ni < Tq) load_qstage(a, h, sp.s_b + ni * BLK, min(sp.s_b + (ni + 1) * BLK, sp.e_b), tid, st);
-        if constexpr (DROP) {   // this wave's dropout bytes for the tile
-            uint32_t w0 = (uint32_t)(r0 + 32 * g + (lane & 31));
-            uint32_t w1 = (uint32_t)(((c0 - sp.s_b) >> 4) + 2 * t + (lane >> 5)), w2 = (uint32_t)h, w3 = a.offset;
-            philox4x32_10(w0, w1, w2, w3, a.seed_lo, a.seed_hi);
-            *(u32x4*)&s_drop[w][((lane & 31) * 2 + (lane >> 5)) * 4] = u32x4{w0, w1, w2, w3};
-        }
-        // P = exp2(S scale log2e - lse2), masked pairs 0; dS = P (dP - Delta);
-        // with dropout Z = keep * 256 / (256 - t): P Z for dV, dS = P (dP Z - Delta);
-        // then dV^T += dO^T P and dK^T += Q^T dS for the 16-row group
-        // 2g + c2.  Written per half so that the second half's vector work
-        // can issue while the first half's products run.
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            bf16x8 pb, db;
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = 2 * c2 + jj;
-                const float4 l4 = *(const float4*)(s_l2 + 32 * g + 8 * j + 4 * hh);
-                const float4 d4 = *(const float4*)(s_dl + 32 * g + 8 * j + 4 * hh);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int e = 4 * j + c;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], sl2, -lv[c]));
-                    if (part) {
-                        const int row = r0 + 32 * g + 8 * j + 4 * hh + c;
-                        const bool m = (a.causal && kj > row) || (mv.lts <= row && row < mv.lte) ||
-                                       (mv.uts <= row && row < mv.ute);
-                        p = m ? 0.f : p;
-                    }
-                    float pz = p, dpz = dp[e];
-                    if constexpr (DROP) {
-                        const int rw = 8 * j + 4 * hh + c;   // row within the wave's 32
-                        const uint32_t word = s_drop[w][(rw * 2 + (n >> 4)) * 4 + ((n & 15) >> 2)];
-                        const bool keep = ((word >> (8 * (n & 3))) & 0xffu) >= (uint32_t)a.drop_t;
-                        pz = keep ? p * a.drop_ks : 0.f;
-                        dpz = keep ? dpz * a.drop_ks : 0.f;
-                    }
-                    const float ds = p * (dpz - dv4[c]);
-                    pb[e & 7] = (__bf16)pz;
-                    db[e & 7] = (__bf16)ds;
-                }
+            for (int c2 = 0; c2 < 2; ++c2) {   // each half's P, dS straight into its products
+                bf16x8 pb, db;
+                dkdv_pds_half<DROP>(a, sc, dp, pb, db, slot(sc_), rstart(ic), pc, kj, g, t, w, lane, c2);
+                dkdv_acc_half(slot(sc_), pb, db, dv, dk, g, c2, lane);
             }
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                dv[dt] = mfma(tr_frag_s(s_g, 2 * g + c2, dt, lane), pb, dv[dt]);
-                dk[dt] = mfma(tr_frag_s(s_q, 2 * g + c2, dt, lane), db, dk[dt]);
-            }
+            ic = in_; pc = pn; in_ = in2; pn = pn2;
+            const int tt = sp_; sp_ = sc_; sc_ = sn_; sn_ = tt;
         }
-        i = ni;
-        part = npart;
+    } else if (g == 0) {
+        // group 0: products (the previous tile's dV, dK, then S, dP), then P, dS
+        f32x16 sc, dp;
+        bf16x8 pb[2], db[2];
+        for (bool first = true; ic < Tq; first = false) {
+            if (!first) {
+                publish(sc_);
+                dkdv_acc(slot(sp_), pb, db, dv, dk, g, lane);
+            }
+            dkdv_sdp(slot(sc_), kf, kh_l, vb_l, sc, dp, g, n, hh);
+            int in2;
+            bool pn2;
+            advance(sn_, in2, pn2);
+            dkdv_pds<DROP>(a, sc, dp, pb, db, slot(sc_), rstart(ic), pc, kj, g, t, w, lane);
+            ic = in_; pc = pn; in_ = in2; pn = pn2;
+            const int tt = sp_; sp_ = sc_; sc_ = sn_; sn_ = tt;
+        }
+        if (any) dkdv_acc(slot(sp_), pb, db, dv, dk, g, lane);   // the last tile's dV, dK
+    } else {
+        // group 1: P, dS of the previous tile, then the products
+        f32x16 sc, dp;
+        bf16x8 pb[2], db[2];
+        int ip = Tq;
+        bool pp = false;
+        for (bool first = true; ic < Tq; first = false) {
+            if (!first) {
+                publish(sc_);
+                dkdv_pds<DROP>(a, sc, dp, pb, db, slot(sp_), rstart(ip), pp, kj, g, t, w, lane);
+            }
+            int in2;
+            bool pn2;
+            advance(sn_, in2, pn2);
+            if (!first) dkdv_acc(slot(sp_), pb, db, dv, dk, g, lane);
+            dkdv_sdp(slot(sc_), kf, kh_l, vb_l, sc, dp, g, n, hh);
+            ip = ic; pp = pc;
+            ic = in_; pc = pn; in_ = in2; pn = pn2;
+            const int tt = sp_; sp_ = sc_; sc_ = sn_; sn_ = tt;
+        }
+        if (ip < Tq) {   // the last tile: P, dS, then its dV, dK
+            dkdv_pds<DROP>(a, sc, dp, pb, db, slot(sp_), rstart(ip), pp, kj, g, t, w, lane);
+            dkdv_acc(slot(sp_), pb, db, dv, dk, g, lane);
+        }
     }
 
     // dK summed into group 0, dV into group 1; then group 0 writes
@@ -578,26 +720,10 @@ __shared__ __attribute__((aligned(16))) char s_qk[QSLOTS][BLK * ROW_S];
 __shared__ __attribute__((aligned(16))) char s_qv[QSLOTS][BLK * ROW_S];
 __shared__ __attribute__((aligned(16))) Vec4 s_qmv[QSLOTS][BLK];
 
-// Staging of a key block: K and V rows go from global memory straight into
-// their LDS slot with asynchronous copies (buffer_load ... lds: 64 lanes x
-// 16 bytes into 1 KB of LDS at M0 + 16 lane, rows past the sequence read
-// as zeros through the buffer's byte count); each lane's source is the
-// chunk that the swizzled layout puts at its LDS position, so copy i of a
-// block fills rows 4i..4i+3 (16 copies per tensor, 2 per wave).  The
-// copies are issued with inline assembly and waited for explicitly.  Wave
-// 0 also loads the mask intervals of key c0 + lane of a partial block into
-// registers and stores them to the slot before the block is published.
-typedef __attribute__((address_space(3))) char lds_char;
-__device__ __attribute__((always_inline)) inline void dma_b16(void* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
-                 "{m0}"((uint32_t)(uintptr_t)(lds_char*)dst)
-                 : "memory");
-}
-// Source offset (bytes from the block's first row) of this lane in copy i.
-__device__ __attribute__((always_inline)) inline uint32_t stage_voff(int i, int lane, uint32_t rsb) {
-    const int r = 4 * i + (lane >> 4);
-    return (uint32_t)r * rsb + 16u * (uint32_t)((lane & 15) ^ swz(r));
-}
+// Staging of a key block: K and V rows into their LDS slot with the
+// asynchronous copies above (2 per wave per tensor); wave 0 also loads the
+// mask intervals of key c0 + lane of a partial block into registers and
+// stores them to the slot before the block is published.
 __device__ __attribute__((always_inline)) inline void stage_block(const BwdArgs& a, int h, int c0, int c1, int slot,
                                                                   int w, const uint32_t (&vo)[2]) {
     const uint32_t rsb = (uint32_t)a.H * 2 * HD;
