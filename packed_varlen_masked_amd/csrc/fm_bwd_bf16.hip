@@ -316,9 +316,11 @@ __device__ __attribute__((always_inline)) inline void dkdv_pds_half(const BwdArg
     const int n = lane & 31, hh = lane >> 5;
     const float* s_l2 = (const float*)(sl + OFF_L2);
     const float* s_dl = (const float*)(sl + OFF_DL);
-    Vec4 mv{0, 0, 0, 0};
-    if (part) mv = s_kmv[32 * t + n];
     const float sl2 = a.scale_log2;
+    // the 8 probabilities of the half (register e = 8 c2 + k: row
+    // 32g + 8(2c2 + (k>>2)) + 4hh + (k&3)), then the mask of a partial tile
+    // in one pass (no branch per element), then P, dS
+    float p[8], dl[8];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * c2 + jj;
@@ -327,25 +329,33 @@ __device__ __attribute__((always_inline)) inline void dkdv_pds_half(const BwdArg
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int e = 4 * j + c;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], sl2, -lv[c]));
-            if (part) {
-                const int row = r0 + 32 * g + 8 * j + 4 * hh + c;
-                const bool m = (a.causal && kj > row) || (mv.lts <= row && row < mv.lte) ||
-                               (mv.uts <= row && row < mv.ute);
-                p = m ? 0.f : p;
-            }
-            float pz = p, dpz = dp[e];
-            if constexpr (DROP) {
-                const int rw = 8 * j + 4 * hh + c;   // row within the wave's 32
-                const uint32_t word = s_drop[w][(rw * 2 + (n >> 4)) * 4 + ((n & 15) >> 2)];
-                const bool keep = ((word >> (8 * (n & 3))) & 0xffu) >= (uint32_t)a.drop_t;
-                pz = keep ? p * a.drop_ks : 0.f;
-                dpz = keep ? dpz * a.drop_ks : 0.f;
-            }
-            pb[e & 7] = (__bf16)pz;
-            db[e & 7] = (__bf16)(p * (dpz - dv4[c]));
+            p[4 * jj + c] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * j + c], sl2, -lv[c]));
+            dl[4 * jj + c] = dv4[c];
         }
+    }
+    if (part) {
+        const Vec4 mv = s_kmv[32 * t + n];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int row = r0 + 32 * g + 8 * (2 * c2 + (k >> 2)) + 4 * hh + (k & 3);
+            const bool m = (a.causal && kj > row) || (mv.lts <= row && row < mv.lte) ||
+                           (mv.uts <= row && row < mv.ute);
+            p[k] = m ? 0.f : p[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int e = 8 * c2 + k;
+        float pz = p[k], dpz = dp[e];
+        if constexpr (DROP) {
+            const int rw = 8 * (2 * c2 + (k >> 2)) + 4 * hh + (k & 3);   // row within the wave's 32
+            const uint32_t word = s_drop[w][(rw * 2 + (n >> 4)) * 4 + ((n & 15) >> 2)];
+            const bool keep = ((word >> (8 * (n & 3))) & 0xffu) >= (uint32_t)a.drop_t;
+            pz = keep ? p[k] * a.drop_ks : 0.f;
+            dpz = keep ? dpz * a.drop_ks : 0.f;
+        }
+        pb[k] = (__bf16)pz;
+        db[k] = (__bf16)(p[k] * (dpz - dl[k]));
     }
 }
 template <bool DROP>
