@@ -769,6 +769,12 @@ __device__ __attribute__((always_inline)) inline Vec4 load_mv(const BwdArgs& a, 
 // The products of half u (keys 32u..32u+31) of a staged block: S^T = K Q^T
 // and dP^T = V dO^T, register e = key 32u + 8(e>>2) + 4hh + (e&3), column =
 // this lane's query.
+// PF: the K and V fragments are read two k-steps ahead of the MFMAs that
+// use them (an LDS read takes longer than one MFMA).  That pays with
+// dropout, whose longer vector phase leaves a wave's products alone on the
+// matrix unit; without dropout the partner wave covers the reads and the
+// compiler's own order is 3 % faster.
+template <bool PF>
 __device__ __attribute__((always_inline)) inline void dq_sdp(int slot, int u, const bf16x8 (&qf)[8],
                                                              const bf16x8 (&gf)[8], f32x16& sc, f32x16& dp, int n,
                                                              int hh) {
@@ -776,20 +782,62 @@ __device__ __attribute__((always_inline)) inline void dq_sdp(int slot, int u, co
     for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
     const char* kt = s_qk[slot];
     const char* vt = s_qv[slot];
+    auto frag = [&](const char* b, int s) __attribute__((always_inline)) {
+        return as_bf16x8(*(const u32x4*)(b + soff(32 * u + n, 2 * s + hh)));
+    };
+    if constexpr (!PF) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            sc = mfma(frag(kt, s), qf[s], sc);
+            dp = mfma(frag(vt, s), gf[s], dp);
+        }
+        return;
+    }
+    bf16x8 kr[3], vr[3];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) { kr[s] = frag(kt, s); vr[s] = frag(vt, s); }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const int o = soff(32 * u + n, 2 * s + hh);
-        sc = mfma(as_bf16x8(*(const u32x4*)(kt + o)), qf[s], sc);
-        dp = mfma(as_bf16x8(*(const u32x4*)(vt + o)), gf[s], dp);
+        if (s + 2 < 8) { kr[(s + 2) % 3] = frag(kt, s + 2); vr[(s + 2) % 3] = frag(vt, s + 2); }
+        sc = mfma(kr[s % 3], qf[s], sc);
+        dp = mfma(vr[s % 3], gf[s], dp);
     }
+    // keep the order: 4 reads, then (2 reads, 2 MFMAs) x 6, then 4 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
-// dQ^T += K^T dS^T over the 16-key groups 2u, 2u + 1 of a staged block.
+// dQ^T += K^T dS^T over the 16-key groups 2u, 2u + 1 of a staged block;
+// PF (as for dq_sdp): every transposed fragment is read before the MFMAs.
+template <bool PF>
 __device__ __attribute__((always_inline)) inline void dq_acc(int slot, int u, const bf16x8 (&db)[2], f32x16 (&dq)[4],
                                                              int lane) {
+    if constexpr (!PF) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) dq[dt] = mfma(tr_frag_s(s_qk[slot], 2 * u + k, dt, lane), db[k], dq[dt]);
+        return;
+    }
+    bf16x8 kt[2][4];
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) dq[dt] = mfma(tr_frag_s(s_qk[slot], 2 * u + k, dt, lane), db[k], dq[dt]);
+        for (int dt = 0; dt < 4; ++dt) kt[k][dt] = tr_frag_s(s_qk[slot], 2 * u + k, dt, lane);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dq[dt] = mfma(kt[k][dt], db[k], dq[dt]);
+    // keep the order: the 8 reads of group 2u, then those of 2u + 1 with
+    // the first group's 4 MFMAs, then the last 4 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 // dS = P o (dP - Delta) of half u of a block as the B operand of dq_acc,
 // with the element mask of a partial block (keys k and k + 4 of register e:
@@ -967,20 +1015,20 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
         for (bool first = true; kc < kb_end; first = false) {
             if (!first) {
                 publish(sc_, pc);
-                dq_acc(sp_, 1, db, dq, lane);            // previous block, half 1
+                dq_acc<DROP>(sp_, 1, db, dq, lane);            // previous block, half 1
             }
-            dq_sdp(sc_, 0, qf, gf, sc, dp, n, hh);
+            dq_sdp<DROP>(sc_, 0, qf, gf, sc, dp, n, hh);
             int kn2;
             bool pn2;
             advance(sn_, kn2, pn2);
             dq_ds<DROP>(a, sc, dp, db, sc_, 0, pc, cstart(kc), cend(kc), kc, q0, qr, l2, dl, h, lane, hh);
-            dq_acc(sc_, 0, db, dq, lane);
-            dq_sdp(sc_, 1, qf, gf, sc, dp, n, hh);
+            dq_acc<DROP>(sc_, 0, db, dq, lane);
+            dq_sdp<DROP>(sc_, 1, qf, gf, sc, dp, n, hh);
             dq_ds<DROP>(a, sc, dp, db, sc_, 1, pc, cstart(kc), cend(kc), kc, q0, qr, l2, dl, h, lane, hh);
             kc = kn; pc = pn; kn = kn2; pn = pn2;
             const int t = sp_; sp_ = sc_; sc_ = sn_; sn_ = t;
         }
-        if (any) dq_acc(sp_, 1, db, dq, lane);           // the last block, half 1
+        if (any) dq_acc<DROP>(sp_, 1, db, dq, lane);           // the last block, half 1
     } else {
         // group 1: dS of the previous half, then the products of this one
         f32x16 sc, dp;
@@ -995,18 +1043,18 @@ __global__ __launch_bounds__(NTQ, 1) void fm_bwd_dq_kernel(BwdArgs a) {
             int kn2;
             bool pn2;
             advance(sn_, kn2, pn2);
-            if (!first) dq_acc(sp_, 1, db, dq, lane);   // previous block, half 1
-            dq_sdp(sc_, 0, qf, gf, sc, dp, n, hh);
+            if (!first) dq_acc<DROP>(sp_, 1, db, dq, lane);   // previous block, half 1
+            dq_sdp<DROP>(sc_, 0, qf, gf, sc, dp, n, hh);
             dq_ds<DROP>(a, sc, dp, db, sc_, 0, pc, cstart(kc), cend(kc), kc, q0, qr, l2, dl, h, lane, hh);
-            dq_acc(sc_, 0, db, dq, lane);
-            dq_sdp(sc_, 1, qf, gf, sc, dp, n, hh);
+            dq_acc<DROP>(sc_, 0, db, dq, lane);
+            dq_sdp<DROP>(sc_, 1, qf, gf, sc, dp, n, hh);
             kp = kc; pp = pc;
             kc = kn; pc = pn; kn = kn2; pn = pn2;
             const int t = sp_; sp_ = sc_; sc_ = sn_; sn_ = t;
         }
         if (kp < kb_end) {   // the last block, half 1: dS, then its dQ
             dq_ds<DROP>(a, sc, dp, db, sp_, 1, pp, cstart(kp), cend(kp), kp, q0, qr, l2, dl, h, lane, hh);
-            dq_acc(sp_, 1, db, dq, lane);
+            dq_acc<DROP>(sp_, 1, db, dq, lane);
         }
     }
 
