@@ -157,6 +157,23 @@ def test_bwd_shared_question_full_heads(pv):
     compare_heads(w, got, g, (0, w.H - 1), "cfg4")
 
 
+def test_bwd_short_documents_unchunked(pv):
+    """Documents of 1 to 320 tokens filling 16384 tokens at 32 heads, enough
+    work that neither launch is cut into chunks: key spans and query tiles
+    that visit one to five tiles, so the phase-shifted loops' first and last
+    steps (and spans of a single step) run at the full-size launch shapes.
+    Heads 0 and H - 1 against the oracle."""
+    pattern = [1, 64, 65, 128, 129, 192, 255, 256, 257, 320]
+    lens = []
+    while sum(lens) + 320 < 16384:
+        lens.append(pattern[len(lens) % len(pattern)])
+    lens.append(16384 - sum(lens))
+    w = W.document_workload(lens, H=32, seed=99)
+    say("bwd short documents B=%d N=%d H=%d" % (w.B, w.N, w.H))
+    got, g = run_bwd(pv, w)
+    compare_heads(w, got, g, (0, w.H - 1), "short docs")
+
+
 def test_bwd_prefix_window_full_sampled(pv):
     """Prefix-LM + window workload at full size (131072 tokens, 8 heads):
     sampled dq rows against the oracle one by one, and for every sequence and
