@@ -629,11 +629,13 @@ __device__ __attribute__((always_inline)) inline Item item_of(const AttnArgs& a,
 // 272 B: 16 bf16 groups of 8 B per lane land in distinct banks), then reads
 // them back 16 B per lane and writes 4 whole rows per store instruction
 // (1 KB, 256 B per row) instead of 16 scattered 8-byte pieces per lane.
+// Waves 0-3 stage in K slots 1-2, waves 4-7 in V slots 1-2: K slot 0 and V
+// slot 0 stay free for the next item's first tile, copied meanwhile.
 constexpr int OST_ROW = 272, OST_WAVE = 32 * OST_ROW;
-static_assert(NW * OST_WAVE <= 6 * 20 * 1024, "output staging fits in the ring");
+static_assert(GW * OST_WAVE <= 2 * SLOT_BYTES, "output staging fits in two ring slots");
 __device__ __attribute__((always_inline)) inline void write_rows(const AttnArgs& a, const Wave& Wv, const Item& I,
                                                                  const State& st, float inv) {
-    char* stg = s_kv + Wv.w * OST_WAVE;
+    char* stg = (Wv.w < GW ? kbuf(1) : vbuf(1)) + (Wv.w % GW) * OST_WAVE;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -720,15 +722,31 @@ __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a
 
 // Q^T fragments (B operand) of the wave's 32 query rows: lane holds query
 // qrow, channels 16s + 8hh .. +7 in qf[s]; rows at or past r1 are zero.
-__device__ __attribute__((always_inline)) inline void load_q(const AttnArgs& a, const Wave& Wv, int r1, int64_t hoff,
-                                                             bf16x8 (&qf)[8]) {
-    if (Wv.qrow < r1) {
-        const uint16_t* qp = (const uint16_t*)a.q + (int64_t)Wv.qrow * ((int64_t)a.H * HD) + hoff + 8 * Wv.hh;
+__device__ __attribute__((always_inline)) inline void load_q_row(const AttnArgs& a, int qrow, int hh, int r1,
+                                                                 int64_t hoff, bf16x8 (&qf)[8]) {
+    if (qrow < r1) {
+        const uint16_t* qp = (const uint16_t*)a.q + (int64_t)qrow * ((int64_t)a.H * HD) + hoff + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
     } else {
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+}
+__device__ __attribute__((always_inline)) inline void load_q(const AttnArgs& a, const Wave& Wv, int r1, int64_t hoff,
+                                                             bf16x8 (&qf)[8]) {
+    load_q_row(a, Wv.qrow, Wv.hh, r1, hoff, qf);
+}
+// The block extrema of the wave's first visit window of an item (lane =
+// key block lo + 64 w + lane, zero past hi).
+__device__ __attribute__((always_inline)) inline void load_window0(const Item& I, const Wave& Wv, int lo, int hi,
+                                                                   u32x4& x0, u32x4& x1) {
+    x0 = u32x4{0, 0, 0, 0};
+    x1 = u32x4{0, 0, 0, 0};
+    const int kb = lo + 64 * Wv.w + Wv.lane;
+    if (kb < hi) {
+        x0 = *(const u32x4*)(I.xb + (int64_t)kb * 8);
+        x1 = *(const u32x4*)(I.xb + (int64_t)kb * 8 + 4);
     }
 }
 
@@ -738,10 +756,16 @@ __device__ __attribute__((always_inline)) inline void load_q(const AttnArgs& a, 
 // extrema in global memory (FlashMask article §3.2 rules) and the next
 // item's record is prefetched during the loop; otherwise the list is ready
 // in s_vis at `vis_off` (fused path).
-template <bool STD, bool DROP>
+// pre (standard kernel): the item's Q fragments, the extrema of its first
+// visit window (pxw0, pxw1) and its first tile (pre_kb) were loaded by the
+// item before it, during that item's output; `handover(T)` is called by
+// every wave once the KV loop is done, to do the same for the next item.
+template <bool STD, bool DROP, typename Handover>
 __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a, Wave& Wv, const Item& I,
                                                                int vis_off, bool& rec_pending, int fv, int& nrec,
-                                                               int n_items, bf16x8 (&qf)[8], int pre_kb = -1) {
+                                                               int n_items, bf16x8 (&qf)[8], int pre_kb, bool pre,
+                                                               const u32x4& pxw0, const u32x4& pxw1,
+                                                               Handover&& handover) {
     const int tid = Wv.tid, lane = Wv.lane, w = Wv.w;
     const int64_t rs = (int64_t)a.H * HD;
     Wv.qrow = I.r0 + 32 * w + Wv.n;
@@ -760,16 +784,19 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
     const int nwin = (STD && lo < hi) ? ceil_div(hi - lo, 64) : 0;
     u32x4 xw0 = {0, 0, 0, 0}, xw1 = {0, 0, 0, 0};
     if constexpr (STD) {
-        const int kb = lo + 64 * w + lane;
-        if (w < nwin && kb < hi) {
-            xw0 = *(const u32x4*)(I.xb + (int64_t)kb * 8);
-            xw1 = *(const u32x4*)(I.xb + (int64_t)kb * 8 + 4);
+        if (pre) {
+            xw0 = pxw0;
+            xw1 = pxw1;
+        } else if (w < nwin) {
+            load_window0(I, Wv, lo, hi, xw0, xw1);
         }
     }
     // (the fused kernel loaded Q before planning and may have copied the
-    // first tile already: pre_kb)
+    // first tile already, as may the standard kernel's previous item: pre_kb)
     if (!Wv.no_skip && lo < hi && lo != pre_kb) copy_tile_pair(a, I, Wv, Kh, Vh, lo);
-    if constexpr (STD) load_q(a, Wv, I.r1, I.hoff, qf);
+    if constexpr (STD) {
+        if (!pre) load_q(a, Wv, I.r1, I.hoff, qf);
+    }
 
     int T;
     const uint16_t* vis;
@@ -889,6 +916,7 @@ __device__ __attribute__((always_inline)) inline void run_item(const AttnArgs& a
     // here, before the output stores, so that the next item can refill the
     // ring without waiting for the stores to reach memory
     wait_vm<0>();
+    handover(T);
     epilogue(a, Wv, I, st);
 }
 
@@ -913,6 +941,11 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
     int it = blockIdx.x;
     if (it < n_items && tid < ITEM_WORDS) s_rec[tid] = a.items[(int64_t)it * ITEM_WORDS + tid];
     __syncthreads();
+    // the next item's first loads, issued during this item's output (pre)
+    bool pre = false;
+    int pre_kb = -1;
+    u32x4 nxw0 = {0, 0, 0, 0}, nxw1 = {0, 0, 0, 0};
+    bf16x8 qf[8];
     while (it < n_items) {
         // the fetch value is only needed when the next record is read: no
         // arithmetic on it here, so nothing waits for the atomic's return
@@ -920,22 +953,60 @@ __global__ __launch_bounds__(NTH, 2) void fm_attn_bf16_kernel(AttnArgs a) {
         if (tid == 0) fv = atomicAdd(a.sched_counter, 1);
         const Item I = item_of(a, s_rec);
         bool rec_pending = (w == 0);
-        bf16x8 qf[8];
-        run_item<true, DROP>(a, Wv, I, 0, rec_pending, fv, nrec, n_items, qf);
+        const bool pre_this = pre;
+        const int pkb = pre_kb;
+        const u32x4 pxw0 = nxw0, pxw1 = nxw1;
+        bool handed = false;
+        // An item that visited tiles read the next record in its first KV
+        // step.  Once its loop is done and the ring drained: the record and
+        // the next index to every wave, then the next item's Q, first extrema
+        // window and first tile (K slot 0, V slot 0, which the output staging
+        // leaves free) are issued before this item's output is written.
+        // (the dropout kernel has no registers to spare for it)
+        auto handover = [&](int T) {
+            if (DROP || T == 0) return;
+            handed = true;
+            if (w == 0) {
+                if (lane < ITEM_WORDS) s_rec[lane] = nrec;
+                if (lane == 0) s_next = G + fv;
+            }
+            item_barrier();   // every wave is past its last ring and s_rec read
+            pre = false;
+            pre_kb = -1;
+            if (__builtin_amdgcn_readfirstlane(s_next) < n_items) {
+                const Item NI = item_of(a, s_rec);
+                const int nlo = Wv.no_skip ? 0 : NI.kbb, nhi = Wv.no_skip ? NI.Tc : NI.kbe;
+                if (64 * w < nhi - nlo) load_window0(NI, Wv, nlo, nhi, nxw0, nxw1);
+                if (!Wv.no_skip && nlo < nhi) {
+                    copy_tile_pair(a, NI, Wv, (const char*)a.k + NI.hoff * 2, (const char*)a.v + NI.hoff * 2, nlo);
+                    pre_kb = nlo;
+                }
+                load_q_row(a, NI.r0 + 32 * w + Wv.n, Wv.hh, NI.r1, NI.hoff, qf);
+                pre = true;
+            }
+        };
+        run_item<true, DROP>(a, Wv, I, 0, rec_pending, fv, nrec, n_items, qf, pre_this ? pkb : -1, pre_this, pxw0,
+                             pxw1, handover);
         int nxt = G + __builtin_amdgcn_readfirstlane(fv);
-        if (rec_pending) {
-            if (nxt < n_items && lane < ITEM_WORDS) nrec = a.items[(int64_t)nxt * ITEM_WORDS + lane];
-        }
-        // the ring copies were drained before the epilogue; the output stores
-        // need no wait
-        item_barrier();   // every wave is done with s_rec, the visit list and the LDS buffers
         if (w == 0) {
             nxt = __builtin_amdgcn_readfirstlane(nxt);
             if (nxt == last_fetch && lane == 0) atomicExch(a.sched_counter, 0);
-            if (lane < ITEM_WORDS) s_rec[lane] = nrec;
-            if (lane == 0) s_next = nxt;
         }
-        __syncthreads();
+        if (!handed) {   // no tile visited: the record is read here
+            pre = false;
+            pre_kb = -1;
+            if (rec_pending) {
+                if (nxt < n_items && lane < ITEM_WORDS) nrec = a.items[(int64_t)nxt * ITEM_WORDS + lane];
+            }
+            // the ring copies were drained before the epilogue; the output
+            // stores need no wait
+            item_barrier();   // every wave is done with s_rec, the visit list and the LDS buffers
+            if (w == 0) {
+                if (lane < ITEM_WORDS) s_rec[lane] = nrec;
+                if (lane == 0) s_next = nxt;
+            }
+            __syncthreads();
+        }
         it = __builtin_amdgcn_readfirstlane(s_next);
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -1000,7 +1071,8 @@ __global__ __launch_bounds__(NTH, 2) void fm_fused_bf16_kernel(AttnArgs a) {
             __syncthreads();                 // every wave is done with the window masks
             continue;
         }
-        run_item<false, false>(a, Wv, I, vis_off, rec_pending, 0, nrec, n_items, qf, pre_kb);
+        run_item<false, false>(a, Wv, I, vis_off, rec_pending, 0, nrec, n_items, qf, pre_kb, false,
+                               u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, [](int) {});
         item_barrier();   // the ring, the visit list and the masks are free for the next item
     }
     __builtin_amdgcn_s_waitcnt(0);
