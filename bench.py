@@ -51,7 +51,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 1000 on the small varlen workload, 200 on the others)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload config id (1..5); 2 is the headline")
     ap.add_argument("--split", type=int, default=-1, help="max key blocks per item (-1 auto, 0 none)")
@@ -84,7 +85,10 @@ def parse():
     ap.add_argument("--preprocess-sweep", action="store_true",
                     help="instead of the step: time the block-extrema pass alone for N = 2^16 .. 2^26 "
                          "(n_vec = 4, non-causal) and report its achieved HBM GB/s")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 1000 if args.config == 2 else 200
+    return args
 
 
 FWD_SOURCES = ("fm_api.cpp", "fm_attn_bf16.hip", "fm_common.hpp", "fm_internal.h", "fm_own_plan.h", "fm_plan.hip")
