@@ -631,7 +631,7 @@ def main():
         preprocess_sweep(args)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     if args.sparsity_sweep:
