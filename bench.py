@@ -96,14 +96,17 @@ FWD_SOURCES = ("fm_api.cpp", "fm_attn_bf16.hip", "fm_common.hpp", "fm_internal.h
 
 def source_hash():
     """sha256 over the sources of the forward bf16 path (the planning and
-    attention kernels and the host code that launches them): stored counter
-    figures apply only to the kernels they were taken from."""
+    attention kernels and the host code that launches them) and the build
+    script (its compiler flags): stored counter figures apply only to the
+    kernels they were taken from."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "packed_varlen_masked_amd", "csrc")
+    pkg = os.path.join(ROOT, "packed_varlen_masked_amd")
     for name in FWD_SOURCES:
         h.update(name.encode())
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(pkg, "csrc", name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(pkg, "build.py"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()
 
 
