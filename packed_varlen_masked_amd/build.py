@@ -20,12 +20,8 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["fm_api.cpp", "fm_plan.hip", "fm_attn_bf16.hip", "fm_attn_f32.hip", "fm_bwd_bf16.hip", "fm_rope.hip"]
 ARCH = "gfx950"
-# The bf16 attention kernels run with the IEEE mode bit off and assume no
-# NaN operands (inputs with NaNs give NaN-free garbage instead of NaNs):
-# their row maxima then need no quieting instructions before the max
-# operations (about 1 % on the long workloads).  Infinities keep their
-# meaning (masked scores are -inf).
-EXTRA_FLAGS = {"fm_attn_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+# Per-source compiler flags beyond compile_flags() (none at present).
+EXTRA_FLAGS = {}
 
 
 def hipcc() -> str:

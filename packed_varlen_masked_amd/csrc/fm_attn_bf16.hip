@@ -459,7 +459,7 @@ __device__ __attribute__((always_inline)) inline float softmax_tile(const AttnAr
     const bool causal = a.causal && (c1 - 1 > Wv.qrow - Wv.n);
     const float mx = mask_max(sacc, causal, (c1 - c0) < BC, iv, c0, c1, Wv.qrow - Wv.n, cmv, a.scale_log2, Wv.lane);
     DropW dw;
-    if constexpr (DROP) dw = drop_words(a.seed_lo, a.seed_hi, a.offset, Wv.qrow, kb, I.h, Wv.hh);
+    if constexpr (DROP) dw = drop_words<true>(a.seed_lo, a.seed_hi, a.offset, Wv.qrow, kb, I.h, Wv.hh);
     return exp_tile<DROP>(sacc, mx, st, pb, a.scale_log2, rsum, dw, a.drop_t, a.drop_ks);
 }
 

@@ -70,13 +70,23 @@ __host__ __device__ inline TileInfo classify_tile(int r0, int r1, int c0, int c1
 // rounds.  The dropout byte of a pair (query row i, key j of a sequence
 // starting at s) for head h is byte (j - s) & 15 of the four words for
 // counter (i, (j - s) >> 4, h, offset) and key (seed lo, seed hi).
+// WIDE: each product as one 32 x 32 -> 64 multiply (one instruction instead
+// of separate high and low products; the same bits).
+template <bool WIDE = false>
 __device__ __attribute__((always_inline)) inline void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2,
                                                                     uint32_t& c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        uint32_t hi0, lo0, hi1, lo1;
+        if constexpr (WIDE) {
+            const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+            hi0 = (uint32_t)(p0 >> 32); lo0 = (uint32_t)p0;
+            hi1 = (uint32_t)(p1 >> 32); lo1 = (uint32_t)p1;
+        } else {
+            hi0 = __umulhi(0xD2511F53u, c0); lo0 = 0xD2511F53u * c0;
+            hi1 = __umulhi(0xCD9E8D57u, c2); lo1 = 0xCD9E8D57u * c2;
+        }
         const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
         c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
     }
@@ -90,13 +100,14 @@ __device__ __attribute__((always_inline)) inline void philox4x32_10(uint32_t& c0
 // computes blocks 2hh, 2hh + 1 and the two halves swap the words the other
 // one needs.
 struct DropW { uint32_t w[4][2]; };
+template <bool WIDE = false>
 __device__ __attribute__((always_inline)) inline DropW drop_words(uint32_t seed_lo, uint32_t seed_hi, uint32_t offset,
                                                                   int row, int kb, int h, int hh) {
     uint32_t own[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         uint32_t c0 = (uint32_t)row, c1 = (uint32_t)(4 * kb + 2 * hh + u), c2 = (uint32_t)h, c3 = offset;
-        philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
+        philox4x32_10<WIDE>(c0, c1, c2, c3, seed_lo, seed_hi);
         own[u][0] = c0; own[u][1] = c1; own[u][2] = c2; own[u][3] = c3;
     }
     DropW d;
