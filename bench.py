@@ -529,9 +529,11 @@ def dropout_bench(args):
                 pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), plan=plan, out=out, lse=lse, **kw)
         grads = [torch.empty_like(q) for _ in range(3)]
 
+        side = torch.cuda.Stream()   # the dQ launches overlap dK/dV on it, with and without dropout
+
         def bwd():
             pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale), workspace=wsb,
-                        dq=grads[0], dk=grads[1], dv=grads[2], **kw)
+                        dq=grads[0], dk=grads[1], dv=grads[2], dq_stream=side, **kw)
         for _ in range(args.warmup):
             fwd()
             bwd()

@@ -423,6 +423,19 @@ int fm_attn_bwd_dropout(const void* q, const void* k, const void* v, const void*
                         float dropout_p, uint64_t seed, uint64_t offset, hipStream_t stream);
 
 /*
+ * fm_attn_bwd_dropout with the dQ launches on a second stream of the
+ * caller's, exactly as fm_attn_bwd_streams does for fm_attn_bwd (same
+ * arguments and results, the same bits; the same ordering, ownership and
+ * FM_E_INVAL rules for dq_stream, fork and join).
+ */
+int fm_attn_bwd_dropout_streams(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* softmax_lse, int dtype, int64_t N, int H, int D,
+                                const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec,
+                                int causal, float scale, void* dq, void* dk, void* dv, void* workspace,
+                                size_t ws_bytes, float dropout_p, uint64_t seed, uint64_t offset,
+                                hipStream_t stream, hipStream_t dq_stream, hipEvent_t fork, hipEvent_t join);
+
+/*
  * Rotary position embedding of packed q and k, in place, one launch for
  * both (Unsloth packing blog, fused QK RoPE section: one kernel for Q and
  * K, positions that restart in every packed sample, in place).  Row i of

@@ -86,6 +86,8 @@ def _load():
         "fm_attn_bwd_dropout": (I, [P, P, P, P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, P, P, SZ, F, U64, U64, P]),
         "fm_attn_fwd_noalloc": (I, [P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, I, I, I, U, P]),
         "fm_attn_bwd_streams": (I, [P, P, P, P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, P, P, SZ, P, P, P, P]),
+        "fm_attn_bwd_dropout_streams": (I, [P, P, P, P, P, P, I, I64, I, I, P, I, P, I, I, F, P, P, P, P, SZ, F, U64,
+                                            U64, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -99,7 +101,8 @@ EXPORTED = ("fm_last_error", "fm_version", "fm_self_check", "fm_get_tile_config"
             "fm_workspace_layout", "fm_workspace_size", "fm_worklist_scratch_size",
             "fm_preprocess_mask", "fm_build_worklist", "fm_build_plan", "fm_attn_fwd",
             "fm_read_status", "fm_fused_path", "fm_bwd_workspace_size", "fm_attn_bwd", "fm_rope_qk",
-            "fm_attn_fwd_dropout", "fm_attn_bwd_dropout", "fm_attn_fwd_noalloc", "fm_attn_bwd_streams")
+            "fm_attn_fwd_dropout", "fm_attn_bwd_dropout", "fm_attn_fwd_noalloc", "fm_attn_bwd_streams",
+            "fm_attn_bwd_dropout_streams")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # FM_NOALLOC_SCRATCH_BYTES
 
 
@@ -412,9 +415,10 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
              dq_stream: Optional[torch.cuda.Stream] = None):
     """FlashMask backward.  q, k, v, out, dout: [N, H, D] bf16 (contiguous,
     same device); lse fp32 [H, N] from the forward; cu_seqlens and startend
-    as for attn_fwd.  dq_stream (no dropout): a second stream of the
-    caller's on which the dQ launches overlap the dK/dV ones
-    (fm_attn_bwd_streams; the fork and join events are this binding's).
+    as for attn_fwd.  dq_stream: a second stream of the caller's on which
+    the dQ launches overlap the dK/dV ones (fm_attn_bwd_streams,
+    fm_attn_bwd_dropout_streams; the fork and join events are this
+    binding's).
     Returns (dq, dk, dv) [N, H, D] bf16."""
     ts = ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"))
     for t, nm in ts:
@@ -453,8 +457,12 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel())
     if dropout_p > 0.0:
         if dq_stream is not None:
-            raise FMError(FM_E_INVAL, "dq_stream is for the backward without dropout")
-        _check(_lib.fm_attn_bwd_dropout(*common, ctypes.c_float(dropout_p), seed, offset, _stream()))
+            fork, join = _bwd_events(q.device)
+            _check(_lib.fm_attn_bwd_dropout_streams(*common, ctypes.c_float(dropout_p), seed, offset, _stream(),
+                                                    ctypes.c_void_p(dq_stream.cuda_stream),
+                                                    ctypes.c_void_p(fork.cuda_event), ctypes.c_void_p(join.cuda_event)))
+        else:
+            _check(_lib.fm_attn_bwd_dropout(*common, ctypes.c_float(dropout_p), seed, offset, _stream()))
     elif dq_stream is not None:
         fork, join = _bwd_events(q.device)
         _check(_lib.fm_attn_bwd_streams(*common, _stream(), ctypes.c_void_p(dq_stream.cuda_stream),

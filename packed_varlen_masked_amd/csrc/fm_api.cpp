@@ -725,6 +725,18 @@ int fm_attn_bwd_dropout(const void* q, const void* k, const void* v, const void*
                          nullptr);
 }
 
+int fm_attn_bwd_dropout_streams(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* softmax_lse, int dtype, int64_t N, int H, int D,
+                                const int32_t* cu_seqlens, int B, const int32_t* startend, int n_vec, int causal,
+                                float scale, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                                float dropout_p, uint64_t seed, uint64_t offset, hipStream_t stream,
+                                hipStream_t dq_stream, hipEvent_t fork, hipEvent_t join) {
+    if (!dq_stream) return fail(FM_E_INVAL, "null dQ stream (use fm_attn_bwd_dropout for one stream)");
+    return attn_bwd_impl(q, k, v, out, dout, softmax_lse, dtype, N, H, D, cu_seqlens, B, startend, n_vec, causal,
+                         scale, dq, dk, dv, workspace, ws_bytes, dropout_p, seed, offset, stream, dq_stream, fork,
+                         join);
+}
+
 int fm_rope_qk(void* q, void* k, int dtype, int64_t N, int Hq, int Hk, int head_dim, const int32_t* cu_seqlens,
                int B, const float* cos_table, const float* sin_table, int64_t max_pos, int inverse,
                int32_t* status, hipStream_t stream) {

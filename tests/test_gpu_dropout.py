@@ -100,6 +100,29 @@ def test_dropout_backward(pv, idx):
         assert err <= 2e-2 + 1e-2 * mx
 
 
+@pytest.mark.parametrize("idx", range(3))
+def test_dropout_backward_two_streams(pv, idx):
+    """fm_attn_bwd_dropout_streams: the dQ launches on a second stream give
+    the one-stream call's bits, and everything is ordered before the next
+    work on the caller's stream (the gradients are read there)."""
+    name, w = cases()[idx]
+    p, seed, off = 0.25, 987654321, 5
+    q, k, v, cu, sv = dev(w)
+    g = torch.from_numpy(np.random.default_rng(idx).standard_normal(w.q.shape, dtype=np.float32))
+    g = g.to(torch.bfloat16).cuda()
+    out, lse = pv.attn_fwd(q, k, v, cu, sv, w.n_vec, w.causal, float(w.scale), dropout_p=p, seed=seed, offset=off)
+    one = pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale),
+                      dropout_p=p, seed=seed, offset=off)
+    side = torch.cuda.Stream()
+    two = pv.attn_bwd(q, k, v, out, lse, g, cu, sv, w.n_vec, w.causal, float(w.scale),
+                      dropout_p=p, seed=seed, offset=off, dq_stream=side)
+    copies = [t.clone() for t in two]   # on the caller's stream, after the join
+    torch.cuda.synchronize()
+    say("dropout bwd two streams", name, "N=%d" % w.N)
+    for nm, a, b in zip(("dq", "dk", "dv"), one, copies):
+        assert torch.equal(a, b), nm
+
+
 @pytest.mark.parametrize("case", ["docs", "random_causal", "random_intervals"])
 def test_dropout_keep_mask_exact(pv, case):
     """The keep mask itself, bit for bit: with q = 0 every visible key gets
